@@ -1,0 +1,131 @@
+"""Seeded synthetic inputs for the compressed-MLP matmul workloads.
+
+This module only draws numbers.  It holds none of the codec's or the matmul's
+arithmetic, so both the CPU oracle (``oracle/``) and the HIP path
+(``mlp_matmul_amd``) may take their inputs from it without sharing any of the
+method between them.
+
+The Unweight page (Cloudflare, "Unweight: how we compressed an LLM 22% without
+sacrificing quality", section "Why compression is harder than you'd think" and
+the introduction) measures on trained Llama-3.1-8B MLP weights.  Those weights
+are not available here, so every input is synthetic with Llama-3.1-8B's MLP
+shapes: gate and up are 14336x4096 (out x in), down is 4096x14336.
+
+Recipe (fixed order, numpy ``default_rng``):
+  1. weights ~ standard_normal(float32) * sigma   (sigma per row for workload 4)
+  2. outlier mask = random() < p
+  3. outlier values ~ standard_normal(float32) * s at the masked positions
+  4. round float32 -> bfloat16, round-to-nearest-even
+  5. activations ~ standard_normal(float32) -> bfloat16 RNE (own stream)
+
+Seeds: the small single-matrix workload uses ``default_rng(0)`` for weights
+then activations.  Every other workload ``c`` uses
+``default_rng([c, layer, m, k])`` with m = 0 gate, 1 up, 2 down and k = 0 for
+weights, 1 for activations.  The 32-layer stack draws each layer's outlier rate
+from ``default_rng([5, layer, 9, 0])``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LLAMA_HIDDEN = 4096
+LLAMA_FFN = 14336
+
+# (rows, cols) of each MLP matrix, stored as torch Linear.weight [out, in].
+MLP_SHAPES = {
+    0: (LLAMA_FFN, LLAMA_HIDDEN),   # gate
+    1: (LLAMA_FFN, LLAMA_HIDDEN),   # up
+    2: (LLAMA_HIDDEN, LLAMA_FFN),   # down
+}
+MATRIX_NAMES = {0: "gate", 1: "up", 2: "down"}
+
+# Outlier rate of the 32-layer stack is uniform in [0.01%, 0.2%].
+STACK_P_LO = 1e-4
+STACK_P_HI = 2e-3
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+
+    NaNs stay NaN (quiet bit forced), infinities stay infinite.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return r
+
+
+def gaussian_weights(rng: np.random.Generator, rows: int, cols: int,
+                     sigma: float = 0.02, p_out: float = 0.0,
+                     s_out: float = 0.0, row_sigma=None) -> np.ndarray:
+    """bf16 bits [rows, cols]: N(0, sigma) plus Bernoulli(p_out) N(0, s_out) outliers."""
+    w = rng.standard_normal((rows, cols), dtype=np.float32)
+    if row_sigma is not None:
+        w *= np.asarray(row_sigma, dtype=np.float32)[:, None]
+    else:
+        w *= np.float32(sigma)
+    if p_out > 0.0:
+        mask = rng.random((rows, cols)) < p_out
+        n = int(mask.sum())
+        w[mask] = rng.standard_normal(n, dtype=np.float32) * np.float32(s_out)
+    return f32_to_bf16_bits(w)
+
+
+def gaussian_activations(rng: np.random.Generator, batch: int, cols: int) -> np.ndarray:
+    """bf16 bits [batch, cols] drawn N(0, 1)."""
+    return f32_to_bf16_bits(rng.standard_normal((batch, cols), dtype=np.float32))
+
+
+# ---------------------------------------------------------------- workload 1
+def small_matrix(batch: int = 1):
+    """512x1024 bf16 N(0,0.02) with 0.1% N(0,1) outliers and a 1x1024 N(0,1)
+    activation, both from default_rng(0).  Returns (W bits, X bits)."""
+    rng = np.random.default_rng(0)
+    w = gaussian_weights(rng, 512, 1024, sigma=0.02, p_out=1e-3, s_out=1.0)
+    x = gaussian_activations(rng, batch, 1024)
+    return w, x
+
+
+# ------------------------------------------------------- workloads 2, 3, 4, 5
+def stack_outlier_rate(layer: int) -> float:
+    u = np.random.default_rng([5, layer, 9, 0]).random()
+    return STACK_P_LO + u * (STACK_P_HI - STACK_P_LO)
+
+
+def layer_weight(workload: int, layer: int, m: int, shape=None) -> np.ndarray:
+    """bf16 bits of MLP matrix m (0 gate, 1 up, 2 down) of one layer.
+
+    workload 2 and 3: N(0,0.02) + 0.05% N(0,0.5) outliers.
+    workload 4: per-row sigma_r log-uniform in [0.005, 0.05], no outliers.
+    workload 5: N(0,0.02) + per-layer outlier rate in [0.01%, 0.2%] of N(0,0.5).
+    ``shape`` overrides Llama's (rows, cols) for reduced-size tests.
+    """
+    rows, cols = shape if shape is not None else MLP_SHAPES[m]
+    rng = np.random.default_rng([workload, layer, m, 0])
+    if workload in (2, 3):
+        return gaussian_weights(rng, rows, cols, 0.02, 5e-4, 0.5)
+    if workload == 4:
+        u = rng.random(rows)
+        lo, hi = np.log(0.005), np.log(0.05)
+        row_sigma = np.exp(lo + u * (hi - lo)).astype(np.float32)
+        return gaussian_weights(rng, rows, cols, row_sigma=row_sigma)
+    if workload == 5:
+        return gaussian_weights(rng, rows, cols, 0.02, stack_outlier_rate(layer), 0.5)
+    raise ValueError(f"no layer weights for workload {workload}")
+
+
+def layer_activation(workload: int, layer: int, m: int, batch: int, cols=None) -> np.ndarray:
+    """bf16 bits [batch, cols] of the activation fed to matrix m."""
+    if cols is None:
+        cols = MLP_SHAPES[m][1]
+    rng = np.random.default_rng([workload, layer, m, 1])
+    return gaussian_activations(rng, batch, cols)
+
+
+def random_bf16_bits(seed: int, n: int) -> np.ndarray:
+    """Uniformly random 16-bit patterns: every exponent, NaNs and subnormals."""
+    return np.random.default_rng(seed).integers(0, 1 << 16, size=n, dtype=np.uint16)
