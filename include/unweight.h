@@ -1,0 +1,280 @@
+/*
+ * unweight.h -- C ABI of the MI355X (gfx950) compressed-MLP matmul library.
+ *
+ * The method: Cloudflare, "Unweight: how we compressed an LLM 22% without
+ * sacrificing quality".
+ *   - "How to compress model weights effectively": a bf16 weight's sign and
+ *     mantissa are kept raw; its exponent byte is Huffman coded against the
+ *     matrix's 16 most frequent exponents (the palette); a 64-element row that
+ *     holds any other exponent is kept verbatim.
+ *   - "Four ways to use compressed weights": full Huffman decode to bf16 then a
+ *     plain matmul; exponent-only decode; runtime transcode to 4-bit palette
+ *     indices; direct palette (indices made once at load time).  The last three
+ *     feed a reconstructive matmul.
+ *   - "How the reconstructive matmul works": the fused kernel reads compressed
+ *     data, rebuilds bf16 on chip and multiplies; rebuilt weights never return
+ *     to device memory.
+ *   - "Why no single pipeline wins": the best pipeline depends on batch size
+ *     and matrix shape and is picked per matrix x batch by measuring.
+ *
+ * Conventions
+ *   - Every function returns int: UW_OK (0) or a negative UW_E* code, except
+ *     where stated.  uw_last_error() returns a thread-local message for the
+ *     last failure on the calling thread.  No C++ exception crosses the ABI.
+ *   - A weight matrix W is [rows, cols] row-major bf16 bit patterns
+ *     (uint16_t), the layout of torch.nn.Linear.weight (out x in).  cols must
+ *     be a multiple of 64.  Activations X are [batch, cols] bf16 row-major;
+ *     outputs Y are [batch, rows] fp32 row-major: Y = X . W^T, accumulated in
+ *     fp32.
+ *   - Host pointers are marked (host); every other pointer is a device
+ *     pointer owned by the caller.  The library never allocates device
+ *     memory; the caller allocates outputs and any scratch
+ *     (uw_scratch_bytes).  Device buffers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls
+ *     are asynchronous and stream ordered; errors found before launch are
+ *     returned, launch failures surface as UW_EHIP.
+ *   - Host blobs (uw_blob) are owned by the library and freed with
+ *     uw_blob_free.
+ */
+#ifndef UNWEIGHT_H
+#define UNWEIGHT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ error codes */
+#define UW_OK            0
+#define UW_EINVAL       -1   /* bad argument (shape, pointer, mode) */
+#define UW_ENOMEM       -2   /* host allocation failed */
+#define UW_EFORMAT      -3   /* blob fails validation */
+#define UW_EHIP         -4   /* HIP runtime error */
+#define UW_EUNSUPPORTED -5   /* valid request this build does not handle */
+
+/* Thread-local text of the last error on this thread ("" if none). */
+const char* uw_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+int uw_version(void);
+
+/* sizeof(uw_info), sizeof(uw_dmat), sizeof(uw_opts) as compiled, so a binding
+ * can check its mirror of these structs (any pointer may be NULL). */
+int uw_abi_struct_sizes(uint64_t* info, uint64_t* dmat, uint64_t* opts);
+
+/* ------------------------------------------------------------- the format */
+/* Sections of a compressed matrix.  N = rows*cols, G = N/64 groups of 64
+ * consecutive elements of a row, T = ceil(G/64) tiles of 64 groups, V
+ * verbatim groups.
+ *   SM         uint8[N]    sign/mantissa byte, (sign << 7) | mantissa
+ *   STREAM     uint8[S]    Huffman codes of the palette index of every element
+ *                          of every non-verbatim group, MSB-first; tile t
+ *                          starts at byte TILE_OFF[t]
+ *   GLEN       uint16[G]   coded bits of each group (0 for verbatim groups)
+ *   TILE_OFF   uint32[T+1] stream byte offset of each tile; [T] = S
+ *   TILE_VBASE uint32[T+1] verbatim groups before each tile; [T] = V
+ *   VEXP       uint8[64*V] raw exponent bytes of the verbatim groups, in order
+ *   BITMAP     uint64[T]   bit (g % 64) of word g/64 set iff group g verbatim
+ *   NIB        uint8[N/2]  direct-palette form: palette index of element i in
+ *                          byte i/2, low nibble for even i; 0 in verbatim groups
+ *   DLUT       uint8[2^L]  decode table (derived, not serialized): entry v =
+ *                          (symbol << 4) | length of the codeword that prefixes
+ *                          the L-bit string v, L = longest code length */
+enum {
+    UW_SEC_SM = 0,
+    UW_SEC_STREAM,
+    UW_SEC_GLEN,
+    UW_SEC_TILE_OFF,
+    UW_SEC_TILE_VBASE,
+    UW_SEC_VEXP,
+    UW_SEC_BITMAP,
+    UW_SEC_NIB,
+    UW_SEC_DLUT,
+    UW_NUM_SECTIONS
+};
+
+typedef struct uw_blob uw_blob;
+
+typedef struct {
+    int emit_palette;   /* nonzero: also build the NIB section */
+    int threads;        /* host threads for compression, 0 = all cores */
+} uw_opts;
+
+typedef struct {
+    int64_t rows, cols;
+    int64_t groups, tiles, verbatim_groups;
+    int32_t palette_size;          /* P <= 16 */
+    int32_t lmax;                  /* longest code length, <= 15 */
+    uint8_t palette[16];           /* exponent of palette index s (0 unused) */
+    uint8_t lengths[16];           /* code length of symbol s, 0 = no code */
+    uint16_t codes[16];            /* canonical codeword of symbol s */
+    uint64_t hist[256];            /* exponent histogram (0 after deserialize) */
+    uint64_t section_bytes[UW_NUM_SECTIONS];
+    uint64_t huffman_form_bytes;   /* header + all sections but NIB and DLUT */
+    uint64_t palette_form_bytes;   /* header + SM + NIB + VEXP + BITMAP + TILE_VBASE */
+    int32_t has_palette;           /* NIB section present */
+    int32_t reserved;
+} uw_info;
+
+/* Compress W (host, [rows, cols] bf16 bits) into a new blob.
+ * Page: "How to compress model weights effectively" (field split, top-16
+ * palette, Huffman-coded exponent, verbatim 64-element rows) and "Four ways to
+ * use compressed weights" (the 4-bit form made at load time, opts->emit_palette).
+ * opts may be NULL (no NIB, all cores).  UW_EINVAL if cols % 64 != 0 or a
+ * size is negative; UW_ENOMEM on host allocation failure.  On success *out
+ * owns the result (free with uw_blob_free). */
+int uw_compress(const uint16_t* w /*host*/, int64_t rows, int64_t cols,
+                const uw_opts* opts, uw_blob** out);
+
+/* Fill *info (host) from a blob. */
+int uw_blob_info(const uw_blob* blob, uw_info* info);
+
+/* Borrow a host pointer to section `sec` and its byte size (pointer valid
+ * until uw_blob_free; NULL with size 0 for an empty or absent section). */
+int uw_blob_section(const uw_blob* blob, int sec, const void** ptr, uint64_t* bytes);
+
+/* Serialize to a byte image: a 256-byte header then each stored section at a
+ * 256-byte aligned offset.  With buf == NULL only *need is set.  UW_EINVAL if
+ * cap < *need. */
+int uw_blob_serialize(const uw_blob* blob, void* buf /*host*/, uint64_t cap, uint64_t* need);
+
+/* Parse a serialized image into a new blob and validate it (UW_EFORMAT). */
+int uw_blob_deserialize(const void* buf /*host*/, uint64_t bytes, uw_blob** out);
+
+/* Build the NIB section of a blob that lacks it (host transcode). */
+int uw_blob_add_palette(uw_blob* blob);
+
+void uw_blob_free(uw_blob* blob);
+
+/* Structural checks before any launch: magic sizes, C % 64, palette size,
+ * code lengths (Kraft equality, <= 15), monotone tile offsets, per-tile
+ * sum of GLEN against the tile's bytes, verbatim groups coded with 0 bits,
+ * bitmap popcounts against TILE_VBASE and VEXP, no bitmap bits past G.
+ * UW_EFORMAT with a message on the first violation. */
+int uw_validate(const uw_blob* blob);
+
+/* ------------------------------------------------ device-resident matrices */
+/* A compressed matrix whose sections the caller has copied to device memory.
+ * Pointers of sections a call does not read may be NULL: the Huffman
+ * decoders read SM (full mode only), STREAM, GLEN, TILE_OFF, TILE_VBASE,
+ * VEXP, BITMAP, DLUT; the palette-source matmul reads SM, NIB (or a
+ * transcoded copy), VEXP, BITMAP, TILE_VBASE; the exponent-source matmul
+ * reads SM and a decoded exponent plane. */
+typedef struct {
+    int64_t rows, cols, groups, tiles, verbatim_groups;
+    uint64_t stream_bytes;
+    int32_t palette_size, lmax;
+    uint8_t palette[16];
+    const uint8_t* sm;
+    const uint8_t* stream;
+    const uint16_t* glen;
+    const uint32_t* tile_off;
+    const uint32_t* tile_vbase;
+    const uint8_t* vexp;
+    const uint64_t* bitmap;
+    const uint8_t* nib;
+    const uint8_t* dlut;
+} uw_dmat;
+
+/* Fill a descriptor from blob info (host) and device section pointers
+ * (dev[s] for section s, NULL where absent). */
+int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_SECTIONS]);
+
+/* ------------------------------------------------ preprocessing (decoders) */
+/* Pipeline 1 preprocessing ("Four ways to use compressed weights", full
+ * Huffman decode): rebuild every bf16 weight into out_bf16 [rows, cols].
+ * One wavefront per 64-group tile; lanes find their group's first bit by a
+ * prefix sum of GLEN; the tile's stream and the decode table sit in LDS. */
+int uw_decode_full(const uw_dmat* d, uint16_t* out_bf16, void* stream);
+
+/* Pipeline 2 preprocessing (exponent-only decode): the exponent byte of every
+ * weight, verbatim groups included, into out_e [rows, cols] uint8. */
+int uw_decode_exponents(const uw_dmat* d, uint8_t* out_e, void* stream);
+
+/* Pipeline 3 preprocessing (palette transcode), also the load-time producer of
+ * pipeline 4's form: 4-bit palette indices into out_nib [rows*cols/2], byte
+ * layout of the NIB section (0 in verbatim groups). */
+int uw_transcode_palette(const uw_dmat* d, uint8_t* out_nib, void* stream);
+
+/* ---------------------------------------------------------------- matmuls */
+/* Kernel family selector for the matmuls (the autotuner's search space). */
+enum {
+    UW_KERNEL_AUTO = 0,   /* GEMV below batch 16, MFMA from 16 */
+    UW_KERNEL_GEMV = 1,   /* wavefront-reduction GEMV (v_dot2 bf16), batch <= 16 */
+    UW_KERNEL_MFMA = 2    /* bf16 MFMA tiles, any batch */
+};
+
+/* Uncompressed baseline and pipeline 1's consumer ("Four ways to use
+ * compressed weights": the plain matmul after a full decode).
+ * Y[batch, rows] = X[batch, cols] . W[rows, cols]^T, fp32 accumulate.
+ * `kernel` is a UW_KERNEL_* value; split_k > 1 (MFMA only) needs
+ * uw_scratch_bytes(UW_PIPE_BF16, ...) bytes of scratch, else scratch may be
+ * NULL. */
+int uw_gemm_bf16(const uint16_t* W, int64_t rows, int64_t cols,
+                 const uint16_t* X, int64_t batch, float* Y,
+                 int kernel, int split_k, void* scratch, uint64_t scratch_bytes,
+                 void* stream);
+
+/* Reconstructive matmul, exponent source (pipeline 2's consumer): weights
+ * rebuilt on chip from the decoded exponent plane e [rows, cols] and d->sm.
+ * ("How the reconstructive matmul works".) */
+int uw_gemm_recon_exp(const uw_dmat* d, const uint8_t* e,
+                      const uint16_t* X, int64_t batch, float* Y,
+                      int kernel, int split_k, void* scratch, uint64_t scratch_bytes,
+                      void* stream);
+
+/* Reconstructive matmul, palette source (pipelines 3 and 4): weights rebuilt
+ * on chip from 4-bit indices nib (NIB layout; d->nib for direct palette or a
+ * uw_transcode_palette output), d->sm, and d->vexp for verbatim groups found
+ * through d->bitmap and d->tile_vbase. */
+int uw_gemm_recon_pal(const uw_dmat* d, const uint8_t* nib,
+                      const uint16_t* X, int64_t batch, float* Y,
+                      int kernel, int split_k, void* scratch, uint64_t scratch_bytes,
+                      void* stream);
+
+/* ------------------------------------------------------------- pipelines */
+enum {
+    UW_PIPE_AUTO = 0,     /* consult the plan table (uw_plan_*) */
+    UW_PIPE_FULL = 1,     /* full decode -> bf16 scratch -> bf16 matmul */
+    UW_PIPE_EXP = 2,      /* exponent decode -> u8 scratch -> recon matmul */
+    UW_PIPE_PAL = 3,      /* palette transcode -> nibble scratch -> recon matmul */
+    UW_PIPE_DIRECT = 4,   /* recon matmul on the resident NIB section */
+    UW_PIPE_BF16 = 5      /* uncompressed weights (baseline; not for uw_matmul) */
+};
+
+/* Scratch bytes uw_matmul needs for (pipeline, shape, batch, split_k).
+ * Returns the size (>= 0) or a negative error code. */
+int64_t uw_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch, int split_k);
+
+/* One matmul through a pipeline ("Four ways to use compressed weights").
+ * UW_PIPE_AUTO looks up (rows, cols, batch) in the plan table and falls
+ * back to UW_PIPE_DIRECT (or UW_PIPE_PAL without a NIB section).  scratch
+ * must hold uw_scratch_bytes(...) bytes.  UW_EINVAL on a too-small scratch. */
+int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k,
+              const uint16_t* X, int64_t batch, float* Y,
+              void* scratch, uint64_t scratch_bytes, void* stream);
+
+/* h[i] = bf16_rne(SiLU(g[i]) * u[i]), SiLU(z) = z / (1 + exp(-z)), in fp32;
+ * g, u fp32 [n], h bf16 bits [n].  The step between the gate/up and down
+ * projections of a SwiGLU MLP. */
+int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, void* stream);
+
+/* --------------------------------------------------------------- autotune */
+/* Plan table: (rows, cols, batch) -> (pipeline, kernel, split_k), filled by a
+ * measuring autotuner ("Why no single pipeline wins").  Process-global,
+ * thread-safe.  lookup returns UW_EINVAL when the key is absent. */
+int uw_plan_set(int64_t rows, int64_t cols, int64_t batch, int pipeline, int kernel, int split_k);
+int uw_plan_lookup(int64_t rows, int64_t cols, int64_t batch, int* pipeline, int* kernel, int* split_k);
+int uw_plan_clear(void);
+int uw_plan_count(void);
+/* Text file, one "rows cols batch pipeline kernel split_k" line per entry. */
+int uw_plan_save(const char* path /*host*/);
+int uw_plan_load(const char* path /*host*/);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UNWEIGHT_H */

@@ -1,0 +1,293 @@
+// C ABI entry points of libunweight: argument checks, scratch layout,
+// pipeline composition and kernel dispatch.  See unweight.h for the contract.
+//
+// Pipelines follow Cloudflare, "Unweight: how we compressed an LLM 22% without
+// sacrificing quality", section "Four ways to use compressed weights":
+//   full      Huffman decode -> bf16 in scratch -> plain bf16 matmul
+//   exp       exponent-only decode -> u8 in scratch -> reconstructive matmul
+//   pal       palette transcode -> nibbles in scratch -> reconstructive matmul
+//   direct    reconstructive matmul on nibbles made once at load time
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+#include "uw_internal.h"
+
+namespace {
+
+int hip_fail(hipError_t e, const char* what) {
+    return uw::fail(UW_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+void pack_palette(const uint8_t pal[16], uint32_t out[4]) {
+    for (int i = 0; i < 4; ++i)
+        out[i] = uint32_t(pal[4 * i]) | (uint32_t(pal[4 * i + 1]) << 8) | (uint32_t(pal[4 * i + 2]) << 16) |
+                 (uint32_t(pal[4 * i + 3]) << 24);
+}
+
+int check_dmat(const uw_dmat* d, const char* who) {
+    if (!d) return uw::fail(UW_EINVAL, std::string(who) + ": NULL descriptor");
+    if (d->rows < 0 || d->cols < 0 || d->cols % uw::kGroup)
+        return uw::fail(UW_EINVAL, std::string(who) + ": bad shape");
+    if (d->groups != d->rows * d->cols / uw::kGroup || d->tiles != (d->groups + uw::kTile - 1) / uw::kTile)
+        return uw::fail(UW_EINVAL, std::string(who) + ": inconsistent descriptor sizes");
+    if (d->lmax < 0 || d->lmax > uw::kMaxCodeLen || d->palette_size < 0 || d->palette_size > 16)
+        return uw::fail(UW_EINVAL, std::string(who) + ": bad code/palette size");
+    return UW_OK;
+}
+
+int check_decoder_inputs(const uw_dmat* d, const char* who, bool need_sm) {
+    int rc = check_dmat(d, who);
+    if (rc) return rc;
+    if (d->groups == 0) return UW_OK;
+    if (!d->glen || !d->tile_off || !d->tile_vbase || !d->bitmap || !d->dlut ||
+        (d->stream_bytes && !d->stream) || (d->verbatim_groups && !d->vexp) || (need_sm && !d->sm))
+        return uw::fail(UW_EINVAL, std::string(who) + ": a required device section is NULL");
+    if (!aligned16(d->stream) || !aligned16(d->dlut) || !aligned16(d->vexp) || !aligned16(d->sm))
+        return uw::fail(UW_EINVAL, std::string(who) + ": device sections must be 16-byte aligned");
+    return UW_OK;
+}
+
+uwk::DecodeArgs decode_args(const uw_dmat* d, void* out) {
+    uwk::DecodeArgs a{};
+    a.sm = d->sm;
+    a.stream = d->stream;
+    a.glen = d->glen;
+    a.tile_off = d->tile_off;
+    a.tile_vbase = d->tile_vbase;
+    a.vexp = d->vexp;
+    a.bitmap = d->bitmap;
+    a.dlut = d->dlut;
+    a.stream_bytes = d->stream_bytes;
+    a.G = d->groups;
+    a.T = d->tiles;
+    a.lmax = d->lmax;
+    pack_palette(d->palette, a.pal);
+    a.out = out;
+    return a;
+}
+
+int run_decode(const uw_dmat* d, void* out, int mode, void* stream, const char* who) {
+    uw::clear_error();
+    int rc = check_decoder_inputs(d, who, mode == uwk::MODE_FULL);
+    if (rc) return rc;
+    if (d->groups && (!out || !aligned16(out)))
+        return uw::fail(UW_EINVAL, std::string(who) + ": output must be a 16-byte aligned device pointer");
+    hipError_t e = uwk::launch_decode(mode, decode_args(d, out), as_stream(stream));
+    return e == hipSuccess ? UW_OK : hip_fail(e, who);
+}
+
+// Common checks and dispatch of one matmul.
+int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* scratch, uint64_t scratch_bytes,
+               void* stream, const char* who) {
+    uwk::MatArgs a = a0;
+    if (a.R < 0 || a.C < 0 || a.C % uw::kGroup || a.B < 0)
+        return uw::fail(UW_EINVAL, std::string(who) + ": bad shape (cols must be a multiple of 64)");
+    if (a.B > (int64_t(1) << 24) || a.R > (int64_t(1) << 31) || a.C > (int64_t(1) << 31))
+        return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": size beyond the supported range");
+    if (a.R == 0 || a.B == 0) return UW_OK;
+    if (!a.X || !a.Y || !aligned16(a.X) || !aligned16(a.Y) || (a.R * a.C && (!a.w || !aligned16(a.w))))
+        return uw::fail(UW_EINVAL, std::string(who) + ": NULL or misaligned device pointer");
+    if (src != uwk::SRC_BF16 && a.R * a.C && (!a.sm || !aligned16(a.sm)))
+        return uw::fail(UW_EINVAL, std::string(who) + ": sign/mantissa plane missing");
+    if (src == uwk::SRC_PAL && a.R * a.C && (!a.bitmap || !a.tile_vbase))
+        return uw::fail(UW_EINVAL, std::string(who) + ": verbatim tables missing");
+    if (kernel == UW_KERNEL_AUTO) kernel = a.B < 16 ? UW_KERNEL_GEMV : UW_KERNEL_MFMA;
+    if (kernel == UW_KERNEL_GEMV && a.B > 16)
+        return uw::fail(UW_EINVAL, std::string(who) + ": the GEMV kernel takes batch <= 16");
+    if (kernel != UW_KERNEL_GEMV && kernel != UW_KERNEL_MFMA)
+        return uw::fail(UW_EINVAL, std::string(who) + ": unknown kernel");
+    if (split_k < 1 || split_k > 64) return uw::fail(UW_EINVAL, std::string(who) + ": split_k must be 1..64");
+    hipError_t e;
+    if (kernel == UW_KERNEL_GEMV) {
+        e = uwk::launch_gemv(src, a, as_stream(stream));
+    } else {
+        a.split_k = split_k;
+        if (split_k > 1) {
+            const uint64_t need = uint64_t(split_k) * a.B * a.R * 4;
+            if (!scratch || scratch_bytes < need || !aligned16(scratch))
+                return uw::fail(UW_EINVAL, std::string(who) + ": split_k > 1 needs split_k*batch*rows*4 bytes of scratch");
+            a.partial = static_cast<float*>(scratch);
+        }
+        e = uwk::launch_mfma(src, a, as_stream(stream));
+    }
+    return e == hipSuccess ? UW_OK : hip_fail(e, who);
+}
+
+uwk::MatArgs compressed_args(const uw_dmat* d, const void* w, const uint16_t* X, int64_t batch, float* Y) {
+    uwk::MatArgs a{};
+    a.w = w;
+    a.sm = d->sm;
+    a.vexp = d->vexp;
+    a.bitmap = d->bitmap;
+    a.tile_vbase = d->tile_vbase;
+    a.X = X;
+    a.Y = Y;
+    a.R = d->rows;
+    a.C = d->cols;
+    a.B = batch;
+    a.split_k = 1;
+    pack_palette(d->palette, a.pal);
+    return a;
+}
+
+uint64_t decoded_bytes(int pipeline, int64_t rows, int64_t cols) {
+    const uint64_t n = uint64_t(rows) * uint64_t(cols);
+    switch (pipeline) {
+        case UW_PIPE_FULL: return 2 * n;
+        case UW_PIPE_EXP: return n;
+        case UW_PIPE_PAL: return n / 2;
+        default: return 0;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_SECTIONS]) {
+    uw::clear_error();
+    if (!d || !info || !dev) return uw::fail(UW_EINVAL, "uw_dmat_init: NULL argument");
+    std::memset(d, 0, sizeof(*d));
+    d->rows = info->rows;
+    d->cols = info->cols;
+    d->groups = info->groups;
+    d->tiles = info->tiles;
+    d->verbatim_groups = info->verbatim_groups;
+    d->stream_bytes = info->section_bytes[UW_SEC_STREAM];
+    d->palette_size = info->palette_size;
+    d->lmax = info->lmax;
+    std::memcpy(d->palette, info->palette, 16);
+    d->sm = static_cast<const uint8_t*>(dev[UW_SEC_SM]);
+    d->stream = static_cast<const uint8_t*>(dev[UW_SEC_STREAM]);
+    d->glen = static_cast<const uint16_t*>(dev[UW_SEC_GLEN]);
+    d->tile_off = static_cast<const uint32_t*>(dev[UW_SEC_TILE_OFF]);
+    d->tile_vbase = static_cast<const uint32_t*>(dev[UW_SEC_TILE_VBASE]);
+    d->vexp = static_cast<const uint8_t*>(dev[UW_SEC_VEXP]);
+    d->bitmap = static_cast<const uint64_t*>(dev[UW_SEC_BITMAP]);
+    d->nib = static_cast<const uint8_t*>(dev[UW_SEC_NIB]);
+    d->dlut = static_cast<const uint8_t*>(dev[UW_SEC_DLUT]);
+    return check_dmat(d, "uw_dmat_init");
+}
+
+int uw_decode_full(const uw_dmat* d, uint16_t* out_bf16, void* stream) {
+    return run_decode(d, out_bf16, uwk::MODE_FULL, stream, "uw_decode_full");
+}
+
+int uw_decode_exponents(const uw_dmat* d, uint8_t* out_e, void* stream) {
+    return run_decode(d, out_e, uwk::MODE_EXP, stream, "uw_decode_exponents");
+}
+
+int uw_transcode_palette(const uw_dmat* d, uint8_t* out_nib, void* stream) {
+    return run_decode(d, out_nib, uwk::MODE_PAL, stream, "uw_transcode_palette");
+}
+
+int uw_gemm_bf16(const uint16_t* W, int64_t rows, int64_t cols, const uint16_t* X, int64_t batch, float* Y,
+                 int kernel, int split_k, void* scratch, uint64_t scratch_bytes, void* stream) {
+    uw::clear_error();
+    uwk::MatArgs a{};
+    a.w = W;
+    a.X = X;
+    a.Y = Y;
+    a.R = rows;
+    a.C = cols;
+    a.B = batch;
+    a.split_k = 1;
+    return run_matmul(uwk::SRC_BF16, a, kernel, split_k, scratch, scratch_bytes, stream, "uw_gemm_bf16");
+}
+
+int uw_gemm_recon_exp(const uw_dmat* d, const uint8_t* e, const uint16_t* X, int64_t batch, float* Y, int kernel,
+                      int split_k, void* scratch, uint64_t scratch_bytes, void* stream) {
+    uw::clear_error();
+    int rc = check_dmat(d, "uw_gemm_recon_exp");
+    if (rc) return rc;
+    return run_matmul(uwk::SRC_EXP, compressed_args(d, e, X, batch, Y), kernel, split_k, scratch, scratch_bytes,
+                      stream, "uw_gemm_recon_exp");
+}
+
+int uw_gemm_recon_pal(const uw_dmat* d, const uint8_t* nib, const uint16_t* X, int64_t batch, float* Y, int kernel,
+                      int split_k, void* scratch, uint64_t scratch_bytes, void* stream) {
+    uw::clear_error();
+    int rc = check_dmat(d, "uw_gemm_recon_pal");
+    if (rc) return rc;
+    if (d->groups && d->verbatim_groups && !d->vexp)
+        return uw::fail(UW_EINVAL, "uw_gemm_recon_pal: verbatim exponents missing");
+    return run_matmul(uwk::SRC_PAL, compressed_args(d, nib, X, batch, Y), kernel, split_k, scratch, scratch_bytes,
+                      stream, "uw_gemm_recon_pal");
+}
+
+int64_t uw_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch, int split_k) {
+    uw::clear_error();
+    if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_BF16 || rows < 0 || cols < 0 || batch < 0 || split_k < 1)
+        return uw::fail(UW_EINVAL, "uw_scratch_bytes: bad argument");
+    uint64_t n = align256(decoded_bytes(pipeline, rows, cols));
+    if (split_k > 1) n += align256(uint64_t(split_k) * uint64_t(batch) * uint64_t(rows) * 4);
+    return int64_t(n);
+}
+
+int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k, const uint16_t* X, int64_t batch, float* Y,
+              void* scratch, uint64_t scratch_bytes, void* stream) {
+    uw::clear_error();
+    int rc = check_dmat(d, "uw_matmul");
+    if (rc) return rc;
+    if (pipeline == UW_PIPE_AUTO) {
+        int p, k, s;
+        if (uw_plan_lookup(d->rows, d->cols, batch, &p, &k, &s) == UW_OK) {
+            pipeline = p;
+            kernel = k;
+            split_k = s;
+        } else {
+            pipeline = d->nib ? UW_PIPE_DIRECT : UW_PIPE_PAL;
+            kernel = UW_KERNEL_AUTO;
+            split_k = 1;
+        }
+        uw::clear_error();
+    }
+    if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_DIRECT)
+        return uw::fail(UW_EINVAL, "uw_matmul: pipeline must be UW_PIPE_AUTO or FULL/EXP/PAL/DIRECT");
+    if (pipeline == UW_PIPE_DIRECT && d->groups && !d->nib)
+        return uw::fail(UW_EINVAL, "uw_matmul: direct palette needs the NIB section on the device");
+    const int64_t need = uw_scratch_bytes(pipeline, d->rows, d->cols, batch, split_k);
+    if (need < 0) return int(need);
+    if (uint64_t(need) > scratch_bytes || (need > 0 && (!scratch || !aligned16(scratch))))
+        return uw::fail(UW_EINVAL, "uw_matmul: scratch smaller than uw_scratch_bytes()");
+    uint8_t* dec = static_cast<uint8_t*>(scratch);
+    const uint64_t dec_bytes = align256(decoded_bytes(pipeline, d->rows, d->cols));
+    void* part = dec_bytes ? dec + dec_bytes : scratch;
+    const uint64_t part_bytes = scratch_bytes - dec_bytes;
+    switch (pipeline) {
+        case UW_PIPE_FULL:
+            rc = uw_decode_full(d, reinterpret_cast<uint16_t*>(dec), stream);
+            if (rc) return rc;
+            return uw_gemm_bf16(reinterpret_cast<uint16_t*>(dec), d->rows, d->cols, X, batch, Y, kernel, split_k, part,
+                                part_bytes, stream);
+        case UW_PIPE_EXP:
+            rc = uw_decode_exponents(d, dec, stream);
+            if (rc) return rc;
+            return uw_gemm_recon_exp(d, dec, X, batch, Y, kernel, split_k, part, part_bytes, stream);
+        case UW_PIPE_PAL:
+            rc = uw_transcode_palette(d, dec, stream);
+            if (rc) return rc;
+            return uw_gemm_recon_pal(d, dec, X, batch, Y, kernel, split_k, part, part_bytes, stream);
+        default:
+            return uw_gemm_recon_pal(d, d->nib, X, batch, Y, kernel, split_k, part, part_bytes, stream);
+    }
+}
+
+int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, void* stream) {
+    uw::clear_error();
+    if (n < 0) return uw::fail(UW_EINVAL, "uw_silu_mul_bf16: negative n");
+    if (n == 0) return UW_OK;
+    if (!g || !u || !h || !aligned16(g) || !aligned16(u) || !aligned16(h))
+        return uw::fail(UW_EINVAL, "uw_silu_mul_bf16: NULL or misaligned pointer");
+    hipError_t e = uwk::launch_silu_mul(g, u, n, h, as_stream(stream));
+    return e == hipSuccess ? UW_OK : hip_fail(e, "uw_silu_mul_bf16");
+}
+
+}  // extern "C"

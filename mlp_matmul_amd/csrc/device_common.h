@@ -1,0 +1,75 @@
+// Device helpers shared by the gfx950 kernels of libunweight.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace uwk {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bswap32(uint32_t v) {
+    // byte reverse: selector picks bytes 3,2,1,0 of v
+    return __builtin_amdgcn_perm(0u, v, 0x00010203u);
+}
+
+// Two bf16 weights (elements 2q and 2q+1 of a 4-element group) as one dword,
+// low half = even element.  `sm4` holds 4 sign/mantissa bytes, `e7pair` the
+// two exponents already shifted into bf16 position: e_even << 7 | e_odd << 23.
+// sign -> bit 15, mantissa -> bits 6..0 of each half.
+template <int Q>
+__device__ __forceinline__ uint32_t join_pair(uint32_t sm4, uint32_t e7pair) {
+    constexpr uint32_t sel = Q == 0 ? 0x01010000u : 0x03030202u;  // [a, a, b, b]
+    uint32_t smp = __builtin_amdgcn_perm(0u, sm4, sel);
+    return (smp & 0x807F807Fu) | e7pair;
+}
+
+// e_even << 7 | e_odd << 23 from exponent bytes 2Q, 2Q+1 of `e4`.
+template <int Q>
+__device__ __forceinline__ uint32_t exp_pair(uint32_t e4) {
+    constexpr uint32_t sel = Q == 0 ? 0x010C000Cu : 0x030C020Cu;  // [0, a, 0, b]
+    return __builtin_amdgcn_perm(0u, e4, sel) >> 1;
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+// Load 16 bytes with a streaming (non-temporal) hint: the data is read once.
+__device__ __forceinline__ u32x4_t load_stream16(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ u32x2_t load_stream8(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void store16(void* p, u32x4_t v) {
+    *reinterpret_cast<u32x4_t*>(p) = v;
+}
+
+// Index of a verbatim group among all verbatim groups: the count before its
+// tile plus the flagged groups before it inside the tile's bitmap word.
+__device__ __forceinline__ uint32_t verbatim_slot(uint64_t word, uint32_t bit, uint32_t vbase) {
+    uint64_t below = bit ? (word & ((~0ull) >> (64 - bit))) : 0ull;
+    return vbase + uint32_t(__popcll(below));
+}
+
+}  // namespace uwk

@@ -1,0 +1,52 @@
+// Kernel argument blocks and launchers (host-callable) of libunweight.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace uwk {
+
+enum DecodeMode { MODE_FULL = 0, MODE_EXP = 1, MODE_PAL = 2 };
+enum WeightSource { SRC_BF16 = 0, SRC_EXP = 1, SRC_PAL = 2 };
+
+struct DecodeArgs {
+    const uint8_t* sm;
+    const uint8_t* stream;
+    const uint16_t* glen;
+    const uint32_t* tile_off;
+    const uint32_t* tile_vbase;
+    const uint8_t* vexp;
+    const uint64_t* bitmap;
+    const uint8_t* dlut;
+    uint64_t stream_bytes;
+    int64_t G, T;
+    int32_t lmax;
+    int32_t buf_words;   // LDS dwords per wave for one staged tile stream
+    uint32_t pal[4];     // palette bytes, index s in byte s%4 of pal[s/4]
+    void* out;
+};
+
+// Weights of one matmul and where they come from.
+struct MatArgs {
+    const void* w;              // SRC_BF16: bf16 W; SRC_EXP: exponent plane; SRC_PAL: nibbles
+    const uint8_t* sm;          // sign/mantissa plane (SRC_EXP, SRC_PAL)
+    const uint8_t* vexp;        // SRC_PAL: verbatim exponents
+    const uint64_t* bitmap;     // SRC_PAL: verbatim bitmap
+    const uint32_t* tile_vbase; // SRC_PAL: verbatim groups before each tile
+    const uint16_t* X;          // [B, C] bf16
+    float* Y;                   // [B, R] fp32
+    float* partial;             // split-K partial sums [split, B, R] (MFMA)
+    int64_t R, C, B;
+    int32_t split_k;
+    uint32_t pal[4];
+};
+
+hipError_t launch_decode(int mode, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_gemv(int src, const MatArgs& a, hipStream_t s);
+hipError_t launch_mfma(int src, const MatArgs& a, hipStream_t s);
+hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, uint16_t* h, hipStream_t s);
+
+// LDS bytes the decoder needs for a code of longest length lmax.
+size_t decode_lds_bytes(int lmax, int* buf_words);
+
+}  // namespace uwk

@@ -1,0 +1,46 @@
+// Internal declarations shared by the host translation units of libunweight.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "unweight.h"
+
+namespace uw {
+
+constexpr int kGroup = 64;       // elements per verbatim decision
+constexpr int kTile = 64;        // groups per stream tile
+constexpr int kPaletteMax = 16;  // 4-bit palette indices
+constexpr int kMaxCodeLen = 15;  // 16 symbols -> Huffman depth <= 15
+constexpr uint64_t kHeaderBytes = 256;
+
+// Record a message for uw_last_error() and return the code.
+int fail(int code, const std::string& msg);
+void clear_error();
+
+}  // namespace uw
+
+struct uw_blob {
+    int64_t rows = 0, cols = 0;
+    int64_t N = 0, G = 0, T = 0, V = 0;
+    int32_t P = 0, lmax = 0;
+    uint8_t palette[16] = {};
+    uint8_t lengths[16] = {};
+    uint16_t codes[16] = {};
+    uint64_t hist[256] = {};
+    bool has_nib = false;
+    std::vector<uint8_t> sm, stream, vexp, nib, dlut;
+    std::vector<uint16_t> glen;
+    std::vector<uint32_t> tile_off, tile_vbase;
+    std::vector<uint64_t> bitmap;
+};
+
+namespace uw {
+// Canonical codewords from code lengths (symbols in (length, symbol) order).
+void canonical_codes(const uint8_t lengths[16], uint16_t codes[16]);
+// Decode table of 2^lmax entries: (symbol << 4) | length.
+void build_dlut(uw_blob& b);
+// Direct-palette nibbles from the exponent of every element.
+void build_nibbles(uw_blob& b, const uint8_t* e, int threads);
+}  // namespace uw

@@ -1,0 +1,53 @@
+"""The C-ABI library loads and exports every function include/unweight.h
+declares, and the binding's struct mirrors match the compiled sizes.  No
+device calls."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import mlp_matmul_amd as uw
+from mlp_matmul_amd import _capi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "unweight.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(uw_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_signatures():
+    assert _declared() == sorted(_capi.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _capi.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (uw_[a-z0-9_]+)\b", out))
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+
+
+def test_library_loads_and_struct_sizes_match():
+    L = uw.lib()   # raises on a size mismatch
+    assert L.uw_version() >> 16 == 1
+
+
+def test_errors_are_reported_not_raised():
+    L = uw.lib()
+    import ctypes as ct
+    h = ct.c_void_p()
+    rc = L.uw_compress(None, 1, 100, None, ct.byref(h))
+    assert rc == _capi.UW_EINVAL
+    assert b"multiple of 64" in L.uw_last_error()
+    assert L.uw_scratch_bytes(99, 1, 64, 1, 1) == _capi.UW_EINVAL
+
+
+def test_no_fallback_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(_capi, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_capi, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _capi.lib()

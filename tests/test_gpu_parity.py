@@ -1,0 +1,332 @@
+"""GPU parity: libunweight's gfx950 kernels against the CPU oracle.
+
+Decoders are bit-exact on every element; matmuls are within 2e-3 of
+sum |w*x| per output (fp32 accumulation against the fp64 oracle); the
+one-hot activations pin the in-kernel reconstruction bit-exactly.
+Every input comes from the seeded generators in workloads.py.
+"""
+import numpy as np
+import pytest
+
+import mlp_matmul_amd as uw
+from oracle import codec, numerics
+import workloads
+from tests.gpu_util import (TOL, assert_matmul_close, from_dev_bits, from_dev_u8, print_case,
+                            to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    uw.lib()
+    return torch
+
+
+def _expected_nibbles(w):
+    """4-bit palette indices from the oracle's palette and verbatim flags."""
+    e, _ = codec.split_fields(w.ravel())
+    pal = codec.top16_palette(codec.exponent_histogram(e))
+    vflag = codec.verbatim_flags(e, pal)
+    return codec.pack_nibbles(codec.element_symbols(e, pal, vflag))
+
+
+def _check_decoders(dm, w, exp_nib=None):
+    import torch
+    full = uw.decode_full(dm)
+    exps = uw.decode_exponents(dm)
+    nib = uw.transcode_palette(dm)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_bits(full), w), "full decode"
+    assert np.array_equal(from_dev_u8(exps), ((w >> 7) & 0xFF).astype(np.uint8)), "exponent decode"
+    if exp_nib is None:
+        exp_nib = _expected_nibbles(w)
+    assert np.array_equal(from_dev_u8(nib), exp_nib), "palette transcode"
+    return full, exps, nib
+
+
+# ------------------------------------------------------------------ decoders
+def test_decoders_small_workload(torch_cuda):
+    print_case("decoders: 512x1024 small workload")
+    w, _ = workloads.small_matrix()
+    ref = codec.encode(w)
+    dm = uw.compress(w).to_device()
+    _check_decoders(dm, w, ref.nib)
+    # the decoders match the oracle's own decode of the same stream too
+    assert np.array_equal(codec.decode_parallel(ref, "full"), w)
+
+
+@pytest.mark.parametrize("case", ["single", "spread", "allverbatim", "special", "partial", "one_group", "empty"])
+def test_decoders_edge_cases(torch_cuda, case):
+    print_case(f"decoders edge case {case}")
+    rng = np.random.default_rng(7)
+    if case == "single":
+        w = ((rng.integers(0, 2, (9, 192)).astype(np.uint16) << 15) | (119 << 7)
+             | rng.integers(0, 128, (9, 192)).astype(np.uint16)).astype(np.uint16)
+    elif case == "spread":
+        w = ((rng.integers(0, 2, (33, 256)).astype(np.uint16) << 15)
+             | (rng.integers(90, 122, (33, 256)).astype(np.uint16) << 7)
+             | rng.integers(0, 128, (33, 256)).astype(np.uint16)).astype(np.uint16)
+    elif case == "allverbatim":
+        w = workloads.random_bf16_bits(11, 64 * 700).reshape(350, 128)
+    elif case == "special":
+        w = workloads.gaussian_weights(rng, 70, 320, 0.02, 0.01, 1.0)
+        flat = w.ravel()
+        sp = np.array([0, 0x8000, 1, 0x807F, 0x7F80, 0xFF80, 0x7FC0, 0x7F81, 0xFFFF], np.uint16)
+        flat[rng.choice(flat.size, sp.size * 5, replace=False)] = np.tile(sp, 5)
+    elif case == "partial":
+        w = workloads.gaussian_weights(rng, 129, 64 * 3, 0.02, 0.003, 1.0)
+    elif case == "one_group":
+        w = workloads.gaussian_weights(rng, 1, 64, 0.02)
+    else:
+        w = np.zeros((0, 128), np.uint16)
+    dm = uw.compress(w).to_device()
+    if w.size == 0:
+        uw.decode_full(dm)
+        return
+    _check_decoders(dm, w)
+
+
+@pytest.mark.parametrize("wl,m", [(2, 0), (2, 2), (4, 1), (5, 2)])
+def test_decoders_full_size(torch_cuda, wl, m):
+    print_case(f"decoders full size workload {wl} matrix {m}")
+    w = workloads.layer_weight(wl, 0 if wl != 5 else 17, m)
+    dm = uw.compress(w).to_device()
+    _check_decoders(dm, w)
+
+
+# --------------------------------------------------------------- one-hot pin
+def _one_hot(cols, C):
+    x = np.zeros((len(cols), C), np.uint16)
+    x[np.arange(len(cols)), cols] = 0x3F80     # bf16 1.0
+    return x
+
+
+@pytest.mark.parametrize("kernel", [uw.UW_KERNEL_GEMV, uw.UW_KERNEL_MFMA])
+def test_one_hot_reveals_rebuilt_weights(torch_cuda, kernel):
+    """With X = rows of the identity, Y[b, r] = W[r, c_b] exactly: the fused
+    kernels reveal the weights they rebuilt without writing them out."""
+    print_case(f"one-hot pin kernel {kernel}")
+    w, _ = workloads.small_matrix()
+    dm = uw.compress(w).to_device()
+    exps = uw.decode_exponents(dm)
+    vflag = codec.encode(w).vflag.reshape(w.shape[0], -1)
+    # columns inside groups that are verbatim in many rows, plus ordinary ones
+    hot = np.argsort(-vflag.sum(axis=0))[:8] * 64 + np.array([0, 5, 17, 63, 31, 40, 2, 62])
+    cols = np.concatenate([hot, np.arange(8) * 111 + 3])
+    x = _one_hot(cols, w.shape[1])
+    X = to_dev_bf16(x)
+    expect = numerics.bf16_to_f64(w[:, cols].T).astype(np.float32)
+    outs = {
+        "bf16": uw.gemm_bf16(to_dev_bf16(w), X, kernel=kernel),
+        "direct": uw.gemm_recon_pal(dm, None, X, kernel=kernel),
+        "exp": uw.gemm_recon_exp(dm, exps, X, kernel=kernel),
+    }
+    torch_cuda.cuda.synchronize()
+    for name, Y in outs.items():
+        got = Y.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), expect.view(np.uint32)), name
+
+
+# ------------------------------------------------------------------ matmuls
+def _x(seed, B, C):
+    return workloads.gaussian_activations(np.random.default_rng(seed), B, C)
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 7, 8, 12, 16])
+def test_gemv_small_workload(torch_cuda, B):
+    print_case(f"gemv small workload B={B}")
+    w, _ = workloads.small_matrix()
+    x = _x(B, B, w.shape[1])
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    exps = uw.decode_exponents(dm)
+    for name, Y in [("bf16", uw.gemm_bf16(to_dev_bf16(w), X, kernel=uw.UW_KERNEL_GEMV)),
+                    ("direct", uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_GEMV)),
+                    ("exp", uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_GEMV))]:
+        assert_matmul_close(Y.cpu().numpy(), w, x, what=f"gemv {name} B={B}")
+
+
+@pytest.mark.parametrize("B", [1, 5, 16, 17, 33, 64, 100, 128, 200, 256, 300])
+def test_mfma_small_workload(torch_cuda, B):
+    print_case(f"mfma small workload B={B}")
+    w, _ = workloads.small_matrix()
+    x = _x(100 + B, B, w.shape[1])
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    exps = uw.decode_exponents(dm)
+    for name, Y in [("bf16", uw.gemm_bf16(to_dev_bf16(w), X, kernel=uw.UW_KERNEL_MFMA)),
+                    ("direct", uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_MFMA)),
+                    ("exp", uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_MFMA))]:
+        assert_matmul_close(Y.cpu().numpy(), w, x, what=f"mfma {name} B={B}")
+
+
+@pytest.mark.parametrize("split", [2, 3, 4, 16])
+def test_mfma_split_k(torch_cuda, split):
+    print_case(f"mfma split_k={split}")
+    w = workloads.layer_weight(2, 3, 2, shape=(200, 14336))
+    x = _x(split, 40, w.shape[1])
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    scratch = uw.alloc_scratch(uw.UW_PIPE_DIRECT, 200, 14336, 40, split)
+    Y = uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_MFMA, split_k=split, scratch=scratch)
+    assert_matmul_close(Y.cpu().numpy(), w, x, what=f"split {split}")
+
+
+@pytest.mark.parametrize("R,C", [(1, 64), (3, 128), (37, 192), (130, 1088), (67, 2048 + 64)])
+@pytest.mark.parametrize("B", [1, 6, 16, 40])
+def test_ragged_shapes(torch_cuda, R, C, B):
+    print_case(f"ragged R={R} C={C} B={B}")
+    w = workloads.gaussian_weights(np.random.default_rng(R * C + B), R, C, 0.02, 0.004, 1.0)
+    x = _x(R + B, B, C)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    kernels = [uw.UW_KERNEL_MFMA] + ([uw.UW_KERNEL_GEMV] if B <= 16 else [])
+    for k in kernels:
+        for name, Y in [("bf16", uw.gemm_bf16(to_dev_bf16(w), X, kernel=k)),
+                        ("direct", uw.gemm_recon_pal(dm, None, X, kernel=k))]:
+            assert_matmul_close(Y.cpu().numpy(), w, x, what=f"{name} k={k}")
+
+
+def test_empty_and_zero_batch(torch_cuda):
+    import torch
+    w = np.zeros((0, 128), np.uint16)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(_x(0, 3, 128))
+    Y = uw.gemm_recon_pal(dm, None, X)
+    assert Y.shape == (3, 0)
+    w2, _ = workloads.small_matrix()
+    dm2 = uw.compress(w2).to_device()
+    X0 = torch.empty((0, 1024), dtype=torch.bfloat16, device="cuda")
+    Y0 = uw.gemm_recon_pal(dm2, None, X0)
+    assert Y0.shape == (0, 512)
+
+
+# ---------------------------------------------------------------- pipelines
+@pytest.mark.parametrize("B", [1, 4, 16, 64])
+def test_four_pipelines_small_workload(torch_cuda, B):
+    print_case(f"pipelines small workload B={B}")
+    w, _ = workloads.small_matrix()
+    x = _x(200 + B, B, w.shape[1])
+    X = to_dev_bf16(x)
+    dm = uw.compress(w).to_device()
+    base = uw.gemm_bf16(to_dev_bf16(w), X)
+    outs = {}
+    for name, p in uw.PIPELINES.items():
+        scratch = uw.alloc_scratch(p, w.shape[0], w.shape[1], B)
+        outs[name] = uw.matmul(dm, X, pipeline=p, scratch=scratch).cpu().numpy()
+        assert_matmul_close(outs[name], w, x, what=f"pipeline {name} B={B}")
+    # full decode feeds the same bf16 kernel as the baseline: identical bits
+    assert np.array_equal(outs["full"].view(np.uint32), base.cpu().numpy().view(np.uint32))
+    # the palette pipelines run the same kernel on identical nibbles
+    assert np.array_equal(outs["pal"].view(np.uint32), outs["direct"].view(np.uint32))
+
+
+def test_deterministic(torch_cuda):
+    w, _ = workloads.small_matrix()
+    dm = uw.compress(w).to_device()
+    for B, k in [(1, uw.UW_KERNEL_GEMV), (64, uw.UW_KERNEL_MFMA)]:
+        X = to_dev_bf16(_x(B, B, 1024))
+        a = uw.gemm_recon_pal(dm, None, X, kernel=k).cpu().numpy()
+        b = uw.gemm_recon_pal(dm, None, X, kernel=k).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_auto_plan_dispatch(torch_cuda):
+    w, _ = workloads.small_matrix()
+    x = _x(5, 4, 1024)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    uw.plan_clear()
+    uw.plan_set(512, 1024, 4, uw.UW_PIPE_EXP, uw.UW_KERNEL_MFMA, 2)
+    scratch = uw.alloc_scratch(uw.UW_PIPE_EXP, 512, 1024, 4, 2)
+    Y = uw.matmul(dm, X, pipeline=uw.UW_PIPE_AUTO, scratch=scratch)
+    assert_matmul_close(Y.cpu().numpy(), w, x, what="auto")
+    uw.plan_clear()
+    Y2 = uw.matmul(dm, X)       # no plan entry: direct palette, no scratch
+    assert_matmul_close(Y2.cpu().numpy(), w, x, what="auto default")
+
+
+def test_scratch_too_small_is_rejected(torch_cuda):
+    w, _ = workloads.small_matrix()
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(_x(1, 1, 1024))
+    small = uw.alloc_scratch(uw.UW_PIPE_PAL, 512, 1024, 1)[:100]
+    with pytest.raises(uw.UnweightError):
+        uw.matmul(dm, X, pipeline=uw.UW_PIPE_FULL, scratch=small)
+
+
+# ---------------------------------------------------------------- SiLU chain
+def test_silu_mul_within_one_ulp(torch_cuda):
+    import torch
+    rng = np.random.default_rng(3)
+    g = (rng.standard_normal(10007) * 4).astype(np.float32)
+    u = (rng.standard_normal(10007) * 4).astype(np.float32)
+    g[:6] = [0.0, -0.0, 80.0, -80.0, 1e-30, -1e-30]
+    h = uw.silu_mul_bf16(torch.from_numpy(g).cuda(), torch.from_numpy(u).cuda())
+    got = from_dev_bits(h).astype(np.int64)
+    ref = numerics.f64_to_bf16_bits(numerics.silu_mul(g, u)).astype(np.int64)
+    # compare as ordered integers: at most one bf16 ulp apart
+    def key(b):
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    assert np.abs(key(got) - key(ref)).max() <= 1
+
+
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_mlp_layer_chain(torch_cuda, B):
+    """gate/up -> bf16(SiLU(g)*u) -> down on reduced-width layer shapes."""
+    print_case(f"mlp chain B={B}")
+    F, H = 1536, 512
+    wg = workloads.layer_weight(3, 0, 0, shape=(F, H))
+    wu = workloads.layer_weight(3, 0, 1, shape=(F, H))
+    wd = workloads.layer_weight(3, 0, 2, shape=(H, F))
+    x = workloads.layer_activation(3, 0, 0, B, cols=H)
+    dms = [uw.compress(m).to_device() for m in (wg, wu, wd)]
+    X = to_dev_bf16(x)
+    g = uw.matmul(dms[0], X, pipeline=uw.UW_PIPE_DIRECT)
+    u = uw.matmul(dms[1], X, pipeline=uw.UW_PIPE_DIRECT)
+    h = uw.silu_mul_bf16(g, u)
+    y = uw.matmul(dms[2], h, pipeline=uw.UW_PIPE_DIRECT)
+    gn, un = g.cpu().numpy(), u.cpu().numpy()
+    assert_matmul_close(gn, wg, x, what="gate")
+    assert_matmul_close(un, wu, x, what="up")
+    hb = from_dev_bits(h)
+    href = numerics.f64_to_bf16_bits(numerics.silu_mul(gn, un))
+    key = lambda b: np.where(b & 0x8000, -(b.astype(np.int64) & 0x7FFF), b.astype(np.int64) & 0x7FFF)
+    assert np.abs(key(hb) - key(href)).max() <= 1
+    assert_matmul_close(y.cpu().numpy(), wd, hb, what="down")
+
+
+# --------------------------------------------------------------- full sizes
+@pytest.mark.parametrize("m", [0, 2])
+def test_full_size_gemv_batch1_all_pipelines(torch_cuda, m):
+    """Llama-3.1-8B gate and down at batch 1, in the launch configuration the
+    benchmark times: every output against the fp64 oracle."""
+    print_case(f"full-size batch-1 pipelines matrix {m}")
+    w = workloads.layer_weight(2, 0, m)
+    x = workloads.layer_activation(2, 0, m, 1)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    Yb = uw.gemm_bf16(to_dev_bf16(w), X).cpu().numpy()
+    assert_matmul_close(Yb, w, x, what="bf16")
+    for name, p in uw.PIPELINES.items():
+        scratch = uw.alloc_scratch(p, w.shape[0], w.shape[1], 1)
+        Y = uw.matmul(dm, X, pipeline=p, scratch=scratch).cpu().numpy()
+        rel = assert_matmul_close(Y, w, x, what=f"{name}")
+        assert rel < TOL
+
+
+@pytest.mark.parametrize("B", [64, 128, 256])
+def test_full_size_mfma_row_spread_workload(torch_cuda, B):
+    """Per-row-scaled weights at large batch: sampled rows against the oracle."""
+    print_case(f"full-size per-row sigma B={B}")
+    w = workloads.layer_weight(4, 0, 0)
+    x = workloads.layer_activation(4, 0, 0, B)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    rows = np.sort(np.random.default_rng(B).choice(w.shape[0], 512, replace=False))
+    for name, Y in [("bf16", uw.gemm_bf16(to_dev_bf16(w), X)),
+                    ("direct", uw.gemm_recon_pal(dm, None, X))]:
+        assert_matmul_close(Y.cpu().numpy()[:, rows], w, x, rows=rows, what=f"{name} B={B}")
