@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""Benchmark: compressed-MLP matmul on one MI355X.
+
+One step = one forward of a Llama-3.1-8B-shaped MLP layer at batch B (default
+1): gate and up projections of the same activation, h = bf16(SiLU(g) * u),
+then the down projection -- all through one pipeline of the Unweight method
+(default: direct palette, the fused reconstructive matmul over 4-bit indices
+made at load time).  Weights are synthetic with Llama's shapes (seeded,
+N(0,0.02) + 0.05% N(0,0.5) outliers); steps rotate over --layers independent
+layer copies (default 4, ~1.1 GB compressed) so the 256 MiB Infinity Cache
+cannot serve them.
+
+Prints one JSON line: bf16-equivalent weight GB/s of the whole step, the
+dominant kernel's roofline (HIP events on its stream over the timed region),
+the uncompressed-bf16 baseline and the other pipelines on the same workload,
+and the CPU oracle timed on a bounded sample on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-MLP matmul: bf16-equiv weight GB/s, % HBM peak, batch 1\u2013256"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--pipeline", default="direct", choices=["direct", "pal", "exp", "full", "auto"])
+    p.add_argument("--layers", type=int, default=4, help="layer copies rotated through (MALL defeat)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-compare", action="store_true", help="skip the other pipelines and the bf16 baseline")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also launch a plain device copy of known size (for counter calibration)")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ workload
+class Layer:
+    """One MLP layer: compressed matrices on the device plus raw bf16 copies."""
+
+    def __init__(self, layer, keep_bf16):
+        import torch
+        import mlp_matmul_amd as uw
+        import workloads
+        self.mats, self.bf16, self.info = [], [], []
+        for m in range(3):
+            w = workloads.layer_weight(2, layer, m)
+            blob = uw.compress(w, emit_palette=True)
+            dm = blob.to_device(uw.DECODE_SECTIONS + ("nib",))
+            self.mats.append(dm)
+            self.info.append(dm.info)
+            if keep_bf16:
+                self.bf16.append(torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda())
+            del w, blob
+
+
+def palette_bytes(info, batch):
+    """Algorithmic bytes one direct-palette matmul launch must move: the 4-bit
+    form (sign/mantissa plane, nibbles, verbatim exponents, bitmap, verbatim
+    bases) + activations in + fp32 outputs."""
+    sb = info.section_bytes
+    import mlp_matmul_amd as uw
+    w = (sb[uw.UW_SEC_SM] + info.rows * info.cols // 2 + sb[uw.UW_SEC_VEXP] + sb[uw.UW_SEC_BITMAP]
+         + sb[uw.UW_SEC_TILE_VBASE])
+    return int(w + 2 * batch * info.cols + 4 * batch * info.rows)
+
+
+class Step:
+    """Preallocated buffers and pre-bound C-ABI calls of one layer forward, so
+    that the host issues a step in a few microseconds and the GPU queue stays
+    ahead of it (the timed region measures the GPU, not Python)."""
+
+    def __init__(self, layers, batch, pipeline, kernel_events=0):
+        import ctypes as ct
+        import functools
+        import torch
+        import mlp_matmul_amd as uw
+        import workloads
+        self.torch = torch
+        self.layers, self.B = layers, batch
+        pipe = {"direct": uw.UW_PIPE_DIRECT, "pal": uw.UW_PIPE_PAL, "exp": uw.UW_PIPE_EXP,
+                "full": uw.UW_PIPE_FULL, "auto": uw.UW_PIPE_AUTO, "bf16": uw.UW_PIPE_BF16}[pipeline]
+        F, H = workloads.LLAMA_FFN, workloads.LLAMA_HIDDEN
+        self.X = [torch.from_numpy(workloads.layer_activation(2, i, 0, batch).view(np.int16))
+                  .view(torch.bfloat16).cuda() for i in range(len(layers))]
+        self.g = torch.empty((batch, F), dtype=torch.float32, device="cuda")
+        self.u = torch.empty_like(self.g)
+        self.h = torch.empty((batch, F), dtype=torch.bfloat16, device="cuda")
+        self.y = torch.empty((batch, H), dtype=torch.float32, device="cuda")
+        sp = pipe if pipe not in (uw.UW_PIPE_AUTO, uw.UW_PIPE_BF16) else uw.UW_PIPE_FULL
+        nscr = max(uw.scratch_bytes(sp, F, H, batch, 4), uw.scratch_bytes(sp, H, F, batch, 4))
+        self.scratch = torch.empty(nscr, dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.current_stream()
+        L = uw.lib()
+        st = ct.c_void_p(self.stream.cuda_stream)
+        P = lambda t: ct.c_void_p(t.data_ptr())
+        scr, nsc = P(self.scratch), ct.c_uint64(self.scratch.numel())
+        self.calls = []          # per layer: [gate, up, silu, down] bound calls
+        self.bytes = []          # per layer: algorithmic bytes of gate, up, down
+        for li, lay in enumerate(layers):
+            X = P(self.X[li])
+            outs = [(X, P(self.g)), (X, P(self.u)), (P(self.h), P(self.y))]
+            row = []
+            for m in range(3):
+                xin, yout = outs[m]
+                if pipe == uw.UW_PIPE_BF16:
+                    R, C = lay.bf16[m].shape
+                    row.append(functools.partial(L.uw_gemm_bf16, P(lay.bf16[m]), R, C, xin, batch, yout, 0, 1,
+                                                 None, 0, st))
+                else:
+                    row.append(functools.partial(L.uw_matmul, ct.byref(lay.mats[m].dmat), pipe, 0, 1, xin,
+                                                 batch, yout, scr, nsc, st))
+            silu = functools.partial(L.uw_silu_mul_bf16, P(self.g), P(self.u), batch * F, P(self.h), st)
+            self.calls.append([row[0], row[1], silu, row[2]])
+            self.bytes.append([palette_bytes(lay.info[m], batch) for m in range(3)])
+        # events bracketing the matmul launches of the first `kernel_events` steps
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(3 * kernel_events)]
+        self.ev_bytes = []
+        self.timing = False
+        self.n_ev = 0
+
+    def run(self, i):
+        li = i % len(self.layers)
+        c = self.calls[li]
+        if self.timing and self.n_ev + 3 <= len(self.ev):
+            s = self.stream
+            for k, f in enumerate(c):
+                if k == 2:                       # SiLU*mul between up and down
+                    if f():
+                        raise RuntimeError("silu launch failed")
+                    continue
+                e0, e1 = self.ev[self.n_ev]
+                e0.record(s)
+                rc = f()
+                e1.record(s)
+                self.ev_bytes.append(self.bytes[li][k if k < 2 else 2])
+                self.n_ev += 1
+                if rc:
+                    raise RuntimeError(f"launch failed: {rc}")
+            return
+        for f in c:
+            if f():
+                raise RuntimeError("launch failed")
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for i in range(warmup):
+        step.run(i)
+    torch.cuda.synchronize()
+    step.timing = True
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step.run(warmup + i)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+# ------------------------------------------------------------- CPU baseline
+def cpu_baseline(frac_rows=8, min_seconds=10.0):
+    """The oracle's per-step work (rebuild bf16 from the direct-palette form,
+    fp64 matmul, SiLU chain) on the first 1/8 of each matrix's rows, repeated
+    until ~10 s of CPU work; scaled to bf16-equivalent GB/s."""
+    from oracle import codec, numerics
+    import workloads
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        blas_threads = 1
+    mats = []
+    for m in range(3):
+        R, C = workloads.MLP_SHAPES[m]
+        w = workloads.layer_weight(2, 0, m)[: R // frac_rows]
+        x = workloads.layer_activation(2, 0, m, 1)
+        mats.append((codec.encode(w), x))
+    nbytes = sum(2 * c.R * c.C for c, _ in mats)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        g = u = None
+        for m, (c, x) in enumerate(mats):
+            wr = codec.reconstruct_from_palette(c)
+            y = numerics.matmul(wr, x)
+            if m == 0:
+                g = y
+            elif m == 1:
+                u = y
+        numerics.f64_to_bf16_bits(numerics.silu_mul(g, u))
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"first 1/{frac_rows} of the rows of gate, up (1792x4096) and down (512x14336), batch 1: "
+                       f"oracle rebuild from the 4-bit form + fp64 matmul + SiLU chain, {reps} reps in "
+                       f"{el:.1f} s; bf16-equivalent bytes of the sample / time")}
+
+
+# --------------------------------------------------------------- profiles
+def traffic_from_profiles(kernel_tag):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if the
+    summary was taken on the current kernel source (else None)."""
+    import hashlib
+    path = os.path.join(PROFILES, f"{kernel_tag}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t:
+        return None
+    src = open(os.path.join(ROOT, "mlp_matmul_amd", "csrc", "gemv.hip"), "rb").read()
+    src += open(os.path.join(ROOT, "mlp_matmul_amd", "csrc", "device_common.h"), "rb").read()
+    if hashlib.sha256(src).hexdigest()[:16] != m.group(1)[:16]:
+        return None
+    return float(t.group(1))
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the compressed matmul path is "
+              "per-GPU work and this build runs it on a single MI355X", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mlp_matmul_amd as uw
+    import workloads
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    uw.lib()
+    B = a.batch
+    t0 = time.perf_counter()
+    layers = [Layer(i, keep_bf16=not a.no_compare) for i in range(a.layers)]
+    log(f"built {a.layers} layer copies in {time.perf_counter() - t0:.1f} s")
+    if a.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    F, H = workloads.LLAMA_FFN, workloads.LLAMA_HIDDEN
+    weights_bf16_bytes = 3 * 2 * F * H
+    step = Step(layers, B, a.pipeline, kernel_events=a.steps)
+    sec = time_steps(step, a.steps, a.warmup)
+    torch.cuda.synchronize()
+    durs = np.array([s.elapsed_time(e) / 1e3 for s, e in step.ev[:step.n_ev]])
+    bytes_ = np.array(step.ev_bytes, dtype=np.float64)
+    achieved = bytes_.sum() / durs.sum() / 1e9
+    compressed_step_bytes = sum(palette_bytes(layers[0].info[m], B) for m in range(3))
+    log(f"{a.pipeline}: {sec * 1e3:.4f} ms/step, dominant kernel {durs.mean() * 1e6:.2f} us avg")
+
+    extra = {}
+    if not a.no_compare:
+        for name in ("bf16", "full", "exp", "pal", "direct"):
+            if name == a.pipeline:
+                extra[name] = round(sec * 1e3, 5)
+                continue
+            st = Step(layers, B, name)
+            extra[name] = round(time_steps(st, max(10, a.steps // 2), 3) * 1e3, 5)
+            del st
+        log(f"ms/step by pipeline: {extra}")
+
+    tag = f"gemv_recon_pal_b{B}"
+    traffic = traffic_from_profiles(tag) if B < 16 and a.pipeline == "direct" else None
+    out = {
+        "metric": METRIC,
+        "value": round(weights_bf16_bytes / sec / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3.1-8b-mlp-layer", "batch": B, "pipeline": a.pipeline,
+                   "gate_up": [F, H], "down": [H, F], "layer_copies_rotated": a.layers,
+                   "weights": "N(0,0.02)+0.05% N(0,0.5), seeded"},
+        "compressed_GBps": round(compressed_step_bytes / sec / 1e9, 2),
+        "compressed_hbm_frac": round(compressed_step_bytes / sec / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": f"recon matmul ({'gemv' if B < 16 else 'mfma'}, palette source)",
+                     "launches": int(durs.size), "avg_launch_us": round(float(durs.mean()) * 1e6, 3)},
+    }
+    if extra:
+        out["ms_per_step_by_pipeline"] = extra
+        out["speedup_vs_bf16"] = round(extra["bf16"] / (sec * 1e3), 4)
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

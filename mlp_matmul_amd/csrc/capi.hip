@@ -89,7 +89,8 @@ int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* s
     uwk::MatArgs a = a0;
     if (a.R < 0 || a.C < 0 || a.C % uw::kGroup || a.B < 0)
         return uw::fail(UW_EINVAL, std::string(who) + ": bad shape (cols must be a multiple of 64)");
-    if (a.B > (int64_t(1) << 24) || a.R > (int64_t(1) << 31) || a.C > (int64_t(1) << 31))
+    if (a.B > (int64_t(1) << 24) || a.R * a.C >= (int64_t(1) << 31) || a.B * a.C >= (int64_t(1) << 31) ||
+        a.B * a.R >= (int64_t(1) << 31))
         return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": size beyond the supported range");
     if (a.R == 0 || a.B == 0) return UW_OK;
     if (!a.X || !a.Y || !aligned16(a.X) || !aligned16(a.Y) || (a.R * a.C && (!a.w || !aligned16(a.w))))

@@ -43,9 +43,28 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Sum over the 64 lanes of a wave; the total lands in every lane.  Butterfly
+// within rows of 16 lanes through DPP row rotations, then across rows with
+// lane permutes (2 of the 6 steps go through the LDS crossbar).
+__device__ __forceinline__ float dpp_ror(float v, int n) {
+    const int iv = __builtin_bit_cast(int, v);
+    int r;
+    switch (n) {
+        case 1: r = __builtin_amdgcn_update_dpp(0, iv, 0x121, 0xF, 0xF, false); break;   // row_ror:1
+        case 2: r = __builtin_amdgcn_update_dpp(0, iv, 0x122, 0xF, 0xF, false); break;   // row_ror:2
+        case 4: r = __builtin_amdgcn_update_dpp(0, iv, 0x124, 0xF, 0xF, false); break;   // row_ror:4
+        default: r = __builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false); break;  // row_ror:8
+    }
+    return __builtin_bit_cast(float, r);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    v += dpp_ror(v, 8);
+    v += dpp_ror(v, 4);
+    v += dpp_ror(v, 2);
+    v += dpp_ror(v, 1);        // every lane of a 16-lane row holds the row sum
+    v += __shfl_xor(v, 16, kWave);
+    v += __shfl_xor(v, 32, kWave);
     return v;
 }
 

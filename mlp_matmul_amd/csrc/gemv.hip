@@ -8,17 +8,34 @@
 // small batch every token streams all weights, so the kernel is bound by HBM
 // bandwidth and the fewer bytes it reads the faster it runs.
 //
-// Mapping to CDNA4: a wavefront owns one output row; per step each lane
-// takes 16 consecutive weights (the wave covers 1024 contiguous weights, so
-// every load instruction is fully coalesced), rebuilds them as 8 packed bf16
-// pairs and accumulates with v_dot2_f32_bf16 per activation row; the 64
-// partial sums are reduced across the wave at the end.
-//   palette source: a 256-entry LDS table maps a byte of two 4-bit indices to
-//     both exponents already in bf16 position; one v_perm and one v_and_or
-//     merge them with the sign/mantissa bytes.  A lane whose 64-element
-//     group is flagged in the bitmap takes its exponents from the verbatim
-//     array instead (checked once per 16 weights, never per element).
+// Mapping to CDNA4.  A wavefront owns NRW consecutive output rows and walks
+// their columns in slabs of 1024 weights; an *item* is one slab of all NRW
+// rows.  In a slab each lane holds 16 weights of every row, laid out so that
+// each load instruction of the wave reads one contiguous block (16 contiguous
+// bytes per lane for the byte planes; for bf16, two 8-weight halves 512
+// weights apart).  Items are software pipelined over two register sets: all
+// loads of item t+1 are issued before item t is rebuilt and multiplied, and
+// the loop has no data-dependent branch around a load, so the in-order vmcnt
+// counter never makes a wave drain its prefetch.  The activations of a slab
+// are read once (from LDS when B*C*2 <= 32 KiB, else from L2) and reused for
+// all NRW rows.  Products go through v_dot2_f32_bf16 (two bf16 MACs, fp32
+// sum); each row's 64 per-lane sums are reduced across the wave at the end.
+//   palette source: the wave reads the verbatim bitmap words and verbatim
+//     bases of all tiles its rows touch once (one per lane).  When an item is
+//     issued each lane picks its group's word with a lane read, derives the
+//     verbatim flag and slot, and issues the 16-byte load of its verbatim
+//     exponents with the item's other loads (lanes outside verbatim groups all
+//     read one shared line: no extra HBM bytes).  The rebuild maps a byte of
+//     two 4-bit indices through a 256-entry LDS table to both exponents
+//     already in bf16 position and merges them with the sign/mantissa bytes
+//     (one v_perm and one v_and_or per pair); verbatim lanes take their raw
+//     exponents instead, behind a wave-uniform branch that is skipped when no
+//     lane of the slab is verbatim.  The check is per 16 weights, never per
+//     element.
 //   exponent source: v_perm spreads two exponent bytes into place.
+#include <cstdio>
+#include <cstdlib>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -26,140 +43,332 @@ namespace uwk {
 
 namespace {
 
-constexpr int kSlab = 1024;   // weights per wave per step: 64 lanes x 16
+constexpr int kSlab = 1024;            // weights per row per item: 64 lanes x 16
+constexpr int kXLdsMax = 32 * 1024;    // activation bytes staged in LDS at most
 
 __device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) {
     return (a.pal[i >> 2] >> (8 * (i & 3))) & 0xFFu;
 }
 
-// Load the compressed (or raw) data of 16 consecutive weights of row-major
-// position `pos` (multiple of 16).
+// Element offsets (within a slab) of a lane's two 8-weight halves.
+template <int SRC>
+__device__ __forceinline__ uint32_t half_off(int lane, int h) {
+    return SRC == SRC_BF16 ? uint32_t(h * 512 + lane * 8) : uint32_t(lane * 16 + h * 8);
+}
+
 template <int SRC>
 struct Chunk {
-    u32x4_t d0, d1;       // BF16: 8 dwords of weights; EXP: d0 = exponents; PAL: d0.xy = nibbles
-    u32x4_t sm;           // EXP, PAL
-    bool verb;
-    uint64_t word;
-    uint32_t vbase;
+    u32x4_t d0, d1;   // BF16: the two weight halves; EXP: d0 = 16 exponents; PAL: d0.xy = 16 nibbles
+    u32x4_t sm;       // EXP, PAL: sign/mantissa bytes
+    u32x4_t vx;       // PAL: verbatim exponents (meaningful when verb)
+    uint32_t verb;    // PAL: 1 when the lane's 64-element group is verbatim
 };
 
-template <int SRC>
-__device__ __forceinline__ void load_chunk(const MatArgs& a, int64_t pos, Chunk<SRC>& c) {
-    if (SRC == SRC_BF16) {
-        const uint16_t* w = static_cast<const uint16_t*>(a.w) + pos;
-        c.d0 = load_stream16(w);
-        c.d1 = load_stream16(w + 8);
-    } else if (SRC == SRC_EXP) {
-        c.d0 = load_stream16(static_cast<const uint8_t*>(a.w) + pos);
-        c.sm = load_stream16(a.sm + pos);
-    } else {
-        const u32x2_t n = load_stream8(static_cast<const uint8_t*>(a.w) + pos / 2);
-        c.d0 = u32x4_t{n[0], n[1], 0u, 0u};
-        c.sm = load_stream16(a.sm + pos);
-        const int64_t g = pos >> 6;
-        c.word = a.bitmap[g >> 6];
-        c.verb = (c.word >> (g & 63)) & 1ull;
-    }
-}
-
-// Rebuild the 8 bf16 pairs of a chunk.
-template <int SRC>
-__device__ __forceinline__ void rebuild(const MatArgs& a, const Chunk<SRC>& c, int64_t pos, const uint32_t* lut,
-                                        uint32_t w[8]) {
-    if (SRC == SRC_BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            w[i] = c.d0[i];
-            w[4 + i] = c.d1[i];
-        }
-    } else if (SRC == SRC_EXP) {
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-            w[p] = (p & 1) ? join_pair<1>(c.sm[p >> 1], exp_pair<1>(c.d0[p >> 1]))
-                           : join_pair<0>(c.sm[p >> 1], exp_pair<0>(c.d0[p >> 1]));
-    } else {
-        uint32_t e7[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) e7[p] = lut[(c.d0[p >> 2] >> (8 * (p & 3))) & 0xFFu];
-        if (c.verb) {
-            const int64_t g = pos >> 6;
-            const uint32_t slot = verbatim_slot(c.word, uint32_t(g & 63), a.tile_vbase[g >> 6]);
-            const u32x4_t v = load16(a.vexp + uint64_t(slot) * 64 + (pos & 63));
-#pragma unroll
-            for (int p = 0; p < 8; ++p) e7[p] = (p & 1) ? exp_pair<1>(v[p >> 1]) : exp_pair<0>(v[p >> 1]);
-        }
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-            w[p] = (p & 1) ? join_pair<1>(c.sm[p >> 1], e7[p]) : join_pair<0>(c.sm[p >> 1], e7[p]);
-    }
-}
-
-template <int SRC, int MB, int UNR>
+template <int SRC, int MB, int NRW, bool EXACT, bool XLDS>
 __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
-    __shared__ uint32_t lut[256];
-    if (SRC == SRC_PAL) {
-        const int t = threadIdx.x;
-        lut[t] = (palb(a, t & 15) << 7) | (palb(a, t >> 4) << 23);
-        __syncthreads();
-    }
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t r = int64_t(blockIdx.x) * 4 + wave;
-    if (r >= a.R) return;
+    __shared__ uint32_t lut[256];                                // nibble pair -> exponents in place
+    extern __shared__ uint32_t lds[];
+    uint16_t* xs = reinterpret_cast<uint16_t*>(lds);             // [B][C] when XLDS
+    const int tid = threadIdx.x;
     const int64_t C = a.C;
+    const uint32_t Cu = uint32_t(C);
     const int B = int(a.B);
-    const int64_t row = r * C;
-    float acc[MB];
-#pragma unroll
-    for (int b = 0; b < MB; ++b) acc[b] = 0.f;
+    if (SRC == SRC_PAL) lut[tid] = (palb(a, tid & 15) << 7) | (palb(a, tid >> 4) << 23);
 
-    for (int64_t k0 = 0; k0 < C; k0 += int64_t(kSlab) * UNR) {
-        Chunk<SRC> ch[UNR];
-        bool ok[UNR];
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int NG = a.row_groups;                                 // row groups per wave
+    const int64_t r0 = (int64_t(blockIdx.x) * 4 + wave) * NRW * NG;
+    const bool live = r0 < a.R;                                  // wave has rows (uniform)
+    const int wrows = live ? int(min(int64_t(NRW) * NG, a.R - r0)) : 0;
+    const int ngroups = (wrows + NRW - 1) / NRW;
+    const int iters = int((C + kSlab - 1) / kSlab);
+    const int total = ngroups * iters;                           // items: (group, slab)
+
+    // the verbatim tables of every tile the wave's rows touch, one per lane
+    // (loaded after item 0's weight loads are out)
+    const int64_t t_first = (r0 * C) >> 12;
+    uint64_t my_word = 0;
+    uint32_t my_vbase = 0;
+    // a lane's group inside a 1024-weight slab, and the mask of the groups below it
+    const uint32_t lane_grp = uint32_t(lane) >> 2;
+    const uint32_t lane_below = (1u << lane_grp) - 1u;
+    // lanes outside verbatim groups all read the first line of this array
+    const uint8_t* vb_ptr = a.vexp ? a.vexp : a.sm;
+    const uint16_t* wb = static_cast<const uint16_t*>(a.w);
+    const uint8_t* w8 = static_cast<const uint8_t*>(a.w);
+
+    float acc[NRW][MB];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int64_t k = k0 + u * kSlab + lane * 16;
-            ok[u] = k < C;
-            if (ok[u]) load_chunk<SRC>(a, row + k, ch[u]);
-        }
+    for (int r = 0; r < NRW; ++r)
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int64_t k = k0 + u * kSlab + lane * 16;
-            uint32_t w[8];
-            if (ok[u]) rebuild<SRC>(a, ch[u], row + k, lut, w);
+        for (int b = 0; b < MB; ++b) acc[r][b] = 0.f;
+
+    // rows past the matrix (beyond wrows) re-read the wave's first row; their
+    // sums are never stored.  issue_w: the weight planes (no dependency);
+    // issue_v: the verbatim exponents, whose address needs the wave's tables.
+    auto row_of = [&](int t, int r) -> uint32_t {
+        const int rr = (t / iters) * NRW + r;                    // row inside the wave's range
+        return uint32_t(r0) + uint32_t(rr < wrows ? rr : 0);
+    };
+    auto issue_w = [&](int t, Chunk<SRC>* ch) {
+        const uint32_t k0 = uint32_t(t % iters) * kSlab;
 #pragma unroll
-            for (int b = 0; b < MB; ++b) {
-                if (!ok[u] || b >= B) continue;
-                const uint16_t* xp = a.X + int64_t(b) * C + k;
-                const u32x4_t x0 = load16(xp), x1 = load16(xp + 8);
-                float s = acc[b];
-                s = dot2_bf16(w[0], x0[0], s);
-                s = dot2_bf16(w[1], x0[1], s);
-                s = dot2_bf16(w[2], x0[2], s);
-                s = dot2_bf16(w[3], x0[3], s);
-                s = dot2_bf16(w[4], x1[0], s);
-                s = dot2_bf16(w[5], x1[1], s);
-                s = dot2_bf16(w[6], x1[2], s);
-                s = dot2_bf16(w[7], x1[3], s);
-                acc[b] = s;
+        for (int r = 0; r < NRW; ++r) {
+            const uint32_t row = row_of(t, r);
+            Chunk<SRC>& c = ch[r];
+            uint32_t k = k0 + half_off<SRC>(lane, 0);
+            if (!EXACT && k >= Cu) k = 0;
+            const uint32_t pos = row * Cu + k;
+            if (SRC == SRC_BF16) {
+                uint32_t k1 = k0 + half_off<SRC>(lane, 1);
+                if (!EXACT && k1 >= Cu) k1 = 0;
+                c.d0 = load_stream16(wb + pos);
+                c.d1 = load_stream16(wb + row * Cu + k1);
+            } else if (SRC == SRC_EXP) {
+                c.d0 = load_stream16(w8 + pos);
+                c.sm = load_stream16(a.sm + pos);
+            } else {
+                const u32x2_t n = load_stream8(w8 + pos / 2);
+                c.d0 = u32x4_t{n[0], n[1], 0u, 0u};
+                c.sm = load_stream16(a.sm + pos);
             }
         }
-    }
+    };
+    auto issue_v = [&](int t, Chunk<SRC>* ch) {
+        if (SRC != SRC_PAL) return;
+        const uint32_t k0 = uint32_t(t % iters) * kSlab;
 #pragma unroll
-    for (int b = 0; b < MB; ++b) {
-        if (b >= B) continue;
-        const float v = wave_sum(acc[b]);
-        if (lane == 0) a.Y[int64_t(b) * a.R + r] = v;
+        for (int r = 0; r < NRW; ++r) {
+            const uint32_t row = row_of(t, r);
+            Chunk<SRC>& c = ch[r];
+            uint32_t k = k0 + half_off<SRC>(lane, 0);
+            if (!EXACT && k >= Cu) k = 0;
+            const uint32_t pos = row * Cu + k;
+            uint32_t voff = 0;
+            if (EXACT) {
+                // the slab lies in one tile: its word and base are uniform
+                // (lane reads), its 16 groups are bits gb..gb+15 of the word
+                const uint32_t sp = row * Cu + k0;
+                const int tl = int((sp >> 12) - uint32_t(t_first));
+                const uint64_t word =
+                    (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(my_word >> 32), tl))) << 32) |
+                    uint32_t(__builtin_amdgcn_readlane(int(uint32_t(my_word)), tl));
+                const uint32_t gb = (sp >> 6) & 63u;
+                const uint32_t m16 = uint32_t(word >> gb) & 0xFFFFu;
+                c.verb = (m16 >> lane_grp) & 1u;
+                if (m16) {                                           // rare: a verbatim group in this slab
+                    const uint32_t vbase = uint32_t(__builtin_amdgcn_readlane(int(my_vbase), tl));
+                    const uint64_t below = gb ? (word & ((~0ull) >> (64 - gb))) : 0ull;
+                    const uint32_t slab_slot = vbase + uint32_t(__popcll(below));
+                    const uint32_t slot = slab_slot + uint32_t(__popc(m16 & lane_below));
+                    voff = c.verb ? slot * 64u + (pos & 63u) : 0u;
+                }
+            } else {
+                const int tl = int((pos >> 12) - uint32_t(t_first));
+                const uint64_t word = (uint64_t(uint32_t(__shfl(int(my_word >> 32), tl))) << 32) |
+                                      uint32_t(__shfl(int(uint32_t(my_word)), tl));
+                const uint32_t vbase = uint32_t(__shfl(int(my_vbase), tl));
+                const uint32_t bit = (pos >> 6) & 63u;
+                c.verb = uint32_t(word >> bit) & 1u;
+                if (__builtin_amdgcn_ballot_w64(c.verb != 0)) {
+                    const uint32_t slot = verbatim_slot(word, bit, vbase);
+                    voff = c.verb ? slot * 64u + (pos & 63u) : 0u;
+                }
+            }
+            c.vx = load16(vb_ptr + voff);
+        }
+    };
+    auto issue = [&](int t, Chunk<SRC>* ch) {
+        issue_w(t, ch);
+        issue_v(t, ch);
+    };
+
+    Chunk<SRC> cur[NRW], nxt[NRW];
+    // item 0's weight loads go out first; the verbatim tables of every tile
+    // the wave's rows touch (one per lane) follow, then item 0's verbatim loads
+    if (live) issue_w(0, cur);
+    if (SRC == SRC_PAL && live) {
+        const int64_t t_end = ((r0 + wrows) * C + 4095) >> 12;
+        if (t_first + lane < t_end) {
+            my_word = a.bitmap[t_first + lane];
+            my_vbase = a.tile_vbase[t_first + lane];
+        }
+    }
+    if (live) issue_v(0, cur);
+    if (XLDS) {
+        const int64_t n16 = int64_t(B) * C / 8;                  // 16-byte pieces
+        for (int64_t i = tid; i < n16; i += 256)
+            reinterpret_cast<u32x4_t*>(xs)[i] = load16(a.X + i * 8);
+    }
+    __syncthreads();
+    if (!live) return;
+
+    auto compute = [&](int t, const Chunk<SRC>* cur) {
+        const uint32_t k0 = uint32_t(t % iters) * kSlab;
+        const uint32_t ka = k0 + half_off<SRC>(lane, 0), kb = k0 + half_off<SRC>(lane, 1);
+        const bool oka = EXACT || ka < Cu, okb = EXACT || kb < Cu;
+        // activations of this slab, shared by all rows
+        u32x4_t xa[MB], xb[MB];
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            if (b < B) {
+                const uint32_t kka = oka ? ka : 0, kkb = okb ? kb : 0;
+                if (XLDS) {
+                    xa[b] = *reinterpret_cast<const u32x4_t*>(xs + b * Cu + kka);
+                    xb[b] = *reinterpret_cast<const u32x4_t*>(xs + b * Cu + kkb);
+                } else {
+                    xa[b] = load16(a.X + b * Cu + kka);
+                    xb[b] = load16(a.X + b * Cu + kkb);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NRW; ++r) {
+            const Chunk<SRC>& c = cur[r];
+            uint32_t w[8];
+            if (SRC == SRC_BF16) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    w[i] = c.d0[i];
+                    w[4 + i] = c.d1[i];
+                }
+            } else if (SRC == SRC_EXP) {
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    w[p] = (p & 1) ? join_pair<1>(c.sm[p >> 1], exp_pair<1>(c.d0[p >> 1]))
+                                   : join_pair<0>(c.sm[p >> 1], exp_pair<0>(c.d0[p >> 1]));
+            } else {
+                uint32_t e7[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const uint32_t off = ((c.d0[p >> 2] >> (8 * (p & 3))) & 0xFFu) << 2;
+                    e7[p] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + off);
+                }
+                if (__builtin_amdgcn_ballot_w64(c.verb != 0)) {    // rare: raw exponents for verbatim lanes
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) {
+                        const uint32_t e_raw = (p & 1) ? exp_pair<1>(c.vx[p >> 1]) : exp_pair<0>(c.vx[p >> 1]);
+                        e7[p] = c.verb ? e_raw : e7[p];
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    w[p] = (p & 1) ? join_pair<1>(c.sm[p >> 1], e7[p]) : join_pair<0>(c.sm[p >> 1], e7[p]);
+            }
+            if (!EXACT) {
+                if (!oka) w[0] = w[1] = w[2] = w[3] = 0u;
+                if (!okb) w[4] = w[5] = w[6] = w[7] = 0u;
+            }
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                if (b < B) {
+                    float s = acc[r][b];
+                    s = dot2_bf16(w[0], xa[b][0], s);
+                    s = dot2_bf16(w[1], xa[b][1], s);
+                    s = dot2_bf16(w[2], xa[b][2], s);
+                    s = dot2_bf16(w[3], xa[b][3], s);
+                    s = dot2_bf16(w[4], xb[b][0], s);
+                    s = dot2_bf16(w[5], xb[b][1], s);
+                    s = dot2_bf16(w[6], xb[b][2], s);
+                    s = dot2_bf16(w[7], xb[b][3], s);
+                    acc[r][b] = s;
+                }
+            }
+        }
+    };
+
+    // a group's rows are complete after its last slab: reduce and store
+    auto finish = [&](int t) {
+        if ((t + 1) % iters != 0) return;
+        const int g = t / iters;
+#pragma unroll
+        for (int r = 0; r < NRW; ++r) {
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                const int rr = g * NRW + r;
+                if (b < B && rr < wrows) {
+                    const float v = wave_sum(acc[r][b]);
+                    if (lane == 0) a.Y[int64_t(b) * a.R + r0 + rr] = v;
+                }
+                acc[r][b] = 0.f;
+            }
+        }
+    };
+
+    // ping-pong over two register sets: the loads of item t+1 are in flight
+    // while item t is computed; the last item is re-issued (an L2 hit) so the
+    // body has no conditional load
+    for (int t = 0; t < total; t += 2) {
+        issue(min(t + 1, total - 1), nxt);
+        compute(t, cur);
+        finish(t);
+        if (t + 1 >= total) break;
+        issue(min(t + 2, total - 1), cur);
+        compute(t + 1, nxt);
+        finish(t + 1);
+    }
+}
+
+__global__ void zero_fill(float* y, int64_t n) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) y[i] = 0.f;
+}
+
+// Tuning overrides read once: UW_GEMV_NRW (rows per group), UW_GEMV_NG (row
+// groups per wave), UW_GEMV_XGLOBAL=1 (activations from L2 instead of LDS).
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e ? atoi(e) : dflt;
+}
+
+template <int SRC, int MB, int NRW, bool XLDS>
+void launch_cfg(const MatArgs& a0, hipStream_t s) {
+    // row groups per wave: long-lived waves amortise the per-wave start (tables,
+    // activation staging); the wave's tiles must fit one per lane (<= 60)
+    static const int ng_env = env_int("UW_GEMV_NG", 0);
+    MatArgs a = a0;
+    // measured on MI355X at batch 1: short rows (4096) run best as one row per
+    // group and two groups per wave, long rows (14336) as two rows, one group
+    int ng = ng_env > 0 ? ng_env : (NRW == 1 ? 2 : 1);
+    while (ng > 1 && int64_t(ng) * NRW * a.C > 60 * 4096) --ng;
+    a.row_groups = ng;
+    const int64_t waves = (a.R + int64_t(NRW) * ng - 1) / (int64_t(NRW) * ng);
+    const unsigned grid = unsigned((waves + 3) / 4);
+    const size_t lds = XLDS ? size_t(a.B * a.C * 2) : 0;
+    if (a.C % kSlab == 0)
+        gemv_kernel<SRC, MB, NRW, true, XLDS><<<grid, 256, lds, s>>>(a);
+    else
+        gemv_kernel<SRC, MB, NRW, false, XLDS><<<grid, 256, lds, s>>>(a);
+}
+
+template <int SRC, int MB, int NRW>
+void launch_x(const MatArgs& a, hipStream_t s) {
+    static const bool xglobal = env_int("UW_GEMV_XGLOBAL", 0) == 1;
+    if (a.B * a.C * 2 <= kXLdsMax && !xglobal) launch_cfg<SRC, MB, NRW, true>(a, s);
+    else launch_cfg<SRC, MB, NRW, false>(a, s);
+}
+
+// Rows per group: 2 for long rows (activations reused twice), 1 for short
+// rows; the verbatim tables of a wave's rows must fit one per lane: NRW*C <=
+// 60 tiles of 4096.
+template <int SRC, int MB>
+void launch_mb(const MatArgs& a, hipStream_t s) {
+    static const int nrw_env = env_int("UW_GEMV_NRW", 0);
+    int nrw = nrw_env ? nrw_env : (a.C >= 8192 ? 2 : 1);
+    while (nrw > 1 && nrw * a.C > 60 * 4096) nrw >>= 1;
+    switch (nrw) {
+        case 2: launch_x<SRC, MB, 2>(a, s); break;
+        default: launch_x<SRC, MB, 1>(a, s); break;
     }
 }
 
 template <int SRC>
 hipError_t launch_src(const MatArgs& a, hipStream_t s) {
-    const unsigned grid = unsigned((a.R + 3) / 4);
-    if (a.B <= 1) gemv_kernel<SRC, 1, 4><<<grid, 256, 0, s>>>(a);
-    else if (a.B <= 2) gemv_kernel<SRC, 2, 4><<<grid, 256, 0, s>>>(a);
-    else if (a.B <= 4) gemv_kernel<SRC, 4, 2><<<grid, 256, 0, s>>>(a);
-    else if (a.B <= 8) gemv_kernel<SRC, 8, 2><<<grid, 256, 0, s>>>(a);
-    else gemv_kernel<SRC, 16, 1><<<grid, 256, 0, s>>>(a);
+    if (a.B <= 1) launch_mb<SRC, 1>(a, s);
+    else if (a.B <= 2) launch_mb<SRC, 2>(a, s);
+    else if (a.B <= 4) launch_mb<SRC, 4>(a, s);
+    else if (a.B <= 8) launch_mb<SRC, 8>(a, s);
+    else launch_mb<SRC, 16>(a, s);
     return hipGetLastError();
 }
 
@@ -167,6 +376,12 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
 
 hipError_t launch_gemv(int src, const MatArgs& a, hipStream_t s) {
     if (a.R == 0 || a.B == 0) return hipSuccess;
+    if (a.C == 0) {
+        const int64_t n = a.B * a.R;
+        zero_fill<<<unsigned((n + 255) / 256), 256, 0, s>>>(a.Y, n);
+        return hipGetLastError();
+    }
+    if (src == SRC_PAL && a.C > 60 * 4096) return hipErrorNotSupported;
     switch (src) {
         case SRC_BF16: return launch_src<SRC_BF16>(a, s);
         case SRC_EXP: return launch_src<SRC_EXP>(a, s);

@@ -38,6 +38,7 @@ struct MatArgs {
     float* partial;             // split-K partial sums [split, B, R] (MFMA)
     int64_t R, C, B;
     int32_t split_k;
+    int32_t row_groups;         // GEMV: groups of NRW rows one wave walks in turn
     uint32_t pal[4];
 };
 
