@@ -44,6 +44,7 @@ def parse():
     p.add_argument("--layers", type=int, default=4, help="layer copies rotated through (MALL defeat)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-compare", action="store_true", help="skip the other pipelines and the bf16 baseline")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches only")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch a plain device copy of known size (for counter calibration)")
     return p.parse_args()
@@ -89,7 +90,7 @@ class Step:
     that the host issues a step in a few microseconds and the GPU queue stays
     ahead of it (the timed region measures the GPU, not Python)."""
 
-    def __init__(self, layers, batch, pipeline, kernel_events=0):
+    def __init__(self, layers, batch, pipeline, stream=None):
         import ctypes as ct
         import functools
         import torch
@@ -109,8 +110,9 @@ class Step:
         sp = pipe if pipe not in (uw.UW_PIPE_AUTO, uw.UW_PIPE_BF16) else uw.UW_PIPE_FULL
         nscr = max(uw.scratch_bytes(sp, F, H, batch, 4), uw.scratch_bytes(sp, H, F, batch, 4))
         self.scratch = torch.empty(nscr, dtype=torch.uint8, device="cuda")
-        self.stream = torch.cuda.current_stream()
+        self.stream = stream if stream is not None else torch.cuda.current_stream()
         L = uw.lib()
+        self.uw_lib = L
         st = ct.c_void_p(self.stream.cuda_stream)
         P = lambda t: ct.c_void_p(t.data_ptr())
         scr, nsc = P(self.scratch), ct.c_uint64(self.scratch.numel())
@@ -132,48 +134,79 @@ class Step:
             silu = functools.partial(L.uw_silu_mul_bf16, P(self.g), P(self.u), batch * F, P(self.h), st)
             self.calls.append([row[0], row[1], silu, row[2]])
             self.bytes.append([palette_bytes(lay.info[m], batch) for m in range(3)])
-        # events bracketing the matmul launches of the first `kernel_events` steps
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(3 * kernel_events)]
-        self.ev_bytes = []
-        self.timing = False
-        self.n_ev = 0
 
     def run(self, i):
-        li = i % len(self.layers)
-        c = self.calls[li]
-        if self.timing and self.n_ev + 3 <= len(self.ev):
-            s = self.stream
-            for k, f in enumerate(c):
-                if k == 2:                       # SiLU*mul between up and down
-                    if f():
-                        raise RuntimeError("silu launch failed")
-                    continue
-                e0, e1 = self.ev[self.n_ev]
-                e0.record(s)
-                rc = f()
-                e1.record(s)
-                self.ev_bytes.append(self.bytes[li][k if k < 2 else 2])
-                self.n_ev += 1
-                if rc:
-                    raise RuntimeError(f"launch failed: {rc}")
-            return
-        for f in c:
+        for f in self.calls[i % len(self.layers)]:
             if f():
-                raise RuntimeError("launch failed")
+                raise RuntimeError("launch failed: " + self.uw_lib.uw_last_error().decode())
 
 
 def time_steps(step, steps, warmup):
+    """Average seconds per step over `steps` eager steps on the step's stream,
+    after `warmup` untimed ones."""
     import torch
-    for i in range(warmup):
-        step.run(i)
-    torch.cuda.synchronize()
-    step.timing = True
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step.run(warmup + i)
-    torch.cuda.synchronize()
+    with torch.cuda.stream(step.stream):
+        for i in range(warmup):
+            step.run(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step.run(warmup + i)
+        torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps
+
+
+class GraphStep:
+    """One captured HIP graph per layer copy; a step replays one of them."""
+
+    def __init__(self, step):
+        import torch
+        self.step = step
+        self.graphs = []
+        with torch.cuda.stream(step.stream):
+            for li in range(len(step.layers)):      # warm the kernels outside capture
+                step.run(li)
+            torch.cuda.synchronize()
+            for li in range(len(step.layers)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=step.stream):
+                    step.run(li)
+                self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def check_against_eager(self):
+        """Every graph replay reproduces the eager outputs bit for bit."""
+        import torch
+        st = self.step
+        for li, g in enumerate(self.graphs):
+            with torch.cuda.stream(st.stream):
+                st.run(li)
+            torch.cuda.synchronize()
+            ref = (st.g.clone(), st.u.clone(), st.h.clone(), st.y.clone())
+            for _ in range(3):
+                for t in (st.g, st.u, st.y):
+                    t.fill_(float("nan"))
+                st.h.zero_()
+                torch.cuda.synchronize()
+                g.replay()
+                torch.cuda.synchronize()
+                for a_, b_ in zip(ref, (st.g, st.u, st.h, st.y)):
+                    if not torch.equal(a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_.view(torch.int32),
+                                       b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_.view(torch.int32)):
+                        return False
+        return True
+
+    def time(self, steps, warmup):
+        import torch
+        n = len(self.graphs)
+        for i in range(warmup):
+            self.graphs[i % n].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.graphs[i % n].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
 
 
 # ------------------------------------------------------------- CPU baseline
@@ -219,10 +252,11 @@ def cpu_baseline(frac_rows=8, min_seconds=10.0):
 
 # --------------------------------------------------------------- profiles
 def traffic_from_profiles(kernel_tag):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if the
+    """HBM bytes per launch from the committed rocprofv3 counter summary (two
+    --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), if the
     summary was taken on the current kernel source (else None)."""
     import hashlib
-    path = os.path.join(PROFILES, f"{kernel_tag}_pmc.md")
+    path = os.path.join(PROFILES, f"{kernel_tag}.md")
     if not os.path.exists(path):
         return None
     txt = open(path).read()
@@ -262,27 +296,47 @@ def main():
 
     F, H = workloads.LLAMA_FFN, workloads.LLAMA_HIDDEN
     weights_bf16_bytes = 3 * 2 * F * H
-    step = Step(layers, B, a.pipeline, kernel_events=a.steps)
-    sec = time_steps(step, a.steps, a.warmup)
-    torch.cuda.synchronize()
-    durs = np.array([s.elapsed_time(e) / 1e3 for s, e in step.ev[:step.n_ev]])
-    bytes_ = np.array(step.ev_bytes, dtype=np.float64)
+    stream = torch.cuda.Stream()
+
+    def measure(pipeline):
+        st = Step(layers, B, pipeline, stream=stream)
+        eager = time_steps(st, a.steps, a.warmup)
+        graph, ok = None, None
+        if not a.no_graph:
+            gs = GraphStep(st)
+            ok = gs.check_against_eager()
+            graph = gs.time(a.steps, a.warmup)
+        return st, eager, graph, ok
+
+    step, eager, graph, graph_ok = measure(a.pipeline)
+    # dominant kernel: the library's kernel timer records HIP events at the
+    # start and end of every matmul launch (on its stream) over a second pass
+    # of the same eager steps
+    with uw.KernelTimer(capacity=3 * a.steps + 8) as kt:
+        time_steps(step, a.steps, 0)
+    durs = np.array(kt.ms, dtype=np.float64) / 1e3
+    bytes_ = np.array([step.bytes[i % len(layers)][m] for i in range(a.steps) for m in range(3)],
+                      dtype=np.float64)[:durs.size]
     achieved = bytes_.sum() / durs.sum() / 1e9
+    # the step time is the faster of the two valid timings
+    use_graph = graph is not None and graph_ok and graph < eager
+    sec = graph if use_graph else eager
     compressed_step_bytes = sum(palette_bytes(layers[0].info[m], B) for m in range(3))
-    log(f"{a.pipeline}: {sec * 1e3:.4f} ms/step, dominant kernel {durs.mean() * 1e6:.2f} us avg")
+    log(f"{a.pipeline}: eager {eager * 1e3:.4f} ms/step, graph {graph and graph * 1e3}, graph==eager {graph_ok}, "
+        f"dominant kernel {durs.mean() * 1e6:.2f} us avg")
 
     extra = {}
     if not a.no_compare:
         for name in ("bf16", "full", "exp", "pal", "direct"):
             if name == a.pipeline:
-                extra[name] = round(sec * 1e3, 5)
+                extra[name] = {"eager_ms": round(eager * 1e3, 5), "graph_ms": graph and round(graph * 1e3, 5)}
                 continue
-            st = Step(layers, B, name)
-            extra[name] = round(time_steps(st, max(10, a.steps // 2), 3) * 1e3, 5)
-            del st
+            _, e_, g_, ok_ = measure(name)
+            extra[name] = {"eager_ms": round(e_ * 1e3, 5), "graph_ms": g_ and round(g_ * 1e3, 5),
+                           "graph_matches_eager": ok_}
         log(f"ms/step by pipeline: {extra}")
 
-    tag = f"gemv_recon_pal_b{B}"
+    tag = f"gemv_recon_pal_llama_mlp_b{B}"
     traffic = traffic_from_profiles(tag) if B < 16 and a.pipeline == "direct" else None
     out = {
         "metric": METRIC,
@@ -292,6 +346,9 @@ def main():
         "steps": a.steps,
         "warmup": a.warmup,
         "ms_per_step": round(sec * 1e3, 5),
+        "timing": "hip-graph replay per step" if use_graph else "eager launches",
+        "ms_per_step_eager": round(eager * 1e3, 5),
+        "ms_per_step_graph": graph and round(graph * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -305,11 +362,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": f"recon matmul ({'gemv' if B < 16 else 'mfma'}, palette source)",
-                     "launches": int(durs.size), "avg_launch_us": round(float(durs.mean()) * 1e6, 3)},
+                     "launches": int(durs.size), "avg_launch_us": round(float(durs.mean()) * 1e6, 3),
+                     "algorithmic_bytes_per_launch": round(float(bytes_.mean()))},
     }
     if extra:
         out["ms_per_step_by_pipeline"] = extra
-        out["speedup_vs_bf16"] = round(extra["bf16"] / (sec * 1e3), 4)
+        b16 = min(v for v in (extra["bf16"]["graph_ms"], extra["bf16"]["eager_ms"]) if v)
+        out["speedup_vs_bf16"] = round(b16 / (sec * 1e3), 4)
     if not a.no_cpu_baseline:
         log("timing the CPU oracle sample")
         out["cpu_baseline"] = cpu_baseline()

@@ -261,6 +261,19 @@ int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k,
  * projections of a SwiGLU MLP. */
 int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, void* stream);
 
+/* ----------------------------------------------------------- kernel timer */
+/* Per-launch durations of the matmul kernels (GEMV and MFMA), for measuring
+ * them on their own stream.  While enabled, each matmul kernel launch takes
+ * the next of `capacity` HIP event pairs, which the launch records at the
+ * kernel's own start and end (hipExtLaunchKernel); launches beyond capacity
+ * are not timed.  uw_kernel_timer_read waits for the recorded launches and
+ * writes their durations in ms, in launch order (*count = launches recorded).
+ * Process-global; enable from one thread at a time. */
+int uw_kernel_timer_enable(int capacity);
+int uw_kernel_timer_disable(void);
+int uw_kernel_timer_reset(void);
+int uw_kernel_timer_read(float* ms /*host*/, int max, int* count /*host*/);
+
 /* --------------------------------------------------------------- autotune */
 /* Plan table: (rows, cols, batch) -> (pipeline, kernel, split_k), filled by a
  * measuring autotuner ("Why no single pipeline wins").  Process-global,

@@ -249,6 +249,27 @@ def silu_mul_bf16(g, u, h=None, stream=None):
     return h
 
 
+class KernelTimer:
+    """Context manager: durations (ms) of the matmul kernels launched inside it,
+    recorded by the launches themselves (uw_kernel_timer_*)."""
+
+    def __init__(self, capacity=4096):
+        self.capacity = capacity
+        self.ms = []
+
+    def __enter__(self):
+        check(lib().uw_kernel_timer_enable(self.capacity), "uw_kernel_timer_enable")
+        return self
+
+    def __exit__(self, *exc):
+        lib().uw_kernel_timer_disable()
+        n = ct.c_int()
+        buf = (ct.c_float * self.capacity)()
+        check(lib().uw_kernel_timer_read(buf, self.capacity, ct.byref(n)), "uw_kernel_timer_read")
+        self.ms = [buf[i] for i in range(min(n.value, self.capacity))]
+        return False
+
+
 def plan_set(rows, cols, batch, pipeline, kernel=UW_KERNEL_AUTO, split_k=1):
     check(lib().uw_plan_set(rows, cols, batch, pipeline, kernel, split_k), "uw_plan_set")
 

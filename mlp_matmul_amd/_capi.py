@@ -79,6 +79,10 @@ SIGNATURES = {
     "uw_scratch_bytes": (_I64, [_INT, _I64, _I64, _I64, _INT]),
     "uw_matmul": (_INT, [ct.POINTER(uw_dmat), _INT, _INT, _INT, _P, _I64, _P, _P, _U64, _P]),
     "uw_silu_mul_bf16": (_INT, [_P, _P, _I64, _P, _P]),
+    "uw_kernel_timer_enable": (_INT, [_INT]),
+    "uw_kernel_timer_disable": (_INT, []),
+    "uw_kernel_timer_reset": (_INT, []),
+    "uw_kernel_timer_read": (_INT, [ct.POINTER(ct.c_float), _INT, ct.POINTER(_INT)]),
     "uw_plan_set": (_INT, [_I64, _I64, _I64, _INT, _INT, _INT]),
     "uw_plan_lookup": (_INT, [_I64, _I64, _I64, ct.POINTER(_INT), ct.POINTER(_INT), ct.POINTER(_INT)]),
     "uw_plan_clear": (_INT, []),

@@ -233,7 +233,7 @@ hipError_t launch_cfg(const MatArgs& a, hipStream_t s) {
         attr_set = true;
     }
     dim3 grid(unsigned((a.R + MT - 1) / MT), unsigned((a.B + NT - 1) / NT), unsigned(a.split_k));
-    hipLaunchKernelGGL((mfma_kernel<SRC, NB, WM, WN>), grid, dim3(256), lds, s, a);
+    launch_timed(mfma_kernel<SRC, NB, WM, WN>, grid, dim3(256), lds, s, a);
     return hipGetLastError();
 }
 

@@ -336,9 +336,9 @@ void launch_cfg(const MatArgs& a0, hipStream_t s) {
     const unsigned grid = unsigned((waves + 3) / 4);
     const size_t lds = XLDS ? size_t(a.B * a.C * 2) : 0;
     if (a.C % kSlab == 0)
-        gemv_kernel<SRC, MB, NRW, true, XLDS><<<grid, 256, lds, s>>>(a);
+        launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS>, dim3(grid), dim3(256), lds, s, a);
     else
-        gemv_kernel<SRC, MB, NRW, false, XLDS><<<grid, 256, lds, s>>>(a);
+        launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS>, dim3(grid), dim3(256), lds, s, a);
 }
 
 template <int SRC, int MB, int NRW>

@@ -1,6 +1,7 @@
 // Kernel argument blocks and launchers (host-callable) of libunweight.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,5 +50,18 @@ hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, uint16_t* 
 
 // LDS bytes the decoder needs for a code of longest length lmax.
 size_t decode_lds_bytes(int lmax, int* buf_words);
+
+// Kernel timer: while enabled, each matmul kernel launch takes the next
+// (start, stop) event pair, recorded by the launch itself around the kernel.
+bool timer_next(hipEvent_t* start, hipEvent_t* stop);
+
+template <class K, class... Args>
+void launch_timed(K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s, Args... args) {
+    hipEvent_t e0, e1;
+    if (timer_next(&e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, uint32_t(lds), s, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+}
 
 }  // namespace uwk
