@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-compare", action="store_true", help="skip the other pipelines and the bf16 baseline")
     p.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the autotuned batch sweep (1..256) over the gate and down shapes")
+    p.add_argument("--sweep-batches", default="1,2,4,8,16,32,64,128,256")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch a plain device copy of known size (for counter calibration)")
     return p.parse_args()
@@ -209,6 +212,82 @@ class GraphStep:
         return (time.perf_counter() - t0) / steps
 
 
+# --------------------------------------------------------------- batch sweep
+def time_bf16(mats_bf16, X, reps=20, warmup=3, stream=None):
+    """Best seconds per call of the uncompressed bf16 matmul (GEMV for batch
+    <= 16, MFMA with split-K 1/2/4 otherwise), rotating over the copies."""
+    import ctypes as ct
+    import torch
+    import mlp_matmul_amd as uw
+    L = uw.lib()
+    stream = stream or torch.cuda.current_stream()
+    R, C = mats_bf16[0].shape
+    B = X.shape[0]
+    Y = torch.empty((B, R), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(4 * 4 * B * R + 256, dtype=torch.uint8, device="cuda")
+    opts = ([(uw.UW_KERNEL_GEMV, 1)] if B <= 16 else []) + [(uw.UW_KERNEL_MFMA, s_) for s_ in (1, 2, 4)]
+    best = None
+    for k, sk in opts:
+        calls = [lambda W=W: uw.check(L.uw_gemm_bf16(ct.c_void_p(W.data_ptr()), R, C, ct.c_void_p(X.data_ptr()), B,
+                                                     ct.c_void_p(Y.data_ptr()), k, sk,
+                                                     ct.c_void_p(scratch.data_ptr()), scratch.numel(),
+                                                     ct.c_void_p(stream.cuda_stream)), "uw_gemm_bf16")
+                 for W in mats_bf16]
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                calls[i % len(calls)]()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                calls[i % len(calls)]()
+            e1.record(stream)
+        e1.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / reps
+        best = t if best is None else min(best, t)
+    return best
+
+
+def batch_sweep(layers, batches):
+    """Autotune (pipeline x kernel x split-K) per shape and batch, and compare
+    the winner with the uncompressed bf16 matmul on the same copies."""
+    import torch
+    import mlp_matmul_amd as uw
+    from mlp_matmul_amd import autotune
+    import workloads
+    F, H = workloads.LLAMA_FFN, workloads.LLAMA_HIDDEN
+    copies = {(F, H): [L.mats[0] for L in layers], (H, F): [L.mats[2] for L in layers]}
+    bf16 = {(F, H): [L.bf16[0] for L in layers], (H, F): [L.bf16[2] for L in layers]}
+    xs = {}
+
+    def x_of(b, c):
+        m = 0 if c == H else 2
+        if (b, c) not in xs:
+            xs[(b, c)] = torch.from_numpy(workloads.layer_activation(2, 0, m, b, cols=c).view(np.int16)) \
+                .view(torch.bfloat16).cuda()
+        return xs[(b, c)]
+
+    uw.plan_clear()
+    report = autotune.tune(copies, batches, x_of)
+    out = []
+    for r, s_ in zip(report, autotune.summarize(report)):
+        shape = (r["rows"], r["cols"])
+        b = r["batch"]
+        t_b16 = time_bf16(bf16[shape], x_of(b, shape[1]))
+        best_us = min(s_["us"].values()) if s_["us"] else None
+        info = copies[shape][0].info
+        direct_bytes = palette_bytes(info, b)
+        row = {"shape": list(shape), "batch": b, "best": r["best"], "us": s_["us"],
+               "bf16_us": round(t_b16 * 1e6, 3),
+               "speedup_vs_bf16": round(t_b16 * 1e6 / best_us, 4) if best_us else None}
+        if "direct" in s_["us"]:
+            row["direct_compressed_GBps"] = round(direct_bytes / (s_["us"]["direct"] * 1e-6) / 1e9, 1)
+            row["direct_hbm_frac"] = round(row["direct_compressed_GBps"] / HBM_PEAK_GBPS, 4)
+            row["direct_mfma_TFLOPs"] = round(2 * b * info.rows * info.cols / (s_["us"]["direct"] * 1e-6) / 1e12, 2)
+        out.append(row)
+        log(f"sweep {shape} B={b}: best {r['best']} {s_['us']} bf16 {row['bf16_us']} us")
+    return out
+
+
 # ------------------------------------------------------------- CPU baseline
 def cpu_baseline(frac_rows=8, min_seconds=10.0):
     """The oracle's per-step work (rebuild bf16 from the direct-palette form,
@@ -369,6 +448,10 @@ def main():
         out["ms_per_step_by_pipeline"] = extra
         b16 = min(v for v in (extra["bf16"]["graph_ms"], extra["bf16"]["eager_ms"]) if v)
         out["speedup_vs_bf16"] = round(b16 / (sec * 1e3), 4)
+    if not a.no_sweep:
+        batches = [int(v) for v in a.sweep_batches.split(",") if v]
+        out["batch_sweep"] = batch_sweep(layers, batches)
+        out["plan"] = [{"shape": r["shape"], "batch": r["batch"], **(r["best"] or {})} for r in out["batch_sweep"]]
     if not a.no_cpu_baseline:
         log("timing the CPU oracle sample")
         out["cpu_baseline"] = cpu_baseline()

@@ -19,7 +19,7 @@ UW_EUNSUPPORTED = -5
  UW_SEC_BITMAP, UW_SEC_NIB, UW_SEC_DLUT, UW_NUM_SECTIONS) = range(10)
 SECTION_NAMES = ("sm", "stream", "glen", "tile_off", "tile_vbase", "vexp", "bitmap", "nib", "dlut")
 
-UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA = 0, 1, 2
+UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY = 0, 1, 2, 3
 UW_PIPE_AUTO, UW_PIPE_FULL, UW_PIPE_EXP, UW_PIPE_PAL, UW_PIPE_DIRECT, UW_PIPE_BF16 = range(6)
 
 

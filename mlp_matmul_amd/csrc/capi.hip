@@ -99,15 +99,21 @@ int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* s
         return uw::fail(UW_EINVAL, std::string(who) + ": sign/mantissa plane missing");
     if (src == uwk::SRC_PAL && a.R * a.C && (!a.bitmap || !a.tile_vbase))
         return uw::fail(UW_EINVAL, std::string(who) + ": verbatim tables missing");
-    if (kernel == UW_KERNEL_AUTO) kernel = a.B < 16 ? UW_KERNEL_GEMV : UW_KERNEL_MFMA;
+    if (kernel == UW_KERNEL_AUTO)
+        kernel = a.B < 4 ? UW_KERNEL_GEMV
+                         : (a.B <= 64 && uwk::mfma_gemv_supported(a) ? UW_KERNEL_SKINNY : UW_KERNEL_MFMA);
     if (kernel == UW_KERNEL_GEMV && a.B > 16)
         return uw::fail(UW_EINVAL, std::string(who) + ": the GEMV kernel takes batch <= 16");
-    if (kernel != UW_KERNEL_GEMV && kernel != UW_KERNEL_MFMA)
+    if (kernel == UW_KERNEL_SKINNY && !uwk::mfma_gemv_supported(a))
+        return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": the skinny MFMA kernel needs cols % 128 == 0 and cols <= 16384");
+    if (kernel < UW_KERNEL_GEMV || kernel > UW_KERNEL_SKINNY)
         return uw::fail(UW_EINVAL, std::string(who) + ": unknown kernel");
     if (split_k < 1 || split_k > 64) return uw::fail(UW_EINVAL, std::string(who) + ": split_k must be 1..64");
     hipError_t e;
     if (kernel == UW_KERNEL_GEMV) {
         e = uwk::launch_gemv(src, a, as_stream(stream));
+    } else if (kernel == UW_KERNEL_SKINNY) {
+        e = uwk::launch_mfma_gemv(src, a, as_stream(stream));
     } else {
         a.split_k = split_k;
         if (split_k > 1) {

@@ -46,7 +46,7 @@ int uw_plan_set(int64_t rows, int64_t cols, int64_t batch, int pipeline, int ker
     if (rows < 0 || cols < 0 || batch < 1) return uw::fail(UW_EINVAL, "uw_plan_set: bad key");
     if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_DIRECT)
         return uw::fail(UW_EINVAL, "uw_plan_set: pipeline must be one of UW_PIPE_FULL..UW_PIPE_DIRECT");
-    if (kernel < UW_KERNEL_AUTO || kernel > UW_KERNEL_MFMA || split_k < 1 || split_k > 64)
+    if (kernel < UW_KERNEL_AUTO || kernel > UW_KERNEL_SKINNY || split_k < 1 || split_k > 64)
         return uw::fail(UW_EINVAL, "uw_plan_set: bad kernel or split_k");
     std::lock_guard<std::mutex> lk(g_plan_mu);
     g_plan[{rows, cols, batch}] = {pipeline, kernel, split_k};

@@ -46,6 +46,8 @@ struct MatArgs {
 hipError_t launch_decode(int mode, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gemv(int src, const MatArgs& a, hipStream_t s);
 hipError_t launch_mfma(int src, const MatArgs& a, hipStream_t s);
+hipError_t launch_mfma_gemv(int src, const MatArgs& a, hipStream_t s);
+bool mfma_gemv_supported(const MatArgs& a);
 hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, uint16_t* h, hipStream_t s);
 
 // LDS bytes the decoder needs for a code of longest length lmax.

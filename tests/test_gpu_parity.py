@@ -104,7 +104,7 @@ def _one_hot(cols, C):
     return x
 
 
-@pytest.mark.parametrize("kernel", [uw.UW_KERNEL_GEMV, uw.UW_KERNEL_MFMA])
+@pytest.mark.parametrize("kernel", [uw.UW_KERNEL_GEMV, uw.UW_KERNEL_MFMA, uw.UW_KERNEL_SKINNY])
 def test_one_hot_reveals_rebuilt_weights(torch_cuda, kernel):
     """With X = rows of the identity, Y[b, r] = W[r, c_b] exactly: the fused
     kernels reveal the weights they rebuilt without writing them out."""
@@ -161,6 +161,68 @@ def test_mfma_small_workload(torch_cuda, B):
                     ("direct", uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_MFMA)),
                     ("exp", uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_MFMA))]:
         assert_matmul_close(Y.cpu().numpy(), w, x, what=f"mfma {name} B={B}")
+
+
+@pytest.mark.parametrize("B", [2, 3, 4, 7, 16, 17, 31, 33, 48, 64, 65, 100])
+def test_skinny_small_workload(torch_cuda, B):
+    print_case(f"skinny small workload B={B}")
+    w, _ = workloads.small_matrix()
+    x = _x(300 + B, B, w.shape[1])
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    exps = uw.decode_exponents(dm)
+    for name, Y in [("bf16", uw.gemm_bf16(to_dev_bf16(w), X, kernel=uw.UW_KERNEL_SKINNY)),
+                    ("direct", uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_SKINNY)),
+                    ("exp", uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_SKINNY))]:
+        assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny {name} B={B}")
+
+
+@pytest.mark.parametrize("R,C", [(1, 128), (3, 256), (37, 384), (130, 1152), (67, 2048 + 128), (19, 16384)])
+@pytest.mark.parametrize("B", [2, 9, 40])
+def test_skinny_ragged_shapes(torch_cuda, R, C, B):
+    """Row blocks past R, batch tiles past B, K-slices of unequal length, wave
+    slices that are empty (C = 128) and row segments that straddle tiles."""
+    print_case(f"skinny ragged R={R} C={C} B={B}")
+    w = workloads.gaussian_weights(np.random.default_rng(R * C + B + 7), R, C, 0.02, 0.004, 1.0)
+    x = _x(R + B + 1, B, C)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    exps = uw.decode_exponents(dm)
+    for name, Y in [("bf16", uw.gemm_bf16(to_dev_bf16(w), X, kernel=uw.UW_KERNEL_SKINNY)),
+                    ("direct", uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_SKINNY)),
+                    ("exp", uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_SKINNY))]:
+        assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny {name}")
+
+
+def test_skinny_mostly_verbatim(torch_cuda):
+    """About 85% of the groups hold exponents far outside the palette (stored
+    verbatim), mixed with ordinary groups: the verbatim override on most lanes
+    of most steps, next to palette lanes."""
+    print_case("skinny mostly verbatim")
+    rng = np.random.default_rng(11)
+    R, C = 96, 2048
+    wide = np.repeat(rng.random((R, C // 64)) < 0.85, 64, axis=1)
+    scale = np.where(wide, np.exp2(rng.integers(-12, 13, (R, C))), 1.0)
+    w = workloads.f32_to_bf16_bits((rng.standard_normal((R, C)) * 0.02 * scale).astype(np.float32))
+    x = _x(12, 24, C)
+    dm = uw.compress(w).to_device()
+    assert 0.8 * dm.info.groups < dm.info.verbatim_groups < dm.info.groups
+    exps = uw.decode_exponents(dm)
+    for name, Y in [("direct", uw.gemm_recon_pal(dm, None, to_dev_bf16(x), kernel=uw.UW_KERNEL_SKINNY)),
+                    ("exp", uw.gemm_recon_exp(dm, exps, to_dev_bf16(x), kernel=uw.UW_KERNEL_SKINNY))]:
+        assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny verbatim {name}")
+
+
+def test_skinny_rejects_unsupported_width(torch_cuda):
+    w = workloads.gaussian_weights(np.random.default_rng(3), 16, 192, 0.02, 0.0, 1.0)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(_x(3, 4, 192))
+    with pytest.raises(uw.UnweightError) as ei:
+        uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_SKINNY)
+    assert ei.value.code == uw.UW_EUNSUPPORTED
+    # AUTO falls back to the tiled MFMA kernel for such widths
+    Y = uw.gemm_recon_pal(dm, None, X)
+    assert_matmul_close(Y.cpu().numpy(), w, _x(3, 4, 192), what="auto width 192")
 
 
 @pytest.mark.parametrize("split", [2, 3, 4, 16])
@@ -227,7 +289,7 @@ def test_four_pipelines_small_workload(torch_cuda, B):
 def test_deterministic(torch_cuda):
     w, _ = workloads.small_matrix()
     dm = uw.compress(w).to_device()
-    for B, k in [(1, uw.UW_KERNEL_GEMV), (64, uw.UW_KERNEL_MFMA)]:
+    for B, k in [(1, uw.UW_KERNEL_GEMV), (64, uw.UW_KERNEL_MFMA), (32, uw.UW_KERNEL_SKINNY)]:
         X = to_dev_bf16(_x(B, B, 1024))
         a = uw.gemm_recon_pal(dm, None, X, kernel=k).cpu().numpy()
         b = uw.gemm_recon_pal(dm, None, X, kernel=k).cpu().numpy()
@@ -316,6 +378,23 @@ def test_full_size_gemv_batch1_all_pipelines(torch_cuda, m):
         Y = uw.matmul(dm, X, pipeline=p, scratch=scratch).cpu().numpy()
         rel = assert_matmul_close(Y, w, x, what=f"{name}")
         assert rel < TOL
+
+
+@pytest.mark.parametrize("m", [0, 2])
+@pytest.mark.parametrize("B", [8, 64])
+def test_full_size_skinny_all_pipelines(torch_cuda, m, B):
+    """Llama-3.1-8B gate and down at batch 8 and 64 on the skinny MFMA kernel,
+    every pipeline: sampled rows against the fp64 oracle."""
+    print_case(f"full-size skinny matrix {m} B={B}")
+    w = workloads.layer_weight(2, 1, m)
+    x = workloads.layer_activation(2, 1, m, B)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    rows = np.sort(np.random.default_rng(B + m).choice(w.shape[0], 384, replace=False))
+    for name, p in uw.PIPELINES.items():
+        scratch = uw.alloc_scratch(p, w.shape[0], w.shape[1], B)
+        Y = uw.matmul(dm, X, pipeline=p, kernel=uw.UW_KERNEL_SKINNY, scratch=scratch).cpu().numpy()
+        assert_matmul_close(Y[:, rows], w, x, rows=rows, what=f"{name} B={B}")
 
 
 @pytest.mark.parametrize("B", [64, 128, 256])
