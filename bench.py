@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "compressed-MLP matmul: bf16-equiv weight GB/s, % HBM peak, batch 1\u2013256"
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -214,18 +215,23 @@ class GraphStep:
 
 # --------------------------------------------------------------- batch sweep
 def time_bf16(mats_bf16, X, reps=20, warmup=3, stream=None):
-    """Best seconds per call of the uncompressed bf16 matmul (GEMV for batch
-    <= 16, MFMA with split-K 1/2/4 otherwise), rotating over the copies."""
+    """Best seconds per call of the hand-written uncompressed bf16 matmul (the
+    same kernel families on bf16 weights: GEMV for batch <= 16, skinny MFMA
+    for batch 2..64, tiled MFMA with split-K 1/2/4), rotating over the copies.
+    Returns (seconds, kernel name)."""
     import ctypes as ct
     import torch
     import mlp_matmul_amd as uw
+    from mlp_matmul_amd import autotune
     L = uw.lib()
     stream = stream or torch.cuda.current_stream()
     R, C = mats_bf16[0].shape
     B = X.shape[0]
     Y = torch.empty((B, R), dtype=torch.float32, device="cuda")
     scratch = torch.empty(4 * 4 * B * R + 256, dtype=torch.uint8, device="cuda")
-    opts = ([(uw.UW_KERNEL_GEMV, 1)] if B <= 16 else []) + [(uw.UW_KERNEL_MFMA, s_) for s_ in (1, 2, 4)]
+    opts = ([(uw.UW_KERNEL_GEMV, 1)] if B <= 16 else []) \
+        + ([(uw.UW_KERNEL_SKINNY, 1)] if 2 <= B <= 64 and autotune.skinny_ok(C) else []) \
+        + [(uw.UW_KERNEL_MFMA, s_) for s_ in (1, 2, 4)]
     best = None
     for k, sk in opts:
         calls = [lambda W=W: uw.check(L.uw_gemm_bf16(ct.c_void_p(W.data_ptr()), R, C, ct.c_void_p(X.data_ptr()), B,
@@ -243,8 +249,25 @@ def time_bf16(mats_bf16, X, reps=20, warmup=3, stream=None):
             e1.record(stream)
         e1.synchronize()
         t = e0.elapsed_time(e1) / 1e3 / reps
-        best = t if best is None else min(best, t)
+        name = autotune.KERNEL_NAMES[k] + (f"(split {sk})" if sk > 1 else "")
+        best = (t, name) if best is None or t < best[0] else best
     return best
+
+
+def time_torch_bf16(mats_bf16, X, reps=20, warmup=3):
+    """Seconds per call of torch.matmul(X, W^T) on the same bf16 copies (the
+    vendor GEMM library): context next to the hand-written baseline."""
+    import torch
+    with torch.no_grad():
+        for i in range(warmup):
+            torch.matmul(X, mats_bf16[i % len(mats_bf16)].t())
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            torch.matmul(X, mats_bf16[i % len(mats_bf16)].t())
+        e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / reps
 
 
 def batch_sweep(layers, batches):
@@ -272,19 +295,28 @@ def batch_sweep(layers, batches):
     for r, s_ in zip(report, autotune.summarize(report)):
         shape = (r["rows"], r["cols"])
         b = r["batch"]
-        t_b16 = time_bf16(bf16[shape], x_of(b, shape[1]))
+        t_b16, k_b16 = time_bf16(bf16[shape], x_of(b, shape[1]))
+        t_torch = time_torch_bf16(bf16[shape], x_of(b, shape[1]))
         best_us = min(s_["us"].values()) if s_["us"] else None
         info = copies[shape][0].info
         direct_bytes = palette_bytes(info, b)
+        flops = 2 * b * info.rows * info.cols
         row = {"shape": list(shape), "batch": b, "best": r["best"], "us": s_["us"],
-               "bf16_us": round(t_b16 * 1e6, 3),
-               "speedup_vs_bf16": round(t_b16 * 1e6 / best_us, 4) if best_us else None}
+               "bf16_us": round(t_b16 * 1e6, 3), "bf16_kernel": k_b16,
+               "speedup_vs_bf16": round(t_b16 * 1e6 / best_us, 4) if best_us else None,
+               "torch_bf16_us": round(t_torch * 1e6, 3),
+               "speedup_vs_torch_bf16": round(t_torch * 1e6 / best_us, 4) if best_us else None,
+               "best_bf16_equiv_GBps": round(2 * info.rows * info.cols / (best_us * 1e-6) / 1e9, 1) if best_us else None}
         if "direct" in s_["us"]:
             row["direct_compressed_GBps"] = round(direct_bytes / (s_["us"]["direct"] * 1e-6) / 1e9, 1)
             row["direct_hbm_frac"] = round(row["direct_compressed_GBps"] / HBM_PEAK_GBPS, 4)
-            row["direct_mfma_TFLOPs"] = round(2 * b * info.rows * info.cols / (s_["us"]["direct"] * 1e-6) / 1e12, 2)
+        if best_us and r["best"] and r["best"]["kernel"] != "gemv":
+            # bf16 MFMA utilisation of the best candidate against the dense peak
+            row["best_mfma_TFLOPs"] = round(flops / (best_us * 1e-6) / 1e12, 2)
+            row["best_mfma_util"] = round(row["best_mfma_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS, 5)
         out.append(row)
-        log(f"sweep {shape} B={b}: best {r['best']} {s_['us']} bf16 {row['bf16_us']} us")
+        log(f"sweep {shape} B={b}: best {r['best']} {s_['us']} bf16 {row['bf16_us']} ({k_b16}) "
+            f"torch {row['torch_bf16_us']} us")
     return out
 
 

@@ -205,7 +205,7 @@ enum {
     UW_KERNEL_GEMV = 1,    /* wavefront-reduction GEMV (v_dot2 bf16), batch <= 16 */
     UW_KERNEL_MFMA = 2,    /* bf16 MFMA, 32 rows x up to 128 batch columns per wave, any batch */
     UW_KERNEL_SKINNY = 3   /* bf16 MFMA, 16 rows x one K-slice per wave, batch tiles of <= 64;
-                              needs cols % 128 == 0 and cols <= 16384 (else UW_EUNSUPPORTED) */
+                              needs cols % 128 == 0 and cols <= 32768 (else UW_EUNSUPPORTED) */
 };
 
 /* Uncompressed baseline and pipeline 1's consumer ("Four ways to use

@@ -30,7 +30,7 @@ KERNEL_NAMES = {UW_KERNEL_GEMV: "gemv", UW_KERNEL_MFMA: "mfma", UW_KERNEL_SKINNY
 
 def skinny_ok(cols):
     steps = cols // 128
-    return cols > 0 and cols % 128 == 0 and (steps + 3) // 4 * 128 <= 4096
+    return cols > 0 and cols % 128 == 0 and (steps + 7) // 8 * 128 <= 4096
 
 
 def candidates(rows, cols, batch, has_palette=True):

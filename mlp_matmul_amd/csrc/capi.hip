@@ -105,7 +105,7 @@ int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* s
     if (kernel == UW_KERNEL_GEMV && a.B > 16)
         return uw::fail(UW_EINVAL, std::string(who) + ": the GEMV kernel takes batch <= 16");
     if (kernel == UW_KERNEL_SKINNY && !uwk::mfma_gemv_supported(a))
-        return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": the skinny MFMA kernel needs cols % 128 == 0 and cols <= 16384");
+        return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": the skinny MFMA kernel needs cols % 128 == 0 and cols <= 32768");
     if (kernel < UW_KERNEL_GEMV || kernel > UW_KERNEL_SKINNY)
         return uw::fail(UW_EINVAL, std::string(who) + ": unknown kernel");
     if (split_k < 1 || split_k > 64) return uw::fail(UW_EINVAL, std::string(who) + ": split_k must be 1..64");

@@ -18,10 +18,10 @@ def test_candidate_space():
     assert any(k == uw.UW_KERNEL_GEMV for _, k, _ in c)
     # no GEMV beyond batch 16, split-K only offered to short matrices
     assert {k for _, k, _ in autotune.candidates(14336, 4096, 64)} == {uw.UW_KERNEL_MFMA, uw.UW_KERNEL_SKINNY}
-    # the skinny kernel needs whole 128-column steps and at most 16384 columns
+    # the skinny kernel needs whole 128-column steps and at most 32768 columns
     assert uw.UW_KERNEL_SKINNY not in {k for _, k, _ in autotune.candidates(64, 192, 8)}
-    assert uw.UW_KERNEL_SKINNY not in {k for _, k, _ in autotune.candidates(64, 16384 + 128, 8)}
-    assert uw.UW_KERNEL_SKINNY in {k for _, k, _ in autotune.candidates(64, 16384, 8)}
+    assert uw.UW_KERNEL_SKINNY not in {k for _, k, _ in autotune.candidates(64, 32768 + 128, 8)}
+    assert uw.UW_KERNEL_SKINNY in {k for _, k, _ in autotune.candidates(64, 32768, 8)}
     assert {s for _, _, s in autotune.candidates(4096, 14336, 256)} == {1, 2, 4}
     assert {s for _, _, s in autotune.candidates(14336, 4096, 256)} == {1}
     assert uw.UW_PIPE_DIRECT not in {p for p, _, _ in autotune.candidates(64, 64, 1, has_palette=False)}

@@ -177,7 +177,8 @@ def test_skinny_small_workload(torch_cuda, B):
         assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny {name} B={B}")
 
 
-@pytest.mark.parametrize("R,C", [(1, 128), (3, 256), (37, 384), (130, 1152), (67, 2048 + 128), (19, 16384)])
+@pytest.mark.parametrize("R,C", [(1, 128), (3, 256), (37, 384), (130, 1152), (67, 2048 + 128), (19, 16384),
+                                 (5, 32768)])
 @pytest.mark.parametrize("B", [2, 9, 40])
 def test_skinny_ragged_shapes(torch_cuda, R, C, B):
     """Row blocks past R, batch tiles past B, K-slices of unequal length, wave
@@ -192,6 +193,30 @@ def test_skinny_ragged_shapes(torch_cuda, R, C, B):
                     ("direct", uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_SKINNY)),
                     ("exp", uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_SKINNY))]:
         assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny {name}")
+
+
+@pytest.mark.parametrize("kw", [2, 4, 8])
+@pytest.mark.parametrize("pd", [1, 2])
+@pytest.mark.parametrize("rb", [1, 2])
+def test_skinny_launch_shapes(torch_cuda, monkeypatch, kw, pd, rb):
+    """Every K-split width, prefetch depth and row-block count the launcher
+    can pick (the tuning overrides UW_SKINNY_KW / _PD / _RB), on slices of
+    1..9 steps with row segments that straddle tiles, rows past R and each
+    batch-tile count."""
+    monkeypatch.setenv("UW_SKINNY_KW", str(kw))
+    monkeypatch.setenv("UW_SKINNY_PD", str(pd))
+    monkeypatch.setenv("UW_SKINNY_RB", str(rb))
+    for R, C, B in [(45, 1152, 5), (33, 4096 + 512, 20), (17, 9216, 64)]:
+        print_case(f"skinny kw={kw} pd={pd} rb={rb} R={R} C={C} B={B}")
+        w = workloads.gaussian_weights(np.random.default_rng(R + C + kw + pd), R, C, 0.02, 0.004, 1.0)
+        x = _x(C + B, B, C)
+        dm = uw.compress(w).to_device()
+        X = to_dev_bf16(x)
+        exps = uw.decode_exponents(dm)
+        for name, Y in [("bf16", uw.gemm_bf16(to_dev_bf16(w), X, kernel=uw.UW_KERNEL_SKINNY)),
+                        ("direct", uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_SKINNY)),
+                        ("exp", uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_SKINNY))]:
+            assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny {name} kw={kw} pd={pd} rb={rb} C={C}")
 
 
 def test_skinny_mostly_verbatim(torch_cuda):
