@@ -49,6 +49,11 @@ def parse():
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the autotuned batch sweep (1..256) over the gate and down shapes")
     p.add_argument("--sweep-batches", default="1,2,4,8,16,32,64,128,256")
+    p.add_argument("--no-stack", action="store_true",
+                   help="skip the 32-layer stack (generation ~1 min, ~22 GB of device memory)")
+    p.add_argument("--stack-layers", type=int, default=32)
+    p.add_argument("--stack-batches", default="1,2,4,8,16,32,64,128,256")
+    p.add_argument("--stack-workers", type=int, default=12)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch a plain device copy of known size (for counter calibration)")
     return p.parse_args()
@@ -94,7 +99,7 @@ class Step:
     that the host issues a step in a few microseconds and the GPU queue stays
     ahead of it (the timed region measures the GPU, not Python)."""
 
-    def __init__(self, layers, batch, pipeline, stream=None):
+    def __init__(self, layers, batch, pipeline, stream=None, workload=2, bf16_choice=None):
         import ctypes as ct
         import functools
         import torch
@@ -105,7 +110,7 @@ class Step:
         pipe = {"direct": uw.UW_PIPE_DIRECT, "pal": uw.UW_PIPE_PAL, "exp": uw.UW_PIPE_EXP,
                 "full": uw.UW_PIPE_FULL, "auto": uw.UW_PIPE_AUTO, "bf16": uw.UW_PIPE_BF16}[pipeline]
         F, H = workloads.LLAMA_FFN, workloads.LLAMA_HIDDEN
-        self.X = [torch.from_numpy(workloads.layer_activation(2, i, 0, batch).view(np.int16))
+        self.X = [torch.from_numpy(workloads.layer_activation(workload, i, 0, batch).view(np.int16))
                   .view(torch.bfloat16).cuda() for i in range(len(layers))]
         self.g = torch.empty((batch, F), dtype=torch.float32, device="cuda")
         self.u = torch.empty_like(self.g)
@@ -130,8 +135,9 @@ class Step:
                 xin, yout = outs[m]
                 if pipe == uw.UW_PIPE_BF16:
                     R, C = lay.bf16[m].shape
-                    row.append(functools.partial(L.uw_gemm_bf16, P(lay.bf16[m]), R, C, xin, batch, yout, 0, 1,
-                                                 None, 0, st))
+                    k, sk = (bf16_choice or {}).get((R, C), (0, 1))
+                    row.append(functools.partial(L.uw_gemm_bf16, P(lay.bf16[m]), R, C, xin, batch, yout, k, sk,
+                                                 scr, nsc, st))
                 else:
                     row.append(functools.partial(L.uw_matmul, ct.byref(lay.mats[m].dmat), pipe, 0, 1, xin,
                                                  batch, yout, scr, nsc, st))
@@ -218,7 +224,7 @@ def time_bf16(mats_bf16, X, reps=20, warmup=3, stream=None):
     """Best seconds per call of the hand-written uncompressed bf16 matmul (the
     same kernel families on bf16 weights: GEMV for batch <= 16, skinny MFMA
     for batch 2..64, tiled MFMA with split-K 1/2/4), rotating over the copies.
-    Returns (seconds, kernel name)."""
+    Returns (seconds, kernel name, kernel id, split_k)."""
     import ctypes as ct
     import torch
     import mlp_matmul_amd as uw
@@ -250,7 +256,7 @@ def time_bf16(mats_bf16, X, reps=20, warmup=3, stream=None):
         e1.synchronize()
         t = e0.elapsed_time(e1) / 1e3 / reps
         name = autotune.KERNEL_NAMES[k] + (f"(split {sk})" if sk > 1 else "")
-        best = (t, name) if best is None or t < best[0] else best
+        best = (t, name, k, sk) if best is None or t < best[0] else best
     return best
 
 
@@ -295,7 +301,7 @@ def batch_sweep(layers, batches):
     for r, s_ in zip(report, autotune.summarize(report)):
         shape = (r["rows"], r["cols"])
         b = r["batch"]
-        t_b16, k_b16 = time_bf16(bf16[shape], x_of(b, shape[1]))
+        t_b16, k_b16, _, _ = time_bf16(bf16[shape], x_of(b, shape[1]))
         t_torch = time_torch_bf16(bf16[shape], x_of(b, shape[1]))
         best_us = min(s_["us"].values()) if s_["us"] else None
         info = copies[shape][0].info
@@ -318,6 +324,160 @@ def batch_sweep(layers, batches):
         log(f"sweep {shape} B={b}: best {r['best']} {s_['us']} bf16 {row['bf16_us']} ({k_b16}) "
             f"torch {row['torch_bf16_us']} us")
     return out
+
+
+# ------------------------------------------------------------ 32-layer stack
+def _stack_blob(job):
+    """Pool worker: generate and compress one matrix of the stack (host only,
+    no GPU call).  Returns (layer, matrix, serialized blob)."""
+    layer, m = job
+    import mlp_matmul_amd as uw
+    import workloads
+    w = workloads.layer_weight(5, layer, m)
+    return layer, m, uw.compress(w, emit_palette=True, threads=2).serialize()
+
+
+def generate_stack_blobs(n_layers, workers):
+    """Serialized blobs of every gate/up/down matrix of the stack, generated by
+    a fork pool.  Must run before this process initialises the GPU (the
+    children are forked copies of it)."""
+    import multiprocessing as mp
+    import torch
+    assert not torch.cuda.is_initialized(), "generate the stack before touching the GPU"
+    jobs = [(l, m) for l in range(n_layers) for m in range(3)]
+    blobs = {}
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        for i, (l, m, data) in enumerate(pool.imap_unordered(_stack_blob, jobs)):
+            blobs[(l, m)] = data
+            if (i + 1) % 12 == 0:
+                log(f"stack: {i + 1}/{len(jobs)} matrices compressed ({time.perf_counter() - t0:.0f} s)")
+    return blobs
+
+
+class StackLayer:
+    """One layer of the stack on the device: compressed gate/up/down, and bf16
+    copies rebuilt by the full-decode kernel (bit-exact)."""
+
+    def __init__(self, blobs, layer, keep_bf16):
+        import mlp_matmul_amd as uw
+        self.mats, self.bf16, self.info = [], [], []
+        self.huffman_bytes = self.palette_bytes = self.bf16_bytes = self.device_bytes = 0
+        for m in range(3):
+            blob = uw.Blob.deserialize(blobs.pop((layer, m)))
+            dm = blob.to_device(uw.DECODE_SECTIONS + ("nib",))
+            inf = dm.info
+            self.mats.append(dm)
+            self.info.append(inf)
+            self.huffman_bytes += inf.huffman_form_bytes
+            self.palette_bytes += inf.palette_form_bytes
+            self.bf16_bytes += 2 * inf.rows * inf.cols
+            self.device_bytes += dm.device_bytes()
+            if keep_bf16:
+                self.bf16.append(uw.decode_full(dm))
+            del blob
+
+
+def time_stack(step, reps, warmup=1):
+    """Seconds per pass of the whole stack (every layer once)."""
+    import torch
+    n = len(step.layers)
+    with torch.cuda.stream(step.stream):
+        for _ in range(warmup):
+            for li in range(n):
+                step.run(li)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for li in range(n):
+                step.run(li)
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps
+
+
+def time_torch_stack(layers, batch, reps, warmup=1):
+    """The same stack through torch.matmul and torch's SiLU (vendor library
+    context; bf16 outputs)."""
+    import torch
+    import workloads
+    Xs = [torch.from_numpy(workloads.layer_activation(5, i, 0, batch).view(np.int16)).view(torch.bfloat16).cuda()
+          for i in range(len(layers))]
+
+    def one():
+        for lay, X in zip(layers, Xs):
+            g = torch.matmul(X, lay.bf16[0].t())
+            u = torch.matmul(X, lay.bf16[1].t())
+            h = torch.nn.functional.silu(g) * u
+            torch.matmul(h, lay.bf16[2].t())
+    with torch.no_grad():
+        for _ in range(warmup):
+            one()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            one()
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / reps
+
+
+def stack_bench(blobs, n_layers, batches, tune_copies=4, reps=5):
+    """The 32-layer Llama-3.1-8B MLP stack with per-layer outlier rates:
+    total sizes, the autotuner's plan per matrix shape and batch (tuned on
+    the stack's own first layers), and whole-stack time per batch against the
+    hand-written bf16 kernels and torch on the same (decoded) weights."""
+    import torch
+    import mlp_matmul_amd as uw
+    from mlp_matmul_amd import autotune
+    import workloads
+    t0 = time.perf_counter()
+    layers = [StackLayer(blobs, l, keep_bf16=True) for l in range(n_layers)]
+    log(f"stack: {n_layers} layers on the device in {time.perf_counter() - t0:.1f} s")
+    F, H = workloads.LLAMA_FFN, workloads.LLAMA_HIDDEN
+    sizes = {k: int(sum(getattr(L, k) for L in layers))
+             for k in ("bf16_bytes", "huffman_bytes", "palette_bytes", "device_bytes")}
+    verb = sum(i.verbatim_groups for L in layers for i in L.info) / sum(i.groups for L in layers for i in L.info)
+    nt = min(tune_copies, n_layers)
+    copies = {(F, H): [L.mats[0] for L in layers[:nt]], (H, F): [L.mats[2] for L in layers[:nt]]}
+    bf16_copies = {(F, H): [L.bf16[0] for L in layers[:nt]], (H, F): [L.bf16[2] for L in layers[:nt]]}
+    stream = torch.cuda.Stream()
+    rows = []
+    for b in batches:
+        def x_of(bb, c, _m={}):
+            key = (bb, c)
+            if key not in _m:
+                _m[key] = torch.from_numpy(workloads.layer_activation(5, 0, 0 if c == H else 2, bb, cols=c)
+                                           .view(np.int16)).view(torch.bfloat16).cuda()
+            return _m[key]
+        uw.plan_clear()
+        report = autotune.tune(copies, [b], x_of)
+        choice = {}
+        for shape in copies:
+            _, name, k, sk = time_bf16(bf16_copies[shape], x_of(b, shape[1]))
+            choice[shape] = (k, sk)
+        st = Step(layers, b, "auto", stream=stream, workload=5)
+        t_c = time_stack(st, reps)
+        del st
+        sb = Step(layers, b, "bf16", stream=stream, workload=5, bf16_choice=choice)
+        t_b = time_stack(sb, reps)
+        del sb
+        t_t = time_torch_stack(layers, b, reps)
+        row = {"batch": b, "ms": round(t_c * 1e3, 4), "bf16_ms": round(t_b * 1e3, 4), "torch_bf16_ms": round(t_t * 1e3, 4),
+               "speedup_vs_bf16": round(t_b / t_c, 4), "speedup_vs_torch_bf16": round(t_t / t_c, 4),
+               "bf16_equiv_GBps": round(sizes["bf16_bytes"] / t_c / 1e9, 1),
+               "plan": [{"shape": [r["rows"], r["cols"]], **(r["best"] or {})} for r in report],
+               "bf16_kernels": {f"{s_[0]}x{s_[1]}": autotune.KERNEL_NAMES[k] + (f"(split {sk})" if sk > 1 else "")
+                                for s_, (k, sk) in choice.items()}}
+        rows.append(row)
+        log(f"stack B={b}: {row['ms']} ms (bf16 {row['bf16_ms']}, torch {row['torch_bf16_ms']}) plan {row['plan']}")
+    uw.plan_clear()
+    return {"workload": "llama3.1-8b-mlp-stack", "layers": n_layers,
+            "weights": "N(0,0.02) + per-layer outlier rate U[0.01%, 0.2%] of N(0,0.5), seeded",
+            "inputs": "one seeded N(0,1) bf16 activation per layer (unit-variance, as after a norm)",
+            **sizes, "verbatim_group_frac": round(verb, 5),
+            "huffman_saved_bytes": sizes["bf16_bytes"] - sizes["huffman_bytes"],
+            "huffman_ratio": round(sizes["huffman_bytes"] / sizes["bf16_bytes"], 5),
+            "palette_ratio": round(sizes["palette_bytes"] / sizes["bf16_bytes"], 5),
+            "sweep": rows}
 
 
 # ------------------------------------------------------------- CPU baseline
@@ -391,6 +551,11 @@ def main():
     import torch
     import mlp_matmul_amd as uw
     import workloads
+    blobs = None
+    if not a.no_stack:
+        # host-only generation first: the pool forks this process, which must
+        # not have touched the GPU yet
+        blobs = generate_stack_blobs(a.stack_layers, a.stack_workers)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     uw.lib()
     B = a.batch
@@ -484,6 +649,8 @@ def main():
         batches = [int(v) for v in a.sweep_batches.split(",") if v]
         out["batch_sweep"] = batch_sweep(layers, batches)
         out["plan"] = [{"shape": r["shape"], "batch": r["batch"], **(r["best"] or {})} for r in out["batch_sweep"]]
+    if blobs is not None:
+        out["stack"] = stack_bench(blobs, a.stack_layers, [int(v) for v in a.stack_batches.split(",") if v])
     if not a.no_cpu_baseline:
         log("timing the CPU oracle sample")
         out["cpu_baseline"] = cpu_baseline()

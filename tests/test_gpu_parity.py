@@ -422,6 +422,26 @@ def test_full_size_skinny_all_pipelines(torch_cuda, m, B):
         assert_matmul_close(Y[:, rows], w, x, rows=rows, what=f"{name} B={B}")
 
 
+@pytest.mark.parametrize("layer", [0, 17, 31])
+def test_full_size_stack_layers(torch_cuda, layer):
+    """Layers of the 32-layer stack (per-layer outlier rate): gate and down
+    through the default (direct-palette) and palette-transcode pipelines at
+    batch 1 and 16, sampled rows against the fp64 oracle."""
+    for m in (0, 2):
+        w = workloads.layer_weight(5, layer, m)
+        dm = uw.compress(w).to_device()
+        for B in (1, 16):
+            print_case(f"stack layer {layer} matrix {m} B={B}")
+            x = workloads.layer_activation(5, layer, m, B)
+            X = to_dev_bf16(x)
+            rows = np.sort(np.random.default_rng(layer * 7 + m + B).choice(w.shape[0], 256, replace=False))
+            uw.plan_clear()
+            for name, p in (("auto", uw.UW_PIPE_AUTO), ("pal", uw.UW_PIPE_PAL)):
+                scratch = uw.alloc_scratch(p if p != uw.UW_PIPE_AUTO else uw.UW_PIPE_DIRECT, *w.shape, B)
+                Y = uw.matmul(dm, X, pipeline=p, scratch=scratch).cpu().numpy()
+                assert_matmul_close(Y[:, rows], w, x, rows=rows, what=f"{name} layer {layer} m {m} B={B}")
+
+
 @pytest.mark.parametrize("B", [64, 128, 256])
 def test_full_size_mfma_row_spread_workload(torch_cuda, B):
     """Per-row-scaled weights at large batch: sampled rows against the oracle."""
