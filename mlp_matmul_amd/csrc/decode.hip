@@ -33,9 +33,7 @@ __device__ __forceinline__ uint32_t load_word(const uint8_t* s, uint32_t w, uint
     return v;
 }
 
-__device__ __forceinline__ uint32_t pal_byte(const DecodeArgs& a, int i) {
-    return (a.pal[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-}
+__device__ __forceinline__ uint32_t pal_byte(const DecodeArgs& a, int i) { return uwk::pal_byte(a.pal, uint32_t(i)); }
 
 template <int MODE>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {

@@ -86,6 +86,18 @@ __device__ __forceinline__ void store16(void* p, u32x4_t v) {
 
 // Index of a verbatim group among all verbatim groups: the count before its
 // tile plus the flagged groups before it inside the tile's bitmap word.
+// Palette byte i (0..15) of the four packed palette words, selected without
+// indexing: the words stay in scalar registers and no memory is read.
+__device__ __forceinline__ uint32_t pal_byte(const uint32_t (&pal)[4], uint32_t i) {
+    // readfirstlane keeps the four words opaque uniform values, so the selects
+    // are not folded back into a load from a lane-dependent address
+    const uint32_t p0 = __builtin_amdgcn_readfirstlane(pal[0]), p1 = __builtin_amdgcn_readfirstlane(pal[1]);
+    const uint32_t p2 = __builtin_amdgcn_readfirstlane(pal[2]), p3 = __builtin_amdgcn_readfirstlane(pal[3]);
+    const uint32_t lo = (i & 4u) ? p1 : p0;
+    const uint32_t hi = (i & 4u) ? p3 : p2;
+    return (((i & 8u) ? hi : lo) >> (8u * (i & 3u))) & 0xFFu;
+}
+
 __device__ __forceinline__ uint32_t verbatim_slot(uint64_t word, uint32_t bit, uint32_t vbase) {
     uint64_t below = bit ? (word & ((~0ull) >> (64 - bit))) : 0ull;
     return vbase + uint32_t(__popcll(below));

@@ -28,9 +28,7 @@ namespace {
 constexpr int kKB = 64;           // K per pipeline step
 constexpr int kXS = kKB + 8;      // LDS row stride of the activation tile (bf16)
 
-__device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) {
-    return (a.pal[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-}
+__device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) { return pal_byte(a.pal, uint32_t(i)); }
 
 template <int SRC>
 struct AFrag {

@@ -46,9 +46,7 @@ namespace {
 constexpr int kSlab = 1024;            // weights per row per item: 64 lanes x 16
 constexpr int kXLdsMax = 32 * 1024;    // activation bytes staged in LDS at most
 
-__device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) {
-    return (a.pal[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-}
+__device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) { return pal_byte(a.pal, uint32_t(i)); }
 
 // Element offsets (within a slab) of a lane's two 8-weight halves.
 template <int SRC>
@@ -83,10 +81,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
     const int ngroups = (wrows + NRW - 1) / NRW;
     const int iters = int((C + kSlab - 1) / kSlab);
     const int total = ngroups * iters;                           // items: (group, slab)
+    // a wave past the matrix issues its loads from row 0 (so every wave runs
+    // the same load sequence) and leaves before computing
+    const int64_t rl0 = live ? r0 : 0;
 
     // the verbatim tables of every tile the wave's rows touch, one per lane
-    // (loaded after item 0's weight loads are out)
-    const int64_t t_first = (r0 * C) >> 12;
+    const int64_t t_first = (rl0 * C) >> 12;
     uint64_t my_word = 0;
     uint32_t my_vbase = 0;
     // a lane's group inside a 1024-weight slab, and the mask of the groups below it
@@ -106,15 +106,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
     // rows past the matrix (beyond wrows) re-read the wave's first row; their
     // sums are never stored.  issue_w: the weight planes (no dependency);
     // issue_v: the verbatim exponents, whose address needs the wave's tables.
-    auto row_of = [&](int t, int r) -> uint32_t {
-        const int rr = (t / iters) * NRW + r;                    // row inside the wave's range
-        return uint32_t(r0) + uint32_t(rr < wrows ? rr : 0);
+    // an item is (row group g, slab s); items run g-major
+    struct Item {
+        int g, s;
     };
-    auto issue_w = [&](int t, Chunk<SRC>* ch) {
-        const uint32_t k0 = uint32_t(t % iters) * kSlab;
+    auto row_of = [&](Item it, int r) -> uint32_t {
+        const int rr = it.g * NRW + r;                           // row inside the wave's range
+        return uint32_t(rl0) + uint32_t(rr < wrows ? rr : 0);
+    };
+    auto issue_w = [&](Item it, Chunk<SRC>* ch) {
+        const uint32_t k0 = uint32_t(it.s) * kSlab;
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
-            const uint32_t row = row_of(t, r);
+            const uint32_t row = row_of(it, r);
             Chunk<SRC>& c = ch[r];
             uint32_t k = k0 + half_off<SRC>(lane, 0);
             if (!EXACT && k >= Cu) k = 0;
@@ -134,12 +138,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
             }
         }
     };
-    auto issue_v = [&](int t, Chunk<SRC>* ch) {
+    auto issue_v = [&](Item it, Chunk<SRC>* ch) {
         if (SRC != SRC_PAL) return;
-        const uint32_t k0 = uint32_t(t % iters) * kSlab;
+        const uint32_t k0 = uint32_t(it.s) * kSlab;
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
-            const uint32_t row = row_of(t, r);
+            const uint32_t row = row_of(it, r);
             Chunk<SRC>& c = ch[r];
             uint32_t k = k0 + half_off<SRC>(lane, 0);
             if (!EXACT && k >= Cu) k = 0;
@@ -178,33 +182,38 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
             c.vx = load16(vb_ptr + voff);
         }
     };
-    auto issue = [&](int t, Chunk<SRC>* ch) {
-        issue_w(t, ch);
-        issue_v(t, ch);
+    auto issue = [&](Item it, Chunk<SRC>* ch) {
+        issue_w(it, ch);
+        issue_v(it, ch);
     };
 
-    Chunk<SRC> cur[NRW], nxt[NRW];
+    auto next = [&](Item it) { return it.s + 1 == iters ? Item{it.g + 1, 0} : Item{it.g, it.s + 1}; };
+    Chunk<SRC> set0[NRW], set1[NRW];
+    const Item it0{0, 0};
     // item 0's weight loads go out first; the verbatim tables of every tile
-    // the wave's rows touch (one per lane) follow, then item 0's verbatim loads
-    if (live) issue_w(0, cur);
-    if (SRC == SRC_PAL && live) {
-        const int64_t t_end = ((r0 + wrows) * C + 4095) >> 12;
-        if (t_first + lane < t_end) {
-            my_word = a.bitmap[t_first + lane];
-            my_vbase = a.tile_vbase[t_first + lane];
+    // the wave's rows touch (one per lane) follow, then item 0's verbatim
+    // loads, then the activations are staged.  (Issuing item 1 here as well,
+    // ahead of the staging, measured slower.)
+    if (live) {
+        issue_w(it0, set0);
+        if (SRC == SRC_PAL) {
+            const int64_t t_end = max(((rl0 + wrows) * C + 4095) >> 12, t_first + 1);
+            const int64_t tl = min(t_first + lane, t_end - 1);
+            my_word = a.bitmap[tl];
+            my_vbase = a.tile_vbase[tl];
         }
+        issue_v(it0, set0);
     }
-    if (live) issue_v(0, cur);
     if (XLDS) {
-        const int64_t n16 = int64_t(B) * C / 8;                  // 16-byte pieces
+        const int64_t n16 = int64_t(B) * C / 8;
         for (int64_t i = tid; i < n16; i += 256)
             reinterpret_cast<u32x4_t*>(xs)[i] = load16(a.X + i * 8);
     }
     __syncthreads();
     if (!live) return;
 
-    auto compute = [&](int t, const Chunk<SRC>* cur) {
-        const uint32_t k0 = uint32_t(t % iters) * kSlab;
+    auto compute = [&](Item it, const Chunk<SRC>* cur) {
+        const uint32_t k0 = uint32_t(it.s) * kSlab;
         const uint32_t ka = k0 + half_off<SRC>(lane, 0), kb = k0 + half_off<SRC>(lane, 1);
         const bool oka = EXACT || ka < Cu, okb = EXACT || kb < Cu;
         // activations of this slab, shared by all rows
@@ -278,9 +287,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
     };
 
     // a group's rows are complete after its last slab: reduce and store
-    auto finish = [&](int t) {
-        if ((t + 1) % iters != 0) return;
-        const int g = t / iters;
+    auto finish = [&](Item it) {
+        if (it.s != iters - 1) return;
+        const int g = it.g;
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
 #pragma unroll
@@ -295,17 +304,28 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
         }
     };
 
-    // ping-pong over two register sets: the loads of item t+1 are in flight
-    // while item t is computed; the last item is re-issued (an L2 hit) so the
-    // body has no conditional load
-    for (int t = 0; t < total; t += 2) {
-        issue(min(t + 1, total - 1), nxt);
-        compute(t, cur);
-        finish(t);
-        if (t + 1 >= total) break;
-        issue(min(t + 2, total - 1), cur);
-        compute(t + 1, nxt);
-        finish(t + 1);
+    // ping-pong over two register sets: the loads of item t+1 are issued
+    // before item t is computed.  Past the end the last item is re-issued (an
+    // L2 hit) so the body has no conditional load; the body holds both halves
+    // with no exit between them (an odd last item is computed after the
+    // loop): a mid-body exit lets the compiler fold the two identical halves
+    // into one with register copies, which must wait for every load in flight.
+    int t = 0;
+    Item i0 = it0;
+    for (; t + 1 < total; t += 2) {
+        const Item i1 = next(i0);
+        const Item i2 = t + 2 < total ? next(i1) : i1;
+        issue(i1, set1);
+        compute(i0, set0);
+        finish(i0);
+        issue(i2, set0);
+        compute(i1, set1);
+        finish(i1);
+        i0 = i2;
+    }
+    if (t < total) {
+        compute(i0, set0);
+        finish(i0);
     }
 }
 
@@ -328,8 +348,8 @@ void launch_cfg(const MatArgs& a0, hipStream_t s) {
     static const int ng_env = env_int("UW_GEMV_NG", 0);
     MatArgs a = a0;
     // measured on MI355X at batch 1: short rows (4096) run best as one row per
-    // group and two groups per wave, long rows (14336) as two rows, one group
-    int ng = ng_env > 0 ? ng_env : (NRW == 1 ? 2 : 1);
+    // group and two groups per wave, long rows (14336) as one row, one group
+    int ng = ng_env > 0 ? ng_env : (NRW == 1 && a.C < 8192 ? 2 : 1);
     while (ng > 1 && int64_t(ng) * NRW * a.C > 60 * 4096) --ng;
     a.row_groups = ng;
     const int64_t waves = (a.R + int64_t(NRW) * ng - 1) / (int64_t(NRW) * ng);
@@ -348,13 +368,14 @@ void launch_x(const MatArgs& a, hipStream_t s) {
     else launch_cfg<SRC, MB, NRW, false>(a, s);
 }
 
-// Rows per group: 2 for long rows (activations reused twice), 1 for short
-// rows; the verbatim tables of a wave's rows must fit one per lane: NRW*C <=
-// 60 tiles of 4096.
+// Rows per group: one (measured best on both Llama shapes at batch 1; two
+// reuse each activation fragment twice and are kept for tuning); the
+// verbatim tables of a wave's rows must fit one per lane: NRW*C <= 60 tiles
+// of 4096.
 template <int SRC, int MB>
 void launch_mb(const MatArgs& a, hipStream_t s) {
     static const int nrw_env = env_int("UW_GEMV_NRW", 0);
-    int nrw = nrw_env ? nrw_env : (a.C >= 8192 ? 2 : 1);
+    int nrw = nrw_env ? nrw_env : 1;
     while (nrw > 1 && nrw * a.C > 60 * 4096) nrw >>= 1;
     switch (nrw) {
         case 2: launch_x<SRC, MB, 2>(a, s); break;

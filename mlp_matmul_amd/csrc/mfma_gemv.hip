@@ -36,9 +36,7 @@ namespace {
 constexpr int kKStep = 128;   // columns per wave per step
 constexpr int kMaxSlice = 4096;  // columns of one wave's K-slice: its row segment spans <= 2 tiles
 
-__device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) {
-    return (a.pal[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-}
+__device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) { return pal_byte(a.pal, uint32_t(i)); }
 
 template <int SRC, int NB, int RB>
 struct Step {
@@ -144,6 +142,9 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
         for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
             for (int n = 0; n < NB; ++n) st.x[sub][n] = load16(a.X + xrow[n] * C + k + 8 * sub);
+        // keep every load of the step here: the scheduler must not sink one
+        // into a later rebuild, whose wait would then cover it
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     f32x4_t acc[RB][NB];
@@ -201,35 +202,38 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
     };
 
     __syncthreads();                                      // LUT ready
+    // Steps past the slice re-issue its last step, so no load is conditional.
+    // Each loop body holds all its steps with no exit between them (the 0..PD
+    // steps left over are computed after the loop): a mid-body exit lets the
+    // compiler fold identical step bodies into one with register copies,
+    // which must wait for every load in flight.
     if (s_lo < s_hi) {
-        // Steps past the slice re-issue its last step, so no load is conditional.
         const uint32_t last = s_hi - 1;
+        uint32_t s = s_lo;
         if (PD == 1) {
             Step<SRC, NB, RB> s0, s1;
             issue(s_lo, s0);
-            for (uint32_t s = s_lo;; s += 2) {
-                issue(min(s + 1, last), s1);
+            for (; s + 1 < s_hi; s += 2) {
+                issue(s + 1, s1);
                 compute(s0);
-                if (s + 1 >= s_hi) break;
                 issue(min(s + 2, last), s0);
                 compute(s1);
-                if (s + 2 >= s_hi) break;
             }
+            if (s < s_hi) compute(s0);
         } else {
             Step<SRC, NB, RB> s0, s1, s2;
             issue(s_lo, s0);
             issue(min(s_lo + 1, last), s1);
-            for (uint32_t s = s_lo;; s += 3) {
-                issue(min(s + 2, last), s2);
+            for (; s + 2 < s_hi; s += 3) {
+                issue(s + 2, s2);
                 compute(s0);
-                if (s + 1 >= s_hi) break;
                 issue(min(s + 3, last), s0);
                 compute(s1);
-                if (s + 2 >= s_hi) break;
                 issue(min(s + 4, last), s1);
                 compute(s2);
-                if (s + 3 >= s_hi) break;
             }
+            if (s < s_hi) compute(s0);
+            if (s + 1 < s_hi) compute(s1);
         }
     }
     // sum the K-slices: D layout, lane l holds batch column l%16, rows 4*(l/16)..+3
