@@ -83,6 +83,13 @@ class Layer:
             del w, blob
 
 
+def gate_up_bytes(info_g, info_u, batch):
+    """Algorithmic bytes of the fused gate/up launch: both matrices' 4-bit
+    forms, the activations once, the bf16 SiLU product out."""
+    return (palette_bytes(info_g, batch) + palette_bytes(info_u, batch) - 2 * batch * info_g.cols
+            - 8 * batch * info_g.rows + 2 * batch * info_g.rows)
+
+
 def palette_bytes(info, batch):
     """Algorithmic bytes one direct-palette matmul launch must move: the 4-bit
     form (sign/mantissa plane, nibbles, verbatim exponents, bitmap, verbatim
@@ -99,7 +106,7 @@ class Step:
     that the host issues a step in a few microseconds and the GPU queue stays
     ahead of it (the timed region measures the GPU, not Python)."""
 
-    def __init__(self, layers, batch, pipeline, stream=None, workload=2, bf16_choice=None):
+    def __init__(self, layers, batch, pipeline, stream=None, workload=2, bf16_choice=None, fuse=True):
         import ctypes as ct
         import functools
         import torch
@@ -142,8 +149,17 @@ class Step:
                     row.append(functools.partial(L.uw_matmul, ct.byref(lay.mats[m].dmat), pipe, 0, 1, xin,
                                                  batch, yout, scr, nsc, st))
             silu = functools.partial(L.uw_silu_mul_bf16, P(self.g), P(self.u), batch * F, P(self.h), st)
-            self.calls.append([row[0], row[1], silu, row[2]])
-            self.bytes.append([palette_bytes(lay.info[m], batch) for m in range(3)])
+            self.fused = (fuse and pipe == uw.UW_PIPE_DIRECT and batch <= 4 and batch * H * 2 <= 32768)
+            if self.fused:
+                # gate, up and the SiLU product in one launch (h only)
+                gu = functools.partial(L.uw_mlp_gate_up, ct.byref(lay.mats[0].dmat), ct.byref(lay.mats[1].dmat),
+                                       X, batch, P(self.h), None, None, st)
+                self.calls.append([gu, row[2]])
+                self.bytes.append([gate_up_bytes(lay.info[0], lay.info[1], batch),
+                                   palette_bytes(lay.info[2], batch)])
+            else:
+                self.calls.append([row[0], row[1], silu, row[2]])
+                self.bytes.append([palette_bytes(lay.info[m], batch) for m in range(3)])
 
     def run(self, i):
         for f in self.calls[i % len(self.layers)]:
@@ -192,15 +208,18 @@ class GraphStep:
             with torch.cuda.stream(st.stream):
                 st.run(li)
             torch.cuda.synchronize()
-            ref = (st.g.clone(), st.u.clone(), st.h.clone(), st.y.clone())
+            outs = (st.h, st.y) if st.fused else (st.g, st.u, st.h, st.y)   # what the step writes
+            ref = tuple(t.clone() for t in outs)
             for _ in range(3):
-                for t in (st.g, st.u, st.y):
-                    t.fill_(float("nan"))
-                st.h.zero_()
+                for t in outs:
+                    if t.dtype == torch.bfloat16:
+                        t.zero_()
+                    else:
+                        t.fill_(float("nan"))
                 torch.cuda.synchronize()
                 g.replay()
                 torch.cuda.synchronize()
-                for a_, b_ in zip(ref, (st.g, st.u, st.h, st.y)):
+                for a_, b_ in zip(ref, outs):
                     if not torch.equal(a_.view(torch.int16) if a_.dtype == torch.bfloat16 else a_.view(torch.int32),
                                        b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_.view(torch.int32)):
                         return False
@@ -574,8 +593,8 @@ def main():
     weights_bf16_bytes = 3 * 2 * F * H
     stream = torch.cuda.Stream()
 
-    def measure(pipeline):
-        st = Step(layers, B, pipeline, stream=stream)
+    def measure(pipeline, fuse=True):
+        st = Step(layers, B, pipeline, stream=stream, fuse=fuse)
         eager = time_steps(st, a.steps, a.warmup)
         graph, ok = None, None
         if not a.no_graph:
@@ -585,21 +604,33 @@ def main():
         return st, eager, graph, ok
 
     step, eager, graph, graph_ok = measure(a.pipeline)
-    # dominant kernel: the library's kernel timer records HIP events at the
-    # start and end of every matmul launch (on its stream) over a second pass
-    # of the same eager steps
-    with uw.KernelTimer(capacity=3 * a.steps + 8) as kt:
+    # the library's kernel timer records HIP events at the start and end of
+    # every matmul launch (on its stream) over a second pass of the same eager
+    # steps; launches come in step order (fused gate/up + down, or gate, up,
+    # down), so each position of the step is one kernel
+    nl = len(step.bytes[0])
+    with uw.KernelTimer(capacity=nl * a.steps + 8) as kt:
         time_steps(step, a.steps, 0)
-    durs = np.array(kt.ms, dtype=np.float64) / 1e3
-    bytes_ = np.array([step.bytes[i % len(layers)][m] for i in range(a.steps) for m in range(3)],
-                      dtype=np.float64)[:durs.size]
-    achieved = bytes_.sum() / durs.sum() / 1e9
+    durs = np.array(kt.ms, dtype=np.float64)[: nl * a.steps].reshape(a.steps, nl) / 1e3
+    bytes_ = np.array([step.bytes[i % len(layers)] for i in range(a.steps)], dtype=np.float64)
+    per_kernel = [{"bytes": float(bytes_[:, m].mean()), "avg_s": float(durs[:, m].mean()),
+                   "total_s": float(durs[:, m].sum())} for m in range(nl)]
+    dom = max(range(nl), key=lambda m: per_kernel[m]["total_s"])
+    achieved = per_kernel[dom]["bytes"] / per_kernel[dom]["avg_s"] / 1e9
+    achieved_all = bytes_.sum() / durs.sum() / 1e9
+    kernel_names = (["fused gate/up GEMV + SiLU (palette source)", "down GEMV (palette source)"] if step.fused else
+                    [f"{n} recon matmul ({'gemv' if B < 16 else 'mfma'})" for n in ("gate", "up", "down")])
     # the step time is the faster of the two valid timings
     use_graph = graph is not None and graph_ok and graph < eager
     sec = graph if use_graph else eager
-    compressed_step_bytes = sum(palette_bytes(layers[0].info[m], B) for m in range(3))
+    compressed_step_bytes = sum(step.bytes[0])
     log(f"{a.pipeline}: eager {eager * 1e3:.4f} ms/step, graph {graph and graph * 1e3}, graph==eager {graph_ok}, "
-        f"dominant kernel {durs.mean() * 1e6:.2f} us avg")
+        f"kernels " + ", ".join(f"{kernel_names[m]} {per_kernel[m]['avg_s'] * 1e6:.2f} us" for m in range(nl)))
+    unfused = None
+    if step.fused and not a.no_compare:
+        _, ue, ug, uok = measure(a.pipeline, fuse=False)
+        unfused = {"eager_ms": round(ue * 1e3, 5), "graph_ms": ug and round(ug * 1e3, 5), "graph_matches_eager": uok}
+        log(f"unfused step: {unfused}")
 
     extra = {}
     if not a.no_compare:
@@ -612,7 +643,7 @@ def main():
                            "graph_matches_eager": ok_}
         log(f"ms/step by pipeline: {extra}")
 
-    tag = f"gemv_recon_pal_llama_mlp_b{B}"
+    tag = f"gemv_gateup_pal_llama_mlp_b{B}" if step.fused else f"gemv_recon_pal_llama_mlp_b{B}"
     traffic = traffic_from_profiles(tag) if B < 16 and a.pipeline == "direct" else None
     out = {
         "metric": METRIC,
@@ -632,15 +663,23 @@ def main():
         "data": "synthetic",
         "config": {"workload": "llama3.1-8b-mlp-layer", "batch": B, "pipeline": a.pipeline,
                    "gate_up": [F, H], "down": [H, F], "layer_copies_rotated": a.layers,
+                   "step": ("fused gate/up + SiLU launch, down launch" if step.fused else
+                            "gate, up, SiLU product, down launches"),
                    "weights": "N(0,0.02)+0.05% N(0,0.5), seeded"},
         "compressed_GBps": round(compressed_step_bytes / sec / 1e9, 2),
         "compressed_hbm_frac": round(compressed_step_bytes / sec / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": f"recon matmul ({'gemv' if B < 16 else 'mfma'}, palette source)",
-                     "launches": int(durs.size), "avg_launch_us": round(float(durs.mean()) * 1e6, 3),
-                     "algorithmic_bytes_per_launch": round(float(bytes_.mean()))},
+                     "kernel": kernel_names[dom],
+                     "launches": int(a.steps), "avg_launch_us": round(per_kernel[dom]["avg_s"] * 1e6, 3),
+                     "algorithmic_bytes_per_launch": round(per_kernel[dom]["bytes"]),
+                     "all_matmul_launches": {"achieved": round(achieved_all, 2),
+                                             "frac": round(achieved_all / HBM_PEAK_GBPS, 4),
+                                             "per_kernel_avg_us": {kernel_names[m]: round(per_kernel[m]["avg_s"] * 1e6, 3)
+                                                                   for m in range(nl)}}},
     }
+    if unfused:
+        out["ms_per_step_unfused"] = unfused
     if extra:
         out["ms_per_step_by_pipeline"] = extra
         b16 = min(v for v in (extra["bf16"]["graph_ms"], extra["bf16"]["eager_ms"]) if v)

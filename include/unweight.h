@@ -263,6 +263,22 @@ int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k,
  * projections of a SwiGLU MLP. */
 int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, void* stream);
 
+/* Fused gate/up projections of a SwiGLU MLP block on the direct-palette
+ * form ("How the reconstructive matmul works": both compressed matrices are
+ * rebuilt on chip inside one GEMV launch; the gate, up and down matrices are
+ * the ones "How to compress model weights effectively" compresses):
+ *   g = X . gate^T,  u = X . up^T  (fp32 accumulation, as uw_matmul with
+ *   UW_PIPE_DIRECT and the GEMV kernel), h[b][r] = bf16_rne(SiLU(g) * u)
+ * with the same SiLU arithmetic as uw_silu_mul_bf16, so h, g and u are
+ * bit-identical to the unfused three calls.
+ * gate, up: same shape [rows, cols], both with a NIB section; X bf16 bits
+ * [batch, cols]; h bf16 bits [batch, rows]; g_out, u_out fp32 [batch, rows]
+ * or NULL (not written).  Device pointers, 16-byte aligned, caller-owned.
+ * UW_EINVAL on NULL/misaligned pointers or mismatched shapes;
+ * UW_EUNSUPPORTED unless 1 <= batch <= 4 and batch*cols*2 <= 32768. */
+int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, int64_t batch,
+                   uint16_t* h, float* g_out, float* u_out, void* stream);
+
 /* ----------------------------------------------------------- kernel timer */
 /* Per-launch durations of the matmul kernels (GEMV and MFMA), for measuring
  * them on their own stream.  While enabled, each matmul kernel launch takes

@@ -242,6 +242,19 @@ def matmul(dm: DeviceMatrix, X, pipeline=UW_PIPE_AUTO, kernel=UW_KERNEL_AUTO, sp
     return Y
 
 
+def mlp_gate_up(gate: DeviceMatrix, up: DeviceMatrix, X, h=None, g=None, u=None, stream=None):
+    """h = bf16(SiLU(X.gate^T) * (X.up^T)) in one fused launch (direct-palette
+    form, batch 1..4); g and u (fp32) are also written when given."""
+    torch = _torch()
+    batch = X.shape[0]
+    if h is None:
+        h = torch.empty((batch, gate.rows), dtype=torch.bfloat16, device="cuda")
+    check(lib().uw_mlp_gate_up(ct.byref(gate.dmat), ct.byref(up.dmat), _ptr(X), batch, _ptr(h),
+                               _ptr(g) if g is not None else None, _ptr(u) if u is not None else None,
+                               _stream(stream)), "uw_mlp_gate_up")
+    return h
+
+
 def silu_mul_bf16(g, u, h=None, stream=None):
     torch = _torch()
     if h is None:

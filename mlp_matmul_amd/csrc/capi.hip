@@ -287,6 +287,29 @@ int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k, const uin
     }
 }
 
+int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, int64_t batch, uint16_t* h,
+                   float* g_out, float* u_out, void* stream) {
+    uw::clear_error();
+    const char* who = "uw_mlp_gate_up";
+    if (!gate || !up) return uw::fail(UW_EINVAL, std::string(who) + ": NULL matrix");
+    if (gate->rows != up->rows || gate->cols != up->cols || gate->rows < 0 || gate->cols % uw::kGroup)
+        return uw::fail(UW_EINVAL, std::string(who) + ": gate and up must have the same shape (cols % 64 == 0)");
+    if (batch < 0) return uw::fail(UW_EINVAL, std::string(who) + ": negative batch");
+    if (gate->rows == 0 || batch == 0) return UW_OK;
+    if (batch > 4 || batch * gate->cols * 2 > 32768 || gate->cols > 60 * 4096 ||
+        gate->rows * gate->cols >= (int64_t(1) << 31))
+        return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": needs 1 <= batch <= 4 and batch*cols*2 <= 32768");
+    if (!X || !h || !aligned16(X) || !aligned16(h) || (g_out && !aligned16(g_out)) || (u_out && !aligned16(u_out)))
+        return uw::fail(UW_EINVAL, std::string(who) + ": NULL or misaligned device pointer");
+    for (const uw_dmat* d : {gate, up})
+        if (!d->nib || !d->sm || !d->bitmap || !d->tile_vbase || !aligned16(d->nib) || !aligned16(d->sm))
+            return uw::fail(UW_EINVAL, std::string(who) + ": a matrix lacks its NIB/SM/BITMAP/TILE_VBASE sections");
+    uwk::MatArgs g = compressed_args(gate, gate->nib, X, batch, g_out);
+    uwk::MatArgs u = compressed_args(up, up->nib, X, batch, u_out);
+    hipError_t e = uwk::launch_gemv_gateup(g, u, h, as_stream(stream));
+    return e == hipSuccess ? UW_OK : hip_fail(e, who);
+}
+
 int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, void* stream) {
     uw::clear_error();
     if (n < 0) return uw::fail(UW_EINVAL, "uw_silu_mul_bf16: negative n");

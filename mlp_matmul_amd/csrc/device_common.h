@@ -86,6 +86,16 @@ __device__ __forceinline__ void store16(void* p, u32x4_t v) {
 
 // Index of a verbatim group among all verbatim groups: the count before its
 // tile plus the flagged groups before it inside the tile's bitmap word.
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// SiLU(g) * u in fp32 (HIP's expf): the SwiGLU step between gate/up and down.
+__device__ __forceinline__ float silu_mul1(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
 // Palette byte i (0..15) of the four packed palette words, selected without
 // indexing: the words stay in scalar registers and no memory is read.
 __device__ __forceinline__ uint32_t pal_byte(const uint32_t (&pal)[4], uint32_t i) {

@@ -54,17 +54,23 @@ __device__ __forceinline__ uint32_t half_off(int lane, int h) {
     return SRC == SRC_BF16 ? uint32_t(h * 512 + lane * 8) : uint32_t(lane * 16 + h * 8);
 }
 
-template <int SRC>
+template <int SRC, int MB>
 struct Chunk {
     u32x4_t d0, d1;   // BF16: the two weight halves; EXP: d0 = 16 exponents; PAL: d0.xy = 16 nibbles
     u32x4_t sm;       // EXP, PAL: sign/mantissa bytes
     u32x4_t vx;       // PAL: verbatim exponents (meaningful when verb)
     uint32_t verb;    // PAL: 1 when the lane's 64-element group is verbatim
+    u32x4_t xa[MB], xb[MB];   // activations read from L2 (row 0's chunk only)
 };
 
-template <int SRC, int MB, int NRW, bool EXACT, bool XLDS>
-__global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
-    __shared__ uint32_t lut[256];                                // nibble pair -> exponents in place
+// DUAL (palette source, one row per wave): the gate/up pair of a SwiGLU MLP.
+// The wave's two row groups are row r of the gate matrix (a) and row r of
+// the up matrix (up), over the same staged activations; the second group's
+// epilogue writes h[b][r] = bf16(SiLU(g) * u), and g and u themselves when
+// a.Y / up.Y are not null.
+template <int SRC, int MB, int NRW, bool EXACT, bool XLDS, bool DUAL>
+__global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16_t* H) {
+    __shared__ uint32_t lut[DUAL ? 512 : 256];                   // nibble pair -> exponents in place
     extern __shared__ uint32_t lds[];
     uint16_t* xs = reinterpret_cast<uint16_t*>(lds);             // [B][C] when XLDS
     const int tid = threadIdx.x;
@@ -72,13 +78,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
     const uint32_t Cu = uint32_t(C);
     const int B = int(a.B);
     if (SRC == SRC_PAL) lut[tid] = (palb(a, tid & 15) << 7) | (palb(a, tid >> 4) << 23);
+    if (DUAL) lut[256 + tid] = (palb(up, tid & 15) << 7) | (palb(up, tid >> 4) << 23);
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int NG = a.row_groups;                                 // row groups per wave
+    const int NG = DUAL ? 1 : a.row_groups;                      // row groups per wave
     const int64_t r0 = (int64_t(blockIdx.x) * 4 + wave) * NRW * NG;
     const bool live = r0 < a.R;                                  // wave has rows (uniform)
     const int wrows = live ? int(min(int64_t(NRW) * NG, a.R - r0)) : 0;
-    const int ngroups = (wrows + NRW - 1) / NRW;
+    const int ngroups = DUAL ? (live ? 2 : 0) : (wrows + NRW - 1) / NRW;
     const int iters = int((C + kSlab - 1) / kSlab);
     const int total = ngroups * iters;                           // items: (group, slab)
     // a wave past the matrix issues its loads from row 0 (so every wave runs
@@ -87,8 +94,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
 
     // the verbatim tables of every tile the wave's rows touch, one per lane
     const int64_t t_first = (rl0 * C) >> 12;
-    uint64_t my_word = 0;
-    uint32_t my_vbase = 0;
+    uint64_t my_word = 0, my_word1 = 0;                          // my_word1, my_vbase1: DUAL's up matrix
+    uint32_t my_vbase = 0, my_vbase1 = 0;
     // a lane's group inside a 1024-weight slab, and the mask of the groups below it
     const uint32_t lane_grp = uint32_t(lane) >> 2;
     const uint32_t lane_below = (1u << lane_grp) - 1u;
@@ -96,12 +103,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
     const uint8_t* vb_ptr = a.vexp ? a.vexp : a.sm;
     const uint16_t* wb = static_cast<const uint16_t*>(a.w);
     const uint8_t* w8 = static_cast<const uint8_t*>(a.w);
+    const uint8_t* vb_ptr1 = DUAL ? (up.vexp ? up.vexp : up.sm) : nullptr;
+    // per-group planes (DUAL: group 1 reads the up matrix; the selects are uniform)
+    auto w8_of = [&](int g) { return DUAL && g ? static_cast<const uint8_t*>(up.w) : w8; };
+    auto sm_of = [&](int g) { return DUAL && g ? up.sm : a.sm; };
 
     float acc[NRW][MB];
 #pragma unroll
     for (int r = 0; r < NRW; ++r)
 #pragma unroll
         for (int b = 0; b < MB; ++b) acc[r][b] = 0.f;
+    float gate_sum[MB];                                          // DUAL: the gate rows' results
+#pragma unroll
+    for (int b = 0; b < MB; ++b) gate_sum[b] = 0.f;
 
     // rows past the matrix (beyond wrows) re-read the wave's first row; their
     // sums are never stored.  issue_w: the weight planes (no dependency);
@@ -111,15 +125,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
         int g, s;
     };
     auto row_of = [&](Item it, int r) -> uint32_t {
-        const int rr = it.g * NRW + r;                           // row inside the wave's range
+        const int rr = DUAL ? r : it.g * NRW + r;                // row inside the wave's range
         return uint32_t(rl0) + uint32_t(rr < wrows ? rr : 0);
     };
-    auto issue_w = [&](Item it, Chunk<SRC>* ch) {
+    auto issue_w = [&](Item it, Chunk<SRC, MB>* ch) {
         const uint32_t k0 = uint32_t(it.s) * kSlab;
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
             const uint32_t row = row_of(it, r);
-            Chunk<SRC>& c = ch[r];
+            Chunk<SRC, MB>& c = ch[r];
             uint32_t k = k0 + half_off<SRC>(lane, 0);
             if (!EXACT && k >= Cu) k = 0;
             const uint32_t pos = row * Cu + k;
@@ -132,19 +146,23 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
                 c.d0 = load_stream16(w8 + pos);
                 c.sm = load_stream16(a.sm + pos);
             } else {
-                const u32x2_t n = load_stream8(w8 + pos / 2);
+                const u32x2_t n = load_stream8(w8_of(it.g) + pos / 2);
                 c.d0 = u32x4_t{n[0], n[1], 0u, 0u};
-                c.sm = load_stream16(a.sm + pos);
+                c.sm = load_stream16(sm_of(it.g) + pos);
             }
         }
     };
-    auto issue_v = [&](Item it, Chunk<SRC>* ch) {
+    auto issue_v = [&](Item it, Chunk<SRC, MB>* ch) {
         if (SRC != SRC_PAL) return;
         const uint32_t k0 = uint32_t(it.s) * kSlab;
+        const bool g1 = DUAL && it.g;                            // the up matrix's tables
+        const uint64_t mw = g1 ? my_word1 : my_word;
+        const uint32_t mv = g1 ? my_vbase1 : my_vbase;
+        const uint8_t* vbp = g1 ? vb_ptr1 : vb_ptr;
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
             const uint32_t row = row_of(it, r);
-            Chunk<SRC>& c = ch[r];
+            Chunk<SRC, MB>& c = ch[r];
             uint32_t k = k0 + half_off<SRC>(lane, 0);
             if (!EXACT && k >= Cu) k = 0;
             const uint32_t pos = row * Cu + k;
@@ -155,13 +173,13 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
                 const uint32_t sp = row * Cu + k0;
                 const int tl = int((sp >> 12) - uint32_t(t_first));
                 const uint64_t word =
-                    (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(my_word >> 32), tl))) << 32) |
-                    uint32_t(__builtin_amdgcn_readlane(int(uint32_t(my_word)), tl));
+                    (uint64_t(uint32_t(__builtin_amdgcn_readlane(int(mw >> 32), tl))) << 32) |
+                    uint32_t(__builtin_amdgcn_readlane(int(uint32_t(mw)), tl));
                 const uint32_t gb = (sp >> 6) & 63u;
                 const uint32_t m16 = uint32_t(word >> gb) & 0xFFFFu;
                 c.verb = (m16 >> lane_grp) & 1u;
                 if (m16) {                                           // rare: a verbatim group in this slab
-                    const uint32_t vbase = uint32_t(__builtin_amdgcn_readlane(int(my_vbase), tl));
+                    const uint32_t vbase = uint32_t(__builtin_amdgcn_readlane(int(mv), tl));
                     const uint64_t below = gb ? (word & ((~0ull) >> (64 - gb))) : 0ull;
                     const uint32_t slab_slot = vbase + uint32_t(__popcll(below));
                     const uint32_t slot = slab_slot + uint32_t(__popc(m16 & lane_below));
@@ -169,9 +187,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
                 }
             } else {
                 const int tl = int((pos >> 12) - uint32_t(t_first));
-                const uint64_t word = (uint64_t(uint32_t(__shfl(int(my_word >> 32), tl))) << 32) |
-                                      uint32_t(__shfl(int(uint32_t(my_word)), tl));
-                const uint32_t vbase = uint32_t(__shfl(int(my_vbase), tl));
+                const uint64_t word = (uint64_t(uint32_t(__shfl(int(mw >> 32), tl))) << 32) |
+                                      uint32_t(__shfl(int(uint32_t(mw)), tl));
+                const uint32_t vbase = uint32_t(__shfl(int(mv), tl));
                 const uint32_t bit = (pos >> 6) & 63u;
                 c.verb = uint32_t(word >> bit) & 1u;
                 if (__builtin_amdgcn_ballot_w64(c.verb != 0)) {
@@ -179,28 +197,52 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
                     voff = c.verb ? slot * 64u + (pos & 63u) : 0u;
                 }
             }
-            c.vx = load16(vb_ptr + voff);
+            c.vx = load16(vbp + voff);
         }
     };
-    auto issue = [&](Item it, Chunk<SRC>* ch) {
+    // activations from L2 (when not staged in LDS) go out with the item, ahead
+    // of its weights; batch rows past B re-read row B-1 so no load is
+    // conditional
+    auto issue_x = [&](Item it, Chunk<SRC, MB>* ch) {
+        if (XLDS) return;
+        const uint32_t k0 = uint32_t(it.s) * kSlab;
+        uint32_t ka = k0 + half_off<SRC>(lane, 0), kb = k0 + half_off<SRC>(lane, 1);
+        if (!EXACT) {
+            if (ka >= Cu) ka = 0;
+            if (kb >= Cu) kb = 0;
+        }
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+            const uint32_t bb = uint32_t(b < B ? b : B - 1);
+            ch[0].xa[b] = load16(a.X + bb * Cu + ka);
+            ch[0].xb[b] = load16(a.X + bb * Cu + kb);
+        }
+    };
+    auto issue = [&](Item it, Chunk<SRC, MB>* ch) {
+        issue_x(it, ch);
         issue_w(it, ch);
         issue_v(it, ch);
     };
 
     auto next = [&](Item it) { return it.s + 1 == iters ? Item{it.g + 1, 0} : Item{it.g, it.s + 1}; };
-    Chunk<SRC> set0[NRW], set1[NRW];
+    Chunk<SRC, MB> set0[NRW], set1[NRW];
     const Item it0{0, 0};
     // item 0's weight loads go out first; the verbatim tables of every tile
     // the wave's rows touch (one per lane) follow, then item 0's verbatim
     // loads, then the activations are staged.  (Issuing item 1 here as well,
     // ahead of the staging, measured slower.)
     if (live) {
+        issue_x(it0, set0);
         issue_w(it0, set0);
         if (SRC == SRC_PAL) {
             const int64_t t_end = max(((rl0 + wrows) * C + 4095) >> 12, t_first + 1);
             const int64_t tl = min(t_first + lane, t_end - 1);
             my_word = a.bitmap[tl];
             my_vbase = a.tile_vbase[tl];
+            if (DUAL) {
+                my_word1 = up.bitmap[tl];
+                my_vbase1 = up.tile_vbase[tl];
+            }
         }
         issue_v(it0, set0);
     }
@@ -212,7 +254,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
     __syncthreads();
     if (!live) return;
 
-    auto compute = [&](Item it, const Chunk<SRC>* cur) {
+    auto compute = [&](Item it, const Chunk<SRC, MB>* cur) {
+        const uint32_t lut_off = DUAL && it.g ? 1024u : 0u;      // DUAL: the up matrix's table
         const uint32_t k0 = uint32_t(it.s) * kSlab;
         const uint32_t ka = k0 + half_off<SRC>(lane, 0), kb = k0 + half_off<SRC>(lane, 1);
         const bool oka = EXACT || ka < Cu, okb = EXACT || kb < Cu;
@@ -226,14 +269,14 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
                     xa[b] = *reinterpret_cast<const u32x4_t*>(xs + b * Cu + kka);
                     xb[b] = *reinterpret_cast<const u32x4_t*>(xs + b * Cu + kkb);
                 } else {
-                    xa[b] = load16(a.X + b * Cu + kka);
-                    xb[b] = load16(a.X + b * Cu + kkb);
+                    xa[b] = cur[0].xa[b];
+                    xb[b] = cur[0].xb[b];
                 }
             }
         }
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
-            const Chunk<SRC>& c = cur[r];
+            const Chunk<SRC, MB>& c = cur[r];
             uint32_t w[8];
             if (SRC == SRC_BF16) {
 #pragma unroll
@@ -251,7 +294,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
 #pragma unroll
                 for (int p = 0; p < 8; ++p) {
                     const uint32_t off = ((c.d0[p >> 2] >> (8 * (p & 3))) & 0xFFu) << 2;
-                    e7[p] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + off);
+                    e7[p] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + lut_off + off);
                 }
                 if (__builtin_amdgcn_ballot_w64(c.verb != 0)) {    // rare: raw exponents for verbatim lanes
 #pragma unroll
@@ -290,6 +333,24 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a) {
     auto finish = [&](Item it) {
         if (it.s != iters - 1) return;
         const int g = it.g;
+        if (DUAL) {
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+                if (b < B) {
+                    const float v = wave_sum(acc[0][b]);
+                    const int64_t o = int64_t(b) * a.R + r0;
+                    if (g == 0) {
+                        gate_sum[b] = v;
+                        if (lane == 0 && a.Y) a.Y[o] = v;
+                    } else if (lane == 0) {
+                        if (up.Y) up.Y[o] = v;
+                        H[o] = uint16_t(f32_to_bf16_rne(silu_mul1(gate_sum[b], v)));
+                    }
+                }
+                acc[0][b] = 0.f;
+            }
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
 #pragma unroll
@@ -356,9 +417,11 @@ void launch_cfg(const MatArgs& a0, hipStream_t s) {
     const unsigned grid = unsigned((waves + 3) / 4);
     const size_t lds = XLDS ? size_t(a.B * a.C * 2) : 0;
     if (a.C % kSlab == 0)
-        launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS>, dim3(grid), dim3(256), lds, s, a);
+        launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS, false>, dim3(grid), dim3(256), lds, s, a, MatArgs{},
+                     static_cast<uint16_t*>(nullptr));
     else
-        launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS>, dim3(grid), dim3(256), lds, s, a);
+        launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS, false>, dim3(grid), dim3(256), lds, s, a, MatArgs{},
+                     static_cast<uint16_t*>(nullptr));
 }
 
 template <int SRC, int MB, int NRW>
@@ -393,7 +456,34 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Gate/up pair: one row of each matrix per wave, activations staged in LDS.
+template <int MB>
+void launch_gateup_mb(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
+    MatArgs a = g;
+    a.row_groups = 1;
+    const unsigned grid = unsigned((a.R + 3) / 4);
+    const size_t lds = size_t(a.B * a.C * 2);
+    if (a.C % kSlab == 0)
+        launch_timed(gemv_kernel<SRC_PAL, MB, 1, true, true, true>, dim3(grid), dim3(256), lds, s, a, u, h);
+    else
+        launch_timed(gemv_kernel<SRC_PAL, MB, 1, false, true, true>, dim3(grid), dim3(256), lds, s, a, u, h);
+}
+
 }  // namespace
+
+bool gemv_gateup_supported(const MatArgs& g, const MatArgs& u) {
+    return g.R == u.R && g.C == u.C && g.B == u.B && g.B >= 1 && g.B <= 4 && g.C > 0 &&
+           g.B * g.C * 2 <= kXLdsMax && g.C <= 60 * 4096;
+}
+
+hipError_t launch_gemv_gateup(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
+    if (g.R == 0) return hipSuccess;
+    if (!gemv_gateup_supported(g, u)) return hipErrorNotSupported;
+    if (g.B <= 1) launch_gateup_mb<1>(g, u, h, s);
+    else if (g.B <= 2) launch_gateup_mb<2>(g, u, h, s);
+    else launch_gateup_mb<4>(g, u, h, s);
+    return hipGetLastError();
+}
 
 hipError_t launch_gemv(int src, const MatArgs& a, hipStream_t s) {
     if (a.R == 0 || a.B == 0) return hipSuccess;

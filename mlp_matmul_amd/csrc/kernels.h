@@ -45,6 +45,9 @@ struct MatArgs {
 
 hipError_t launch_decode(int mode, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gemv(int src, const MatArgs& a, hipStream_t s);
+// Fused gate/up GEMV with the SiLU product (palette sources, batch 1..4).
+bool gemv_gateup_supported(const MatArgs& gate, const MatArgs& up);
+hipError_t launch_gemv_gateup(const MatArgs& gate, const MatArgs& up, uint16_t* h, hipStream_t s);
 hipError_t launch_mfma(int src, const MatArgs& a, hipStream_t s);
 hipError_t launch_mfma_gemv(int src, const MatArgs& a, hipStream_t s);
 bool mfma_gemv_supported(const MatArgs& a);

@@ -9,14 +9,6 @@ namespace uwk {
 
 namespace {
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ float silu_mul1(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
 __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ g, const float* __restrict__ u,
                                                        int64_t n, uint16_t* __restrict__ h) {
     const int64_t i4 = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;

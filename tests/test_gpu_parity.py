@@ -386,6 +386,88 @@ def test_mlp_layer_chain(torch_cuda, B):
     assert_matmul_close(y.cpu().numpy(), wd, hb, what="down")
 
 
+# ----------------------------------------------------- fused gate/up + SiLU
+def _bf16_key(b):
+    b = b.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def _gate_up_case(wg, wu, x, rows=None, what=""):
+    """The fused launch against the unfused three calls (bit for bit) and
+    against the fp64 oracle (g, u within tolerance; h within one bf16 ulp of
+    bf16(SiLU(g)*u) on the GPU's g, u)."""
+    import torch
+    dg, du = uw.compress(wg).to_device(), uw.compress(wu).to_device()
+    X = to_dev_bf16(x)
+    B, R = x.shape[0], wg.shape[0]
+    g = torch.empty((B, R), dtype=torch.float32, device="cuda")
+    u = torch.empty_like(g)
+    h = uw.mlp_gate_up(dg, du, X, g=g, u=u)
+    h_only = uw.mlp_gate_up(dg, du, X)                       # no g/u outputs
+    g2 = uw.gemm_recon_pal(dg, None, X, kernel=uw.UW_KERNEL_GEMV)
+    u2 = uw.gemm_recon_pal(du, None, X, kernel=uw.UW_KERNEL_GEMV)
+    h2 = uw.silu_mul_bf16(g2, u2)
+    gn, un = g.cpu().numpy(), u.cpu().numpy()
+    assert np.array_equal(gn.view(np.uint32), g2.cpu().numpy().view(np.uint32)), what + " g"
+    assert np.array_equal(un.view(np.uint32), u2.cpu().numpy().view(np.uint32)), what + " u"
+    hb = from_dev_bits(h)
+    assert np.array_equal(hb, from_dev_bits(h2)), what + " h"
+    assert np.array_equal(hb, from_dev_bits(h_only)), what + " h without g/u"
+    if rows is None:
+        assert_matmul_close(gn, wg, x, what=what + " gate")
+        assert_matmul_close(un, wu, x, what=what + " up")
+    else:
+        assert_matmul_close(gn[:, rows], wg, x, rows=rows, what=what + " gate")
+        assert_matmul_close(un[:, rows], wu, x, rows=rows, what=what + " up")
+    href = numerics.f64_to_bf16_bits(numerics.silu_mul(gn, un))
+    assert np.abs(_bf16_key(hb) - _bf16_key(href)).max() <= 1
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4])
+def test_gate_up_fused_small(torch_cuda, B):
+    print_case(f"fused gate/up small B={B}")
+    wg = workloads.layer_weight(3, 1, 0, shape=(1536, 512))
+    wu = workloads.layer_weight(3, 1, 1, shape=(1536, 512))
+    _gate_up_case(wg, wu, workloads.layer_activation(3, 1, 0, B, cols=512), what=f"B={B}")
+
+
+@pytest.mark.parametrize("R,C,B", [(1, 64, 1), (37, 1088, 2), (130, 2048 + 64, 3), (5, 8192, 2)])
+def test_gate_up_fused_ragged(torch_cuda, R, C, B):
+    """Rows not a multiple of a workgroup, columns not a multiple of a slab,
+    one-row and one-group matrices, outliers forcing verbatim groups."""
+    print_case(f"fused gate/up ragged R={R} C={C} B={B}")
+    rng = np.random.default_rng(R * C + B)
+    wg = workloads.gaussian_weights(rng, R, C, 0.02, 0.004, 1.0)
+    wu = workloads.gaussian_weights(rng, R, C, 0.03, 0.002, 2.0)
+    _gate_up_case(wg, wu, _x(R + C, B, C), what=f"R={R} C={C} B={B}")
+
+
+def test_gate_up_fused_full_size(torch_cuda):
+    """Llama-3.1-8B gate and up at batch 1, the benchmark's launch: bitwise
+    equal to the unfused calls, sampled rows against the oracle."""
+    print_case("fused gate/up full size")
+    wg, wu = workloads.layer_weight(2, 0, 0), workloads.layer_weight(2, 0, 1)
+    rows = np.sort(np.random.default_rng(5).choice(wg.shape[0], 384, replace=False))
+    _gate_up_case(wg, wu, workloads.layer_activation(2, 0, 0, 1), rows=rows, what="llama")
+
+
+def test_gate_up_fused_rejects(torch_cuda):
+    wg = workloads.layer_weight(3, 1, 0, shape=(64, 512))
+    wu = workloads.layer_weight(3, 1, 1, shape=(64, 512))
+    wo = workloads.layer_weight(3, 1, 1, shape=(64, 576))
+    dg, du, do = (uw.compress(w).to_device() for w in (wg, wu, wo))
+    with pytest.raises(uw.UnweightError) as ei:
+        uw.mlp_gate_up(dg, du, to_dev_bf16(_x(1, 5, 512)))
+    assert ei.value.code == uw.UW_EUNSUPPORTED
+    with pytest.raises(uw.UnweightError) as ei:
+        uw.mlp_gate_up(dg, do, to_dev_bf16(_x(1, 1, 512)))
+    assert ei.value.code == uw.UW_EINVAL
+    dn = uw.compress(wg).to_device(uw.DECODE_SECTIONS)      # no NIB section
+    with pytest.raises(uw.UnweightError) as ei:
+        uw.mlp_gate_up(dn, du, to_dev_bf16(_x(1, 1, 512)))
+    assert ei.value.code == uw.UW_EINVAL
+
+
 # --------------------------------------------------------------- full sizes
 @pytest.mark.parametrize("m", [0, 2])
 def test_full_size_gemv_batch1_all_pipelines(torch_cuda, m):
