@@ -149,7 +149,8 @@ class Step:
                     row.append(functools.partial(L.uw_matmul, ct.byref(lay.mats[m].dmat), pipe, 0, 1, xin,
                                                  batch, yout, scr, nsc, st))
             silu = functools.partial(L.uw_silu_mul_bf16, P(self.g), P(self.u), batch * F, P(self.h), st)
-            self.fused = (fuse and pipe == uw.UW_PIPE_DIRECT and batch <= 4 and batch * H * 2 <= 32768)
+            self.fused = (fuse and batch <= 4 and batch * H * 2 <= 32768
+                          and self._plans_direct_gemv(uw, pipe, F, H, batch))
             if self.fused:
                 # gate, up and the SiLU product in one launch (h only)
                 gu = functools.partial(L.uw_mlp_gate_up, ct.byref(lay.mats[0].dmat), ct.byref(lay.mats[1].dmat),
@@ -160,6 +161,21 @@ class Step:
             else:
                 self.calls.append([row[0], row[1], silu, row[2]])
                 self.bytes.append([palette_bytes(lay.info[m], batch) for m in range(3)])
+
+    @staticmethod
+    def _plans_direct_gemv(uw, pipe, F, H, batch):
+        """Gate/up may be fused when they would run as direct-palette GEMVs:
+        asked for directly, or what the plan table holds for the gate shape
+        at this batch (no entry: direct palette, GEMV below batch 4)."""
+        if pipe == uw.UW_PIPE_DIRECT:
+            return True
+        if pipe != uw.UW_PIPE_AUTO:
+            return False
+        plan = uw.plan_lookup(F, H, batch)
+        if plan is None:
+            return batch < 4
+        p, k, _ = plan
+        return p in (uw.UW_PIPE_DIRECT, uw.UW_PIPE_AUTO) and k == uw.UW_KERNEL_GEMV
 
     def run(self, i):
         for f in self.calls[i % len(self.layers)]:
@@ -475,6 +491,7 @@ def stack_bench(blobs, n_layers, batches, tune_copies=4, reps=5):
             choice[shape] = (k, sk)
         st = Step(layers, b, "auto", stream=stream, workload=5)
         t_c = time_stack(st, reps)
+        fused = st.fused
         del st
         sb = Step(layers, b, "bf16", stream=stream, workload=5, bf16_choice=choice)
         t_b = time_stack(sb, reps)
@@ -484,6 +501,7 @@ def stack_bench(blobs, n_layers, batches, tune_copies=4, reps=5):
                "speedup_vs_bf16": round(t_b / t_c, 4), "speedup_vs_torch_bf16": round(t_t / t_c, 4),
                "bf16_equiv_GBps": round(sizes["bf16_bytes"] / t_c / 1e9, 1),
                "plan": [{"shape": [r["rows"], r["cols"]], **(r["best"] or {})} for r in report],
+               "gate_up_fused": fused,
                "bf16_kernels": {f"{s_[0]}x{s_[1]}": autotune.KERNEL_NAMES[k] + (f"(split {sk})" if sk > 1 else "")
                                 for s_, (k, sk) in choice.items()}}
         rows.append(row)
