@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true",
                    help="skip the autotuned batch sweep (1..256) over the gate and down shapes")
     p.add_argument("--sweep-batches", default="1,2,4,8,16,32,64,128,256")
+    p.add_argument("--no-config34", action="store_true",
+                   help="skip the batch-4/16 layer steps and the per-row-sigma batch-64..256 comparison")
     p.add_argument("--no-stack", action="store_true",
                    help="skip the 32-layer stack (generation ~1 min, ~22 GB of device memory)")
     p.add_argument("--stack-layers", type=int, default=32)
@@ -67,13 +69,16 @@ def log(msg):
 class Layer:
     """One MLP layer: compressed matrices on the device plus raw bf16 copies."""
 
-    def __init__(self, layer, keep_bf16):
+    def __init__(self, layer, keep_bf16, workload=2, mats=(0, 1, 2)):
         import torch
         import mlp_matmul_amd as uw
         import workloads
         self.mats, self.bf16, self.info = [], [], []
         for m in range(3):
-            w = workloads.layer_weight(2, layer, m)
+            if m not in mats:
+                self.mats.append(None), self.bf16.append(None), self.info.append(None)
+                continue
+            w = workloads.layer_weight(workload, layer, m)
             blob = uw.compress(w, emit_palette=True)
             dm = blob.to_device(uw.DECODE_SECTIONS + ("nib",))
             self.mats.append(dm)
@@ -358,6 +363,79 @@ def batch_sweep(layers, batches):
         out.append(row)
         log(f"sweep {shape} B={b}: best {r['best']} {s_['us']} bf16 {row['bf16_us']} ({k_b16}) "
             f"torch {row['torch_bf16_us']} us")
+    return out
+
+
+# ------------------------------------------------------------ config 3 / 4
+def layer_steps(layers, batches, stream, steps=30, warmup=5):
+    """The MLP-layer step (gate/up -> SiLU product -> down) at small batches:
+    direct palette (kernel by the library's default choice; gate/up fused
+    where it applies) against the hand-written bf16 kernels."""
+    rows = []
+    for b in batches:
+        sd = Step(layers, b, "direct", stream=stream)
+        t_d = time_steps(sd, steps, warmup)
+        sb = Step(layers, b, "bf16", stream=stream)
+        t_b = time_steps(sb, steps, warmup)
+        rows.append({"batch": b, "direct_ms": round(t_d * 1e3, 5), "bf16_ms": round(t_b * 1e3, 5),
+                     "speedup_vs_bf16": round(t_b / t_d, 4), "gate_up_fused": sd.fused,
+                     "bf16_equiv_GBps": round(3 * 2 * 14336 * 4096 / t_d / 1e9, 1)})
+        log(f"layer step B={b}: direct {rows[-1]['direct_ms']} ms, bf16 {rows[-1]['bf16_ms']} ms")
+        del sd, sb
+    return rows
+
+
+def time_pipeline(copies, pipeline, kernel, split_k, X, reps=20, warmup=3, stream=None):
+    """Seconds per uw_matmul call (pipeline, kernel, split_k), rotating copies."""
+    import torch
+    import mlp_matmul_amd as uw
+    from mlp_matmul_amd import autotune
+    stream = stream or torch.cuda.current_stream()
+    R, C, B = copies[0].rows, copies[0].cols, X.shape[0]
+    Y = torch.empty((B, R), dtype=torch.float32, device="cuda")
+    scratch = torch.empty(max(uw.scratch_bytes(pipeline, R, C, B, split_k), 16), dtype=torch.uint8, device="cuda")
+    return autotune.time_candidate(copies, X, Y, scratch, (pipeline, kernel, split_k), stream, reps, warmup)
+
+
+def config4(batches, n_copies=4):
+    """Per-row-scaled weights (sigma_r log-uniform in [0.005, 0.05]) at batch
+    64/128/256 on both Llama shapes: palette transcode (P3) vs direct palette
+    (P4), each with its best kernel, vs the best hand-written bf16 kernel and
+    torch.matmul; MFMA utilisation of each against the dense bf16 peak."""
+    import torch
+    import mlp_matmul_amd as uw
+    from mlp_matmul_amd import autotune
+    import workloads
+    F, H = workloads.LLAMA_FFN, workloads.LLAMA_HIDDEN
+    layers = [Layer(i, keep_bf16=True, workload=4, mats=(0, 2)) for i in range(n_copies)]
+    out = []
+    for m in (0, 2):
+        R, C = workloads.MLP_SHAPES[m]
+        copies = [L.mats[m] for L in layers]
+        for b in batches:
+            X = torch.from_numpy(workloads.layer_activation(4, 0, m, b).view(np.int16)).view(torch.bfloat16).cuda()
+            row = {"shape": [R, C], "batch": b}
+            flops = 2.0 * b * R * C
+            for name, p in (("pal", uw.UW_PIPE_PAL), ("direct", uw.UW_PIPE_DIRECT)):
+                best = None
+                for (p_, k, sk) in autotune.candidates(R, C, b):
+                    if p_ != p:
+                        continue
+                    t = time_pipeline(copies, p, k, sk, X)
+                    if best is None or t < best[0]:
+                        best = (t, autotune.KERNEL_NAMES[k] + (f"(split {sk})" if sk > 1 else ""))
+                row[name] = {"us": round(best[0] * 1e6, 3), "kernel": best[1],
+                             "mfma_util": round(flops / best[0] / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)}
+            t_b, k_b, _, _ = time_bf16([L.bf16[m] for L in layers], X)
+            t_t = time_torch_bf16([L.bf16[m] for L in layers], X)
+            row["bf16"] = {"us": round(t_b * 1e6, 3), "kernel": k_b,
+                           "mfma_util": round(flops / t_b / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)}
+            row["torch_bf16"] = {"us": round(t_t * 1e6, 3),
+                                 "mfma_util": round(flops / t_t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)}
+            out.append(row)
+            log(f"config4 {R}x{C} B={b}: pal {row['pal']} direct {row['direct']} bf16 {row['bf16']} "
+                f"torch {row['torch_bf16']}")
+    del layers
     return out
 
 
@@ -706,6 +784,12 @@ def main():
         batches = [int(v) for v in a.sweep_batches.split(",") if v]
         out["batch_sweep"] = batch_sweep(layers, batches)
         out["plan"] = [{"shape": r["shape"], "batch": r["batch"], **(r["best"] or {})} for r in out["batch_sweep"]]
+    if not a.no_config34 and not a.no_compare:
+        out["layer_steps"] = {"workload": "llama3.1-8b-mlp-layer, direct palette vs bf16, batch 4 and 16",
+                              "rows": layer_steps(layers, [4, 16], stream)}
+        out["per_row_sigma"] = {"workload": "llama3.1-8b gate/down shapes, per-row sigma log-U[0.005,0.05], "
+                                            "4 copies rotated",
+                                "rows": config4([64, 128, 256])}
     if blobs is not None:
         out["stack"] = stack_bench(blobs, a.stack_layers, [int(v) for v in a.stack_batches.split(",") if v])
     if not a.no_cpu_baseline:
