@@ -274,10 +274,10 @@ def time_bf16(mats_bf16, X, reps=20, warmup=3, stream=None):
     R, C = mats_bf16[0].shape
     B = X.shape[0]
     Y = torch.empty((B, R), dtype=torch.float32, device="cuda")
-    scratch = torch.empty(4 * 4 * B * R + 256, dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(8 * 4 * B * R + 256, dtype=torch.uint8, device="cuda")
     opts = ([(uw.UW_KERNEL_GEMV, 1)] if B <= 16 else []) \
         + ([(uw.UW_KERNEL_SKINNY, 1)] if 2 <= B <= 64 and autotune.skinny_ok(C) else []) \
-        + [(uw.UW_KERNEL_MFMA, s_) for s_ in (1, 2, 4)]
+        + [(uw.UW_KERNEL_MFMA, s_) for s_ in ((1, 2, 4, 8) if R <= 8192 else (1, 2, 4))]
     best = None
     for k, sk in opts:
         calls = [lambda W=W: uw.check(L.uw_gemm_bf16(ct.c_void_p(W.data_ptr()), R, C, ct.c_void_p(X.data_ptr()), B,

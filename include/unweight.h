@@ -203,7 +203,7 @@ int uw_transcode_palette(const uw_dmat* d, uint8_t* out_nib, void* stream);
 enum {
     UW_KERNEL_AUTO = 0,    /* GEMV below batch 4, SKINNY up to 64 (when supported), MFMA above */
     UW_KERNEL_GEMV = 1,    /* wavefront-reduction GEMV (v_dot2 bf16), batch <= 16 */
-    UW_KERNEL_MFMA = 2,    /* bf16 MFMA, 32 rows x up to 128 batch columns per wave, any batch */
+    UW_KERNEL_MFMA = 2,    /* bf16 MFMA, 64 rows x 64 or 128 batch columns per wave, any batch; cols <= 65536 */
     UW_KERNEL_SKINNY = 3   /* bf16 MFMA, 16 rows x one K-slice per wave, batch tiles of <= 64;
                               needs cols % 128 == 0 and cols <= 32768 (else UW_EUNSUPPORTED) */
 };

@@ -43,9 +43,10 @@ def candidates(rows, cols, batch, has_palette=True):
         if batch >= 2 and skinny_ok(cols):
             out.append((p, UW_KERNEL_SKINNY, 1))
         splits = [1]
-        # few row tiles: split the K loop so every CU gets work
-        if rows <= 8192 and cols >= 4096:
-            splits += [2, 4]
+        # the tiled kernel covers 256 rows x 64-128 batch columns per
+        # workgroup: split the K loop so every CU gets work
+        if cols >= 2048 and batch >= 16:
+            splits += [2, 4] + ([8] if rows <= 8192 else [])
         for s in splits:
             out.append((p, UW_KERNEL_MFMA, s))
     return out

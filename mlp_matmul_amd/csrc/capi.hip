@@ -109,6 +109,8 @@ int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* s
     if (kernel < UW_KERNEL_GEMV || kernel > UW_KERNEL_SKINNY)
         return uw::fail(UW_EINVAL, std::string(who) + ": unknown kernel");
     if (split_k < 1 || split_k > 64) return uw::fail(UW_EINVAL, std::string(who) + ": split_k must be 1..64");
+    if (kernel == UW_KERNEL_MFMA && !uwk::mfma_supported(a))
+        return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": the tiled MFMA kernel takes cols <= 65536");
     hipError_t e;
     if (kernel == UW_KERNEL_GEMV) {
         e = uwk::launch_gemv(src, a, as_stream(stream));

@@ -1,5 +1,6 @@
-// bf16 MFMA matmul on gfx950 over uncompressed weights or with on-chip
-// weight reconstruction, for batches from 16 up (any batch works).
+// bf16 MFMA matmul on gfx950 for larger batches, over uncompressed weights
+// or with on-chip weight reconstruction (any batch works; it is the kernel
+// family the launcher picks above the skinny kernel's range).
 //
 // Method: Cloudflare, "Unweight: how we compressed an LLM 22% without
 // sacrificing quality", "How the reconstructive matmul works": compressed
@@ -9,15 +10,30 @@
 // the reconstruction work.
 //
 // Mapping to CDNA4 (the page's Hopper producer/consumer TMA + WGMMA design is
-// not used): v_mfma_f32_16x16x32_bf16 takes its A operand as 8 consecutive-K
-// bf16 per lane (lane l -> row l%16, K slice l/16).  Each lane therefore loads
-// the compressed bytes of 16 consecutive weights of one row straight from HBM,
-// rebuilds them in registers and feeds two MFMAs; no LDS round trip for the
-// weights.  The activations, shared by every wave of the workgroup, are staged
-// through double-buffered LDS with a padded row stride (no bank conflicts on
-// the 16-byte B-operand reads).  A wave owns 32 rows x NB*16 batch columns.
-// The K order inside an MFMA is a free permutation as long as A and B agree,
-// so a lane's K slice is 16 contiguous weights split over two MFMAs.
+// not used).  Y^T = W . X^T is a tall-skinny product (rows up to 14336, batch
+// up to a few hundred), so the tiling is set by two budgets:
+//   * LDS bandwidth: the activation (B) fragments come from LDS, and each one
+//     feeds one v_mfma_f32_16x16x32_bf16 per 16-row block a wave owns; with
+//     four row blocks per wave the B reads stay at ~64 B/clk per CU at the
+//     full MFMA rate (half the LDS bandwidth);
+//   * registers: the weights (A) are rebuilt straight into A-operand
+//     registers from the compressed planes (no LDS round trip, no
+//     redundancy: every wave owns distinct rows), double-buffered.
+// A workgroup is 4 waves x 64 rows = 256 rows by NB*16 batch columns; a step
+// covers 64 columns of K.  Lane l holds 16 consecutive weights of row l%16 of
+// each of its row blocks (columns 16*(l/16)..+16 of the step) and the
+// matching activation runs as B fragments: the K order inside an MFMA is a
+// free permutation as long as A and B agree.  All loads of step s+1 (the
+// activation tile, the weight planes, the verbatim exponents) are issued
+// before step s is computed, with no load behind a branch.  The verbatim
+// bitmap words and bases of every tile the workgroup's rows touch are staged
+// in LDS once, so a step's verbatim flag and slot cost LDS reads, not a
+// dependent global load.  Split-K (blockIdx -> K slice) adds workgroups for
+// short matrices; partial tiles go to a scratch array that a second kernel
+// sums in a fixed order (deterministic).  Workgroups are numbered so that the
+// batch tiles of one row band run back to back on one XCD and share its L2.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -25,189 +41,271 @@ namespace uwk {
 
 namespace {
 
-constexpr int kKB = 64;           // K per pipeline step
-constexpr int kXS = kKB + 8;      // LDS row stride of the activation tile (bf16)
+constexpr int kKS = 64;          // K per step
+constexpr int kXST = kKS + 8;    // LDS row stride of the activation tile (bf16), padded
+constexpr int kMaxMT = 256;      // rows per workgroup at most
 
 __device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) { return pal_byte(a.pal, uint32_t(i)); }
 
+// Per row block and step: the lane's 16 compressed weights.
 template <int SRC>
-struct AFrag {
-    u32x4_t d0, d1, sm;
-    uint64_t word;
-    bool verb, ok;
+struct AStep {
+    u32x4_t d0, d1;   // BF16: 16 weights; EXP: d0 = 16 exponents; PAL: d0.xy = 16 nibbles
+    u32x4_t sm;       // EXP, PAL
+    u32x4_t vx;       // PAL: raw exponents when verbatim
+    uint32_t verb;    // PAL
 };
 
-template <int SRC>
-__device__ __forceinline__ void load_a(const MatArgs& a, int64_t row, int64_t k, AFrag<SRC>& f) {
-    f.ok = row < a.R;
-    if (!f.ok) return;
-    const int64_t pos = row * a.C + k;
-    if (SRC == SRC_BF16) {
-        const uint16_t* w = static_cast<const uint16_t*>(a.w) + pos;
-        f.d0 = load_stream16(w);
-        f.d1 = load_stream16(w + 8);
-    } else if (SRC == SRC_EXP) {
-        f.d0 = load_stream16(static_cast<const uint8_t*>(a.w) + pos);
-        f.sm = load_stream16(a.sm + pos);
-    } else {
-        const u32x2_t n = load_stream8(static_cast<const uint8_t*>(a.w) + pos / 2);
-        f.d0 = u32x4_t{n[0], n[1], 0u, 0u};
-        f.sm = load_stream16(a.sm + pos);
-        const int64_t g = pos >> 6;
-        f.word = a.bitmap[g >> 6];
-        f.verb = (f.word >> (g & 63)) & 1ull;
+template <int SRC, int NB, int RBW, int WPG>
+struct Step {
+    static constexpr int kThreads = 64 * WPG;
+    AStep<SRC> r[RBW];
+    u32x4_t x[(NB * 16 * kKS / 8 + kThreads - 1) / kThreads];   // this thread's activation pieces
+};
+
+// WPG waves per workgroup, each with RBW 16-row blocks (WPG*16*RBW rows per
+// workgroup).  Two row blocks per wave keep two waves per SIMD, so one
+// wave's rebuild overlaps another's MFMAs; with four waves per workgroup
+// those are waves of two independent workgroups, whose barriers and LDS
+// waits do not line up.  PD steps of loads are kept in flight ahead of the
+// step being computed (PD + 1 register sets).  Register budget: two row
+// blocks, or four with four batch blocks and PD = 1, fit two waves per SIMD;
+// deeper prefetch or four row blocks with eight batch blocks take the
+// register file of one wave per SIMD.
+template <int SRC, int NB, int PD, int RBW, int WPG>
+__global__ __launch_bounds__(64 * WPG, (RBW == 2 || (NB <= 4 && PD == 1)) ? 2 : 1)
+void mfma_kernel(MatArgs a, int tiles_n, int split) {
+    constexpr int kRBW = RBW;
+    constexpr int kMT = WPG * 16 * RBW;                // rows per workgroup
+    constexpr int NTHR = 64 * WPG;                     // threads per workgroup
+    constexpr int NT = NB * 16;                        // batch columns per workgroup
+    constexpr int XP = (NT * kKS / 8 + NTHR - 1) / NTHR;   // 16-byte activation pieces per thread
+    __shared__ uint32_t lut[256];
+    __shared__ __align__(16) uint16_t xs[2][NT * kXST];
+    extern __shared__ __align__(16) uint32_t tabs[];   // PAL: u64 words [nt], then u32 bases [nt]
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    if (SRC == SRC_PAL && tid < 256) lut[tid] = (palb(a, tid & 15) << 7) | (palb(a, tid >> 4) << 23);
+
+    // workgroup id -> (row band m, K slice s, batch tile n), n fastest, each
+    // XCD (id % 8) taking a contiguous run of logical tiles
+    const uint32_t G = gridDim.x, id = blockIdx.x;
+    const uint32_t xcd = id & 7u, jx = id >> 3, q8 = G >> 3, r8 = G & 7u;
+    const uint32_t L = xcd * q8 + min(xcd, r8) + jx;
+    const uint32_t n_t = L % uint32_t(tiles_n);
+    const uint32_t s_t = (L / uint32_t(tiles_n)) % uint32_t(split);
+    const uint32_t m_t = L / (uint32_t(tiles_n) * uint32_t(split));
+
+    const uint32_t R = uint32_t(a.R), C = uint32_t(a.C), B = uint32_t(a.B);
+    const uint32_t steps = C / kKS;
+    const uint32_t s_lo = steps * s_t / uint32_t(split), s_hi = steps * (s_t + 1) / uint32_t(split);
+    const uint32_t n0 = n_t * NT;
+    const uint32_t band0 = m_t * kMT;
+    const uint32_t q = uint32_t(lane) >> 4, rl = uint32_t(lane) & 15u;
+
+    // rows of this lane in each row block (rows past R read the last row; never stored)
+    uint32_t rowc[kRBW];
+#pragma unroll
+    for (int rb = 0; rb < kRBW; ++rb) rowc[rb] = min(band0 + uint32_t(wave) * (16u * kRBW) + 16u * rb + rl, R - 1u);
+
+    // verbatim tables of every tile the band touches, staged in LDS
+    const uint32_t t_base = (band0 * C) >> 12;
+    uint64_t* tword = reinterpret_cast<uint64_t*>(tabs);
+    uint32_t nt = 0;
+    if (SRC == SRC_PAL) {
+        const uint32_t last_row = min(band0 + kMT, R) - 1u;
+        nt = ((last_row * C + C - 1u) >> 12) - t_base + 1u;
     }
-}
+    uint32_t* tbase = tabs + 2 * nt;
 
-// 16 weights -> two bf16x8 MFMA operands (elements 0-7, 8-15).
-template <int SRC>
-__device__ __forceinline__ void rebuild_a(const MatArgs& a, const AFrag<SRC>& f, int64_t row, int64_t k,
-                                          const uint32_t* lut, bf16x8_t& o0, bf16x8_t& o1) {
-    uint32_t w[8];
-    if (!f.ok) {
+    const uint8_t* vb_ptr = a.vexp ? a.vexp : a.sm;
+    const uint16_t* wb = static_cast<const uint16_t*>(a.w);
+    const uint8_t* w8 = static_cast<const uint8_t*>(a.w);
+
+    // issue_w: activation pieces and weight planes of step s (no dependency);
+    // issue_v: the verbatim exponents (needs the LDS tables)
+    auto issue_w = [&](uint32_t s, Step<SRC, NB, RBW, WPG>& st) {
+        const uint32_t k0 = s * kKS;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) w[p] = 0;
-    } else if (SRC == SRC_BF16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            w[i] = f.d0[i];
-            w[4 + i] = f.d1[i];
-        }
-    } else if (SRC == SRC_EXP) {
-#pragma unroll
-        for (int p = 0; p < 8; ++p)
-            w[p] = (p & 1) ? join_pair<1>(f.sm[p >> 1], exp_pair<1>(f.d0[p >> 1]))
-                           : join_pair<0>(f.sm[p >> 1], exp_pair<0>(f.d0[p >> 1]));
-    } else {
-        uint32_t e7[8];
-#pragma unroll
-        for (int p = 0; p < 8; ++p) e7[p] = lut[(f.d0[p >> 2] >> (8 * (p & 3))) & 0xFFu];
-        if (f.verb) {
-            const int64_t pos = row * a.C + k;
-            const int64_t g = pos >> 6;
-            const uint32_t slot = verbatim_slot(f.word, uint32_t(g & 63), a.tile_vbase[g >> 6]);
-            const u32x4_t v = load16(a.vexp + uint64_t(slot) * 64 + (pos & 63));
-#pragma unroll
-            for (int p = 0; p < 8; ++p) e7[p] = (p & 1) ? exp_pair<1>(v[p >> 1]) : exp_pair<0>(v[p >> 1]);
+        for (int j = 0; j < XP; ++j) {
+            const uint32_t c = uint32_t(tid) + uint32_t(NTHR) * j;   // piece: batch row c/8, 8 columns (c%8)*8
+            const uint32_t nb = min(c / 8u, uint32_t(NT) - 1u);
+            const uint32_t b = min(n0 + nb, B - 1u);
+            st.x[j] = load16(a.X + b * C + k0 + (c % 8u) * 8u);
         }
 #pragma unroll
-        for (int p = 0; p < 8; ++p)
-            w[p] = (p & 1) ? join_pair<1>(f.sm[p >> 1], e7[p]) : join_pair<0>(f.sm[p >> 1], e7[p]);
-    }
-    o0 = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
-    o1 = __builtin_bit_cast(bf16x8_t, u32x4_t{w[4], w[5], w[6], w[7]});
-}
-
-// NB: 16-column batch blocks per wave; WM x WN waves per workgroup.
-template <int SRC, int NB, int WM, int WN>
-__global__ __launch_bounds__(256) void mfma_kernel(MatArgs a) {
-    constexpr int NT = WN * NB * 16;       // batch columns per workgroup
-    constexpr int MT = WM * 32;            // rows per workgroup
-    constexpr int XCH = NT * (kKB / 8);    // 16-byte activation chunks per step
-    constexpr int XPT = (XCH + 255) / 256; // chunks per thread
-    extern __shared__ uint32_t lds[];
-    uint32_t* lut = lds;                                       // 256 dwords
-    uint16_t* xs = reinterpret_cast<uint16_t*>(lds + 256);     // [2][NT][kXS]
-
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int wm = wave % WM, wn = wave / WM;
-    if (SRC == SRC_PAL) lut[tid] = (palb(a, tid & 15) << 7) | (palb(a, tid >> 4) << 23);
-
-    const int64_t C = a.C;
-    const int64_t row0 = int64_t(blockIdx.x) * MT + wm * 32;
-    const int64_t nbase = int64_t(blockIdx.y) * NT;            // first batch row of this workgroup
-    // K range of this split
-    const int64_t nkb = C / kKB;
-    const int64_t per = (nkb + a.split_k - 1) / a.split_k;
-    const int64_t kb0 = int64_t(blockIdx.z) * per;
-    const int64_t kb1 = min(nkb, kb0 + per);
-
-    const int64_t arow0 = row0 + (lane & 15);
-    const int64_t arow1 = arow0 + 16;
-    const int ksl = 16 * (lane >> 4);                           // lane's K slice inside a step
-
-    f32x4_t acc[2][NB];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    AFrag<SRC> fa0, fa1;
-    u32x4_t xr[XPT];
-    auto load_x = [&](int64_t kb) {
-#pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int c = tid + i * 256;
-            xr[i] = u32x4_t{0u, 0u, 0u, 0u};
-            if (c < XCH) {
-                const int n = c / (kKB / 8), part = c % (kKB / 8);
-                const int64_t b = nbase + n;
-                if (b < a.B) xr[i] = load16(a.X + b * C + kb * kKB + part * 8);
+        for (int rb = 0; rb < kRBW; ++rb) {
+            const uint32_t pos = rowc[rb] * C + k0 + 16u * q;
+            AStep<SRC>& f = st.r[rb];
+            if (SRC == SRC_BF16) {
+                f.d0 = load16(wb + pos);
+                f.d1 = load16(wb + pos + 8);
+            } else if (SRC == SRC_EXP) {
+                f.d0 = load16(w8 + pos);
+                f.sm = load16(a.sm + pos);
+            } else {
+                const u32x2_t n = *reinterpret_cast<const u32x2_t*>(w8 + pos / 2);
+                f.d0 = u32x4_t{n[0], n[1], 0u, 0u};
+                f.sm = load16(a.sm + pos);
             }
         }
     };
-    auto store_x = [&](int buf) {
-        uint16_t* dst = xs + buf * NT * kXS;
+    auto issue_v = [&](uint32_t s, Step<SRC, NB, RBW, WPG>& st) {
+        if (SRC != SRC_PAL) return;
+        const uint32_t k0 = s * kKS;
 #pragma unroll
-        for (int i = 0; i < XPT; ++i) {
-            const int c = tid + i * 256;
-            if (c < XCH) {
-                const int n = c / (kKB / 8), part = c % (kKB / 8);
-                *reinterpret_cast<u32x4_t*>(dst + n * kXS + part * 8) = xr[i];
-            }
+        for (int rb = 0; rb < kRBW; ++rb) {
+            const uint32_t pos = rowc[rb] * C + k0 + 16u * q;
+            const uint32_t g = pos >> 6, tl = (g >> 6) - t_base, bit = g & 63u;
+            const uint64_t word = tword[tl];
+            AStep<SRC>& f = st.r[rb];
+            f.verb = uint32_t(word >> bit) & 1u;
+            const uint32_t slot = verbatim_slot(word, bit, tbase[tl]);
+            // lanes outside verbatim groups all read one shared line
+            f.vx = load16(vb_ptr + (f.verb ? slot * 64u + (pos & 63u) : 0u));
+        }
+    };
+    auto stage_x = [&](uint32_t buf, const Step<SRC, NB, RBW, WPG>& st) {
+#pragma unroll
+        for (int j = 0; j < XP; ++j) {
+            const uint32_t c = uint32_t(tid) + uint32_t(NTHR) * j;
+            if (c < uint32_t(NT) * 8u)
+                *reinterpret_cast<u32x4_t*>(&xs[buf][(c / 8u) * kXST + (c % 8u) * 8u]) = st.x[j];
         }
     };
 
-    if (kb0 < kb1) {
-        load_a<SRC>(a, arow0, kb0 * kKB + ksl, fa0);
-        load_a<SRC>(a, arow1, kb0 * kKB + ksl, fa1);
-        load_x(kb0);
-    }
-    int buf = 0;
-    for (int64_t kb = kb0; kb < kb1; ++kb) {
-        store_x(buf);
-        __syncthreads();
-        bf16x8_t A0[2], A1[2];
-        rebuild_a<SRC>(a, fa0, arow0, kb * kKB + ksl, lut, A0[0], A0[1]);
-        rebuild_a<SRC>(a, fa1, arow1, kb * kKB + ksl, lut, A1[0], A1[1]);
-        if (kb + 1 < kb1) {
-            load_a<SRC>(a, arow0, (kb + 1) * kKB + ksl, fa0);
-            load_a<SRC>(a, arow1, (kb + 1) * kKB + ksl, fa1);
-            load_x(kb + 1);
+    f32x4_t acc[kRBW][NB];
+#pragma unroll
+    for (int rb = 0; rb < kRBW; ++rb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](uint32_t buf, const Step<SRC, NB, RBW, WPG>& st) {
+        // B fragments of the step: batch block nb, substep sub (8 columns)
+        bf16x8_t Bf[2][NB];
+        const uint16_t* xb = &xs[buf][rl * kXST + 16u * q];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                Bf[sub][nb] = *reinterpret_cast<const bf16x8_t*>(xb + nb * 16 * kXST + 8 * sub);
+#pragma unroll
+        for (int rb = 0; rb < kRBW; ++rb) {
+            const AStep<SRC>& f = st.r[rb];
+            uint32_t w[8];
+            if (SRC == SRC_BF16) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    w[i] = f.d0[i];
+                    w[4 + i] = f.d1[i];
+                }
+            } else if (SRC == SRC_EXP) {
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    w[p] = (p & 1) ? join_pair<1>(f.sm[p >> 1], exp_pair<1>(f.d0[p >> 1]))
+                                   : join_pair<0>(f.sm[p >> 1], exp_pair<0>(f.d0[p >> 1]));
+            } else {
+                uint32_t e7[8];
+#pragma unroll
+                for (int p = 0; p < 8; ++p) e7[p] = lut[(f.d0[p >> 2] >> (8 * (p & 3))) & 0xFFu];
+                if (__builtin_amdgcn_ballot_w64(f.verb != 0)) {      // rare: raw exponents for verbatim lanes
+#pragma unroll
+                    for (int p = 0; p < 8; ++p) {
+                        const uint32_t er = (p & 1) ? exp_pair<1>(f.vx[p >> 1]) : exp_pair<0>(f.vx[p >> 1]);
+                        e7[p] = f.verb ? er : e7[p];
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < 8; ++p)
+                    w[p] = (p & 1) ? join_pair<1>(f.sm[p >> 1], e7[p]) : join_pair<0>(f.sm[p >> 1], e7[p]);
+            }
+            const bf16x8_t Asub[2] = {__builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]}),
+                                      __builtin_bit_cast(bf16x8_t, u32x4_t{w[4], w[5], w[6], w[7]})};
+            // substep outer: consecutive MFMAs update different accumulators
+            // (a dependent pair back to back waits out the MFMA latency)
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Asub[sub], Bf[sub][nb], acc[rb][nb], 0, 0, 0);
         }
-        const uint16_t* xb = xs + buf * NT * kXS + (wn * NB * 16 + (lane & 15)) * kXS + ksl;
+    };
+
+    // Start: the first step's weight loads go out first, then the tables are
+    // staged (the loads before them are not waited for), then its verbatim
+    // loads and the next PD-1 steps.  Steps past the slice re-issue its last
+    // step, so no load is conditional.  Step t's activations go to xs[t & 1]:
+    // its previous reader, step t-2, finished before every wave passed the
+    // barrier of step t-1, so one barrier per step suffices.  The loop body
+    // holds its PD+1 steps with no exit between them (leftover steps run
+    // after the loop).
+    constexpr int NS = PD + 1;
+    const bool work = s_lo < s_hi;
+    const uint32_t first = work ? s_lo : 0u, last = work ? s_hi - 1u : 0u;
+    Step<SRC, NB, RBW, WPG> st[NS];
+    issue_w(first, st[0]);
+    if (SRC == SRC_PAL) {
+        for (uint32_t i = uint32_t(tid); i < nt; i += uint32_t(NTHR)) {
+            tword[i] = a.bitmap[t_base + i];
+            tbase[i] = a.tile_vbase[t_base + i];
+        }
+    }
+    __syncthreads();                                   // LUT and tables ready
+    issue_v(first, st[0]);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+    for (int j = 1; j < PD; ++j) {
+        issue_w(min(first + j, last), st[j]);
+        issue_v(min(first + j, last), st[j]);
+    }
+    if (work) {
+        uint32_t s = first;
+        for (; s + NS - 1 < s_hi; s += NS) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(xb + nb * 16 * kXS + 8 * s);
-                acc[0][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A0[s], B, acc[0][nb], 0, 0, 0);
-                acc[1][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1[s], B, acc[1][nb], 0, 0, 0);
+            for (int j = 0; j < NS; ++j) {
+                issue_w(min(s + j + PD, last), st[(j + PD) % NS]);
+                issue_v(min(s + j + PD, last), st[(j + PD) % NS]);
+                stage_x((s + j) & 1u, st[j]);
+                __syncthreads();
+                compute((s + j) & 1u, st[j]);
             }
         }
-        buf ^= 1;
+#pragma unroll
+        for (int j = 0; j < NS - 1; ++j) {             // leftover steps: already issued
+            if (s + j < s_hi) {
+                stage_x((s + j) & 1u, st[j]);
+                __syncthreads();
+                compute((s + j) & 1u, st[j]);
+            }
+        }
     }
 
-    // D layout: lane l holds column (batch) l%16, rows 4*(l/16) .. +3
-    float* out = a.split_k > 1 ? a.partial + int64_t(blockIdx.z) * a.B * a.R : a.Y;
+    // D layout: lane l holds batch column l%16, rows 4*(l/16) .. +3
+    float* out = split > 1 ? a.partial + uint64_t(s_t) * a.B * a.R : a.Y;
+    const uint32_t col = lane & 15;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRBW; ++rb) {
+        const uint32_t r = band0 + uint32_t(wave) * (16u * kRBW) + 16u * rb + 4u * q;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int64_t b = nbase + wn * NB * 16 + nb * 16 + (lane & 15);
-            const int64_t r = row0 + rb * 16 + 4 * (lane >> 4);
-            if (b >= a.B) continue;
-            float* o = out + b * a.R + r;
+            const uint32_t b = n0 + 16u * nb + col;
+            if (b >= B) continue;
+            float* o = out + uint64_t(b) * R + r;
             const f32x4_t v = acc[rb][nb];
-            if (r + 3 < a.R && ((a.R & 3) == 0)) {
+            if (r + 3 < R && (R & 3u) == 0) {
                 *reinterpret_cast<f32x4_t*>(o) = v;
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (r + i < a.R) o[i] = v[i];
+                    if (r + i < R) o[i] = v[i];
             }
         }
     }
+}
+
+__global__ __launch_bounds__(256) void zero_fill(float* __restrict__ y, int64_t n) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) y[i] = 0.f;
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p, int splits, int64_t n,
@@ -219,35 +317,69 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float* __restrict__ p
     y[i] = s;
 }
 
-template <int SRC, int NB, int WM, int WN>
+// LDS bytes of the verbatim tables for a band of at most 256 rows (PAL).
+size_t table_bytes(const MatArgs& a) {
+    const int64_t rows = a.R < kMaxMT ? a.R : int64_t(kMaxMT);
+    const int64_t nt = (rows * a.C + a.C) / 4096 + 2;
+    return size_t(nt) * 12;
+}
+
+template <int SRC, int NB, int PD, int RBW, int WPG>
 hipError_t launch_cfg(const MatArgs& a, hipStream_t s) {
-    constexpr int NT = WN * NB * 16, MT = WM * 32;
-    const size_t lds = 256 * 4 + size_t(2) * NT * kXS * 2;
-    static bool attr_set = false;   // opt in to more than 64 KiB of dynamic LDS once
-    if (!attr_set && lds > 65536) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&mfma_kernel<SRC, NB, WM, WN>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    dim3 grid(unsigned((a.R + MT - 1) / MT), unsigned((a.B + NT - 1) / NT), unsigned(a.split_k));
-    launch_timed(mfma_kernel<SRC, NB, WM, WN>, grid, dim3(256), lds, s, a);
+    constexpr int NT = NB * 16, kMT = WPG * 16 * RBW;
+    const size_t lds = SRC == SRC_PAL ? table_bytes(a) : 0;
+    const int tiles_m = int((a.R + kMT - 1) / kMT), tiles_n = int((a.B + NT - 1) / NT);
+    const int64_t grid = int64_t(tiles_m) * tiles_n * a.split_k;
+    launch_timed(mfma_kernel<SRC, NB, PD, RBW, WPG>, dim3(unsigned(grid)), dim3(64 * WPG), lds, s, a, tiles_n,
+                 int(a.split_k));
     return hipGetLastError();
 }
 
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return e && *e ? atoi(e) : dflt;
+}
+
+// Batch blocks per workgroup (4 up to batch 64, else 8), row blocks per
+// wave (2), waves per workgroup (4, 8 above batch 128) and prefetch depth
+// (1), as measured on the Llama MLP shapes at batch 64-256; UW_MFMA_NB /
+// _RBW / _WPG / _PD override for tuning.  Combinations that do not fit the register file
+// are never instantiated.
 template <int SRC>
 hipError_t launch_src(const MatArgs& a, hipStream_t s) {
-    if (a.B <= 16) return launch_cfg<SRC, 1, 4, 1>(a, s);
-    if (a.B <= 32) return launch_cfg<SRC, 2, 4, 1>(a, s);
-    if (a.B <= 64) return launch_cfg<SRC, 4, 4, 1>(a, s);
-    if (a.B <= 128) return launch_cfg<SRC, 4, 2, 2>(a, s);
-    return launch_cfg<SRC, 8, 2, 2>(a, s);
+    const int nb = env_int("UW_MFMA_NB", a.B <= 64 ? 4 : 8);
+    const int rbw = env_int("UW_MFMA_RBW", 2);
+    const int wpg = env_int("UW_MFMA_WPG", a.B > 128 ? 8 : 4);
+    const int pd = env_int("UW_MFMA_PD", 1);
+    if (rbw <= 2) {
+        if (wpg <= 4) return nb <= 4 ? launch_cfg<SRC, 4, 1, 2, 4>(a, s) : launch_cfg<SRC, 8, 1, 2, 4>(a, s);
+        return nb <= 4 ? launch_cfg<SRC, 4, 1, 2, 8>(a, s) : launch_cfg<SRC, 8, 1, 2, 8>(a, s);
+    }
+    if (nb <= 4) {
+        if (pd <= 1) return launch_cfg<SRC, 4, 1, 4, 4>(a, s);
+        if (pd == 2) return launch_cfg<SRC, 4, 2, 4, 4>(a, s);
+        return launch_cfg<SRC, 4, 3, 4, 4>(a, s);
+    }
+    if (SRC == SRC_BF16 && pd > 1) return launch_cfg<SRC, 8, (SRC == SRC_BF16 ? 3 : 1), 4, 4>(a, s);
+    return launch_cfg<SRC, 8, 1, 4, 4>(a, s);
 }
 
 }  // namespace
 
+// The kernel keeps a lane's row segment of one step in one 64-column group
+// and stages the verbatim tables of a 256-row band in LDS (at most 48 KiB).
+bool mfma_supported(const MatArgs& a) {
+    return a.C % kKS == 0 && (a.C == 0 || table_bytes(a) <= 48 * 1024);
+}
+
 hipError_t launch_mfma(int src, const MatArgs& a, hipStream_t s) {
     if (a.R == 0 || a.B == 0) return hipSuccess;
+    if (a.C == 0) {                                    // empty sums
+        const int64_t n = a.B * a.R;
+        zero_fill<<<unsigned((n + 255) / 256), 256, 0, s>>>(a.Y, n);
+        return hipGetLastError();
+    }
+    if (!mfma_supported(a)) return hipErrorNotSupported;
     hipError_t e;
     switch (src) {
         case SRC_BF16: e = launch_src<SRC_BF16>(a, s); break;

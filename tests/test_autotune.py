@@ -22,8 +22,9 @@ def test_candidate_space():
     assert uw.UW_KERNEL_SKINNY not in {k for _, k, _ in autotune.candidates(64, 192, 8)}
     assert uw.UW_KERNEL_SKINNY not in {k for _, k, _ in autotune.candidates(64, 32768 + 128, 8)}
     assert uw.UW_KERNEL_SKINNY in {k for _, k, _ in autotune.candidates(64, 32768, 8)}
-    assert {s for _, _, s in autotune.candidates(4096, 14336, 256)} == {1, 2, 4}
-    assert {s for _, _, s in autotune.candidates(14336, 4096, 256)} == {1}
+    assert {s for _, _, s in autotune.candidates(4096, 14336, 256)} == {1, 2, 4, 8}
+    assert {s for _, _, s in autotune.candidates(14336, 4096, 256)} == {1, 2, 4}
+    assert {s for _, _, s in autotune.candidates(14336, 4096, 8)} == {1}
     assert uw.UW_PIPE_DIRECT not in {p for p, _, _ in autotune.candidates(64, 64, 1, has_palette=False)}
 
 

@@ -262,6 +262,26 @@ def test_mfma_split_k(torch_cuda, split):
     assert_matmul_close(Y.cpu().numpy(), w, x, what=f"split {split}")
 
 
+@pytest.mark.parametrize("R,C,B,split", [(300, 128, 20, 4), (257, 64, 70, 3), (513, 1024, 129, 16)])
+def test_mfma_split_k_short_slices(torch_cuda, R, C, B, split):
+    """Split-K with empty and one-step K slices, a band past R, a batch tile
+    past B: every partial tile is written and summed."""
+    print_case(f"mfma split short R={R} C={C} B={B} split={split}")
+    w = workloads.gaussian_weights(np.random.default_rng(R + C + split), R, C, 0.02, 0.004, 1.0)
+    x = _x(R * split, B, C)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    exps = uw.decode_exponents(dm)
+    for p in (uw.UW_PIPE_DIRECT, uw.UW_PIPE_EXP, uw.UW_PIPE_FULL):
+        scratch = uw.alloc_scratch(p, R, C, B, split)
+        Y = uw.matmul(dm, X, pipeline=p, kernel=uw.UW_KERNEL_MFMA, split_k=split, scratch=scratch)
+        assert_matmul_close(Y.cpu().numpy(), w, x, what=f"pipeline {p} split {split}")
+    Yb = uw.gemm_bf16(to_dev_bf16(w), X, kernel=uw.UW_KERNEL_MFMA)
+    assert_matmul_close(Yb.cpu().numpy(), w, x, what="bf16")
+    Ye = uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_MFMA)
+    assert_matmul_close(Ye.cpu().numpy(), w, x, what="exp")
+
+
 @pytest.mark.parametrize("R,C", [(1, 64), (3, 128), (37, 192), (130, 1088), (67, 2048 + 64)])
 @pytest.mark.parametrize("B", [1, 6, 16, 40])
 def test_ragged_shapes(torch_cuda, R, C, B):
