@@ -81,7 +81,15 @@ int uw_abi_struct_sizes(uint64_t* info, uint64_t* dmat, uint64_t* opts);
  *                          byte i/2, low nibble for even i; 0 in verbatim groups
  *   DLUT       uint8[2^L]  decode table (derived, not serialized): entry v =
  *                          (symbol << 4) | length of the codeword that prefixes
- *                          the L-bit string v, L = longest code length */
+ *                          the L-bit string v, L = longest code length
+ *   MLUT       uint32[4096] multi-symbol decode table (derived, not
+ *                          serialized): entry v describes the codewords that
+ *                          lie wholly inside the 12-bit string v, taken one
+ *                          after another as DLUT decodes them, at most 4:
+ *                          bits 0-7 their total length, bits 8-15 four times
+ *                          their count, bits 16+4k the symbol of the k-th.
+ *                          Count 0 means the first codeword is longer than
+ *                          12 bits (decode it with DLUT). */
 enum {
     UW_SEC_SM = 0,
     UW_SEC_STREAM,
@@ -92,6 +100,7 @@ enum {
     UW_SEC_BITMAP,
     UW_SEC_NIB,
     UW_SEC_DLUT,
+    UW_SEC_MLUT,
     UW_NUM_SECTIONS
 };
 
@@ -115,7 +124,7 @@ typedef struct {
     uint64_t huffman_form_bytes;   /* header + all sections but NIB and DLUT */
     uint64_t palette_form_bytes;   /* header + SM + NIB + VEXP + BITMAP + TILE_VBASE */
     int32_t has_palette;           /* NIB section present */
-    int32_t reserved;
+    uint32_t max_tile_bytes;       /* longest tile of STREAM, bytes */
 } uw_info;
 
 /* Compress W (host, [rows, cols] bf16 bits) into a new blob.
@@ -159,12 +168,13 @@ int uw_validate(const uw_blob* blob);
 /* A compressed matrix whose sections the caller has copied to device memory.
  * Pointers of sections a call does not read may be NULL: the Huffman
  * decoders read SM (full mode only), STREAM, GLEN, TILE_OFF, TILE_VBASE,
- * VEXP, BITMAP, DLUT; the palette-source matmul reads SM, NIB (or a
+ * VEXP, BITMAP, DLUT, MLUT; the palette-source matmul reads SM, NIB (or a
  * transcoded copy), VEXP, BITMAP, TILE_VBASE; the exponent-source matmul
  * reads SM and a decoded exponent plane. */
 typedef struct {
     int64_t rows, cols, groups, tiles, verbatim_groups;
     uint64_t stream_bytes;
+    uint64_t max_tile_bytes;       /* longest tile of STREAM (sizes the decoders' LDS) */
     int32_t palette_size, lmax;
     uint8_t palette[16];
     const uint8_t* sm;
@@ -176,6 +186,7 @@ typedef struct {
     const uint64_t* bitmap;
     const uint8_t* nib;
     const uint8_t* dlut;
+    const uint32_t* mlut;
 } uw_dmat;
 
 /* Fill a descriptor from blob info (host) and device section pointers

@@ -18,7 +18,7 @@ import numpy as np
 from ._capi import (  # noqa: F401
     SECTION_NAMES, UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY, UW_NUM_SECTIONS,
     UW_PIPE_AUTO, UW_PIPE_BF16, UW_PIPE_DIRECT, UW_PIPE_EXP, UW_PIPE_FULL, UW_PIPE_PAL,
-    UW_SEC_BITMAP, UW_SEC_DLUT, UW_SEC_GLEN, UW_SEC_NIB, UW_SEC_SM, UW_SEC_STREAM,
+    UW_SEC_BITMAP, UW_SEC_DLUT, UW_SEC_GLEN, UW_SEC_MLUT, UW_SEC_NIB, UW_SEC_SM, UW_SEC_STREAM,
     UW_SEC_TILE_OFF, UW_SEC_TILE_VBASE, UW_SEC_VEXP, UW_EUNSUPPORTED, UW_EINVAL, UnweightError, check, lib,
     uw_dmat, uw_info,
     uw_opts,
@@ -28,11 +28,11 @@ PIPELINES = {"full": UW_PIPE_FULL, "exp": UW_PIPE_EXP, "pal": UW_PIPE_PAL, "dire
 KERNELS = {"auto": UW_KERNEL_AUTO, "gemv": UW_KERNEL_GEMV, "mfma": UW_KERNEL_MFMA, "skinny": UW_KERNEL_SKINNY}
 
 # sections each use reads on the device
-DECODE_SECTIONS = ("sm", "stream", "glen", "tile_off", "tile_vbase", "vexp", "bitmap", "dlut")
+DECODE_SECTIONS = ("sm", "stream", "glen", "tile_off", "tile_vbase", "vexp", "bitmap", "dlut", "mlut")
 DIRECT_SECTIONS = ("sm", "nib", "vexp", "bitmap", "tile_vbase")
 SECTION_DTYPES = {"sm": np.uint8, "stream": np.uint8, "glen": np.uint16, "tile_off": np.uint32,
                   "tile_vbase": np.uint32, "vexp": np.uint8, "bitmap": np.uint64, "nib": np.uint8,
-                  "dlut": np.uint8}
+                  "dlut": np.uint8, "mlut": np.uint32}
 
 
 def _torch():

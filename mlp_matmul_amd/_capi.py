@@ -16,8 +16,8 @@ UW_EHIP = -4
 UW_EUNSUPPORTED = -5
 
 (UW_SEC_SM, UW_SEC_STREAM, UW_SEC_GLEN, UW_SEC_TILE_OFF, UW_SEC_TILE_VBASE, UW_SEC_VEXP,
- UW_SEC_BITMAP, UW_SEC_NIB, UW_SEC_DLUT, UW_NUM_SECTIONS) = range(10)
-SECTION_NAMES = ("sm", "stream", "glen", "tile_off", "tile_vbase", "vexp", "bitmap", "nib", "dlut")
+ UW_SEC_BITMAP, UW_SEC_NIB, UW_SEC_DLUT, UW_SEC_MLUT, UW_NUM_SECTIONS) = range(11)
+SECTION_NAMES = ("sm", "stream", "glen", "tile_off", "tile_vbase", "vexp", "bitmap", "nib", "dlut", "mlut")
 
 UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY = 0, 1, 2, 3
 UW_PIPE_AUTO, UW_PIPE_FULL, UW_PIPE_EXP, UW_PIPE_PAL, UW_PIPE_DIRECT, UW_PIPE_BF16 = range(6)
@@ -36,7 +36,7 @@ class uw_info(ct.Structure):
         ("hist", ct.c_uint64 * 256),
         ("section_bytes", ct.c_uint64 * UW_NUM_SECTIONS),
         ("huffman_form_bytes", ct.c_uint64), ("palette_form_bytes", ct.c_uint64),
-        ("has_palette", ct.c_int32), ("reserved", ct.c_int32),
+        ("has_palette", ct.c_int32), ("max_tile_bytes", ct.c_uint32),
     ]
 
 
@@ -44,10 +44,10 @@ class uw_dmat(ct.Structure):
     _fields_ = [
         ("rows", ct.c_int64), ("cols", ct.c_int64), ("groups", ct.c_int64), ("tiles", ct.c_int64),
         ("verbatim_groups", ct.c_int64), ("stream_bytes", ct.c_uint64),
-        ("palette_size", ct.c_int32), ("lmax", ct.c_int32), ("palette", ct.c_uint8 * 16),
+        ("max_tile_bytes", ct.c_uint64), ("palette_size", ct.c_int32), ("lmax", ct.c_int32), ("palette", ct.c_uint8 * 16),
         ("sm", ct.c_void_p), ("stream", ct.c_void_p), ("glen", ct.c_void_p), ("tile_off", ct.c_void_p),
         ("tile_vbase", ct.c_void_p), ("vexp", ct.c_void_p), ("bitmap", ct.c_void_p), ("nib", ct.c_void_p),
-        ("dlut", ct.c_void_p),
+        ("dlut", ct.c_void_p), ("mlut", ct.c_void_p),
     ]
 
 

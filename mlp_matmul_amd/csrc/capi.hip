@@ -46,11 +46,15 @@ int check_decoder_inputs(const uw_dmat* d, const char* who, bool need_sm) {
     int rc = check_dmat(d, who);
     if (rc) return rc;
     if (d->groups == 0) return UW_OK;
-    if (!d->glen || !d->tile_off || !d->tile_vbase || !d->bitmap || !d->dlut ||
+    if (!d->glen || !d->tile_off || !d->tile_vbase || !d->bitmap || !d->dlut || !d->mlut ||
         (d->stream_bytes && !d->stream) || (d->verbatim_groups && !d->vexp) || (need_sm && !d->sm))
         return uw::fail(UW_EINVAL, std::string(who) + ": a required device section is NULL");
-    if (!aligned16(d->stream) || !aligned16(d->dlut) || !aligned16(d->vexp) || !aligned16(d->sm))
+    if (!aligned16(d->stream) || !aligned16(d->dlut) || !aligned16(d->mlut) || !aligned16(d->vexp) || !aligned16(d->sm))
         return uw::fail(UW_EINVAL, std::string(who) + ": device sections must be 16-byte aligned");
+    // a tile holds at most 64 x 64 codewords of lmax bits
+    if ((d->stream_bytes && d->max_tile_bytes == 0) ||
+        d->max_tile_bytes > uint64_t(512) * uint64_t(d->lmax > 0 ? d->lmax : 1) + 1)
+        return uw::fail(UW_EINVAL, std::string(who) + ": max_tile_bytes out of range for lmax");
     return UW_OK;
 }
 
@@ -64,7 +68,9 @@ uwk::DecodeArgs decode_args(const uw_dmat* d, void* out) {
     a.vexp = d->vexp;
     a.bitmap = d->bitmap;
     a.dlut = d->dlut;
+    a.mlut = d->mlut;
     a.stream_bytes = d->stream_bytes;
+    a.max_tile_bytes = uint32_t(d->max_tile_bytes);
     a.G = d->groups;
     a.T = d->tiles;
     a.lmax = d->lmax;
@@ -170,6 +176,7 @@ int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_S
     d->tiles = info->tiles;
     d->verbatim_groups = info->verbatim_groups;
     d->stream_bytes = info->section_bytes[UW_SEC_STREAM];
+    d->max_tile_bytes = info->max_tile_bytes;
     d->palette_size = info->palette_size;
     d->lmax = info->lmax;
     std::memcpy(d->palette, info->palette, 16);
@@ -182,6 +189,7 @@ int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_S
     d->bitmap = static_cast<const uint64_t*>(dev[UW_SEC_BITMAP]);
     d->nib = static_cast<const uint8_t*>(dev[UW_SEC_NIB]);
     d->dlut = static_cast<const uint8_t*>(dev[UW_SEC_DLUT]);
+    d->mlut = static_cast<const uint32_t*>(dev[UW_SEC_MLUT]);
     return check_dmat(d, "uw_dmat_init");
 }
 

@@ -126,6 +126,28 @@ void build_dlut(uw_blob& b) {
     b.dlut.resize(n);
 }
 
+void build_mlut(uw_blob& b) {
+    const int L = b.lmax;
+    const uint32_t mask = (1u << kMlutBits) - 1;
+    b.mlut.assign(size_t(1) << kMlutBits, 0u);
+    if (L == 0) return;
+    for (uint32_t v = 0; v <= mask; ++v) {
+        // apply the decode table to the bits not yet used (zero filled past
+        // the string's end) while the codeword it names ends inside the string
+        uint32_t used = 0, n = 0, syms = 0;
+        while (n < 4) {
+            const uint32_t rest = (v << used) & mask;
+            const uint32_t idx = L <= kMlutBits ? rest >> (kMlutBits - L) : rest << (L - kMlutBits);
+            const uint32_t ent = b.dlut[idx], len = ent & 15u;
+            if (len == 0 || used + len > uint32_t(kMlutBits)) break;
+            syms |= (ent >> 4) << (16 + 4 * n);
+            used += len;
+            ++n;
+        }
+        b.mlut[v] = used | ((4 * n) << 8) | syms;
+    }
+}
+
 void build_nibbles(uw_blob& b, const uint8_t* e, int threads) {
     int8_t idx_of[256];
     std::memset(idx_of, -1, sizeof(idx_of));
@@ -305,6 +327,7 @@ int uw_compress(const uint16_t* w, int64_t rows, int64_t cols, const uw_opts* op
         // 7. optional direct-palette nibbles, decode table
         if (emit_pal) uw::build_nibbles(*b, e.data(), nt);
         uw::build_dlut(*b);
+        uw::build_mlut(*b);
     } catch (const std::bad_alloc&) {
         delete b;
         return uw::fail(UW_ENOMEM, "uw_compress: out of host memory");
@@ -372,12 +395,16 @@ int uw_blob_info(const uw_blob* b, uw_info* info) {
     sb[UW_SEC_BITMAP] = b->bitmap.size() * 8;
     sb[UW_SEC_NIB] = b->has_nib ? b->nib.size() : 0;
     sb[UW_SEC_DLUT] = b->dlut.size();
+    sb[UW_SEC_MLUT] = b->mlut.size() * 4;
     info->huffman_form_bytes = uw::kHeaderBytes + sb[UW_SEC_SM] + sb[UW_SEC_STREAM] + sb[UW_SEC_GLEN] +
                                sb[UW_SEC_TILE_OFF] + sb[UW_SEC_TILE_VBASE] + sb[UW_SEC_VEXP] +
                                sb[UW_SEC_BITMAP];
     info->palette_form_bytes = uw::kHeaderBytes + sb[UW_SEC_SM] + b->N / 2 + sb[UW_SEC_VEXP] +
                                sb[UW_SEC_BITMAP] + sb[UW_SEC_TILE_VBASE];
     info->has_palette = b->has_nib;
+    uint32_t mt = 0;
+    for (size_t t = 0; t + 1 < b->tile_off.size(); ++t) mt = std::max(mt, b->tile_off[t + 1] - b->tile_off[t]);
+    info->max_tile_bytes = mt;
     return UW_OK;
 }
 
@@ -398,6 +425,7 @@ int uw_blob_section(const uw_blob* b, int sec, const void** ptr, uint64_t* bytes
             if (b->has_nib) { p = b->nib.data(); n = b->nib.size(); }
             break;
         case UW_SEC_DLUT: p = b->dlut.data(); n = b->dlut.size(); break;
+        case UW_SEC_MLUT: p = b->mlut.data(); n = b->mlut.size() * 4; break;
         default: return uw::fail(UW_EINVAL, "uw_blob_section: unknown section");
     }
     *ptr = n ? p : nullptr;
@@ -535,6 +563,7 @@ int uw_blob_deserialize(const void* buf, uint64_t bytes, uw_blob** out) {
         return rc;
     }
     uw::build_dlut(*b);
+    uw::build_mlut(*b);
     *out = b;
     return UW_OK;
 }

@@ -9,12 +9,23 @@
 // time.  Verbatim 64-element rows ("How to compress model weights
 // effectively") are copied from the raw exponent array.
 //
-// Mapping to CDNA4: one wavefront per tile of 64 groups, one lane per group.
-// The wave copies the tile's stream bytes into LDS with coalesced dword loads;
-// each lane finds its group's first bit by a wave prefix sum of the per-group
-// bit lengths, then walks 64 codewords through a 64-bit window and a 2^lmax
-// byte lookup table held in LDS.  Symbols are kept as packed nibbles in
-// registers and written out with 16-byte stores per lane.
+// Mapping to CDNA4: one wavefront per tile of 64 groups, one lane per group,
+// eight wavefronts per workgroup sharing the lookup tables in LDS.  The wave
+// copies the tile's stream into LDS with 16-byte loads issued together
+// (byte-swapped so each word reads MSB-first), and each lane finds its
+// group's first bit by a wave prefix sum of the per-group bit lengths.  A
+// lane then decodes its 64 codewords several at a time: a 32-bit window at
+// its bit position (one funnel shift of two LDS words) indexes a 4096-entry
+// multi-symbol table that yields up to four symbols, their count and their
+// total length per lookup (about 3.7 symbols for these codes, so ~19
+// lookups per group instead of 64).  Codewords longer than the 12-bit index
+// fall back to the single-symbol table.  Symbols are appended to a 64-bit
+// accumulator whose words go to a per-lane LDS slot.  The output phase then
+// walks the tile in element order, 8 elements per lane and 512 per wave
+// instruction, so that exponent and bf16 stores (and the sign/mantissa
+// loads) are contiguous across the wave.  The stream buffer is sized by the
+// matrix's longest tile, which keeps LDS per wave small enough for several
+// workgroups per CU.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -22,7 +33,12 @@ namespace uwk {
 
 namespace {
 
-constexpr int kDecWaves = 4;
+constexpr int kDecWaves = 8;
+constexpr int kMlutEntries = 4096;      // 12-bit index
+constexpr int kSlot = 9;                // LDS words per lane: 64 nibbles + one overflow word
+constexpr int kStageRounds = 4;         // 16-byte loads per lane issued before one wait
+
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 __device__ __forceinline__ uint32_t load_word(const uint8_t* s, uint32_t w, uint64_t nbytes) {
     uint64_t b = uint64_t(w) * 4;
@@ -35,174 +51,246 @@ __device__ __forceinline__ uint32_t load_word(const uint8_t* s, uint32_t w, uint
 
 __device__ __forceinline__ uint32_t pal_byte(const DecodeArgs& a, int i) { return uwk::pal_byte(a.pal, uint32_t(i)); }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-    extern __shared__ uint32_t lds[];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int lmax = a.lmax;
-    const uint32_t lut_bytes = 1u << lmax;
-    const uint32_t lut_words = (lut_bytes + 3) / 4;
-    uint32_t* lut_w = lds;
-    uint32_t* ptab = lds + lut_words;          // 256 entries indexed by a nibble pair
-    uint32_t* buf = ptab + 256 + wave * a.buf_words;
+// Orders this wave's LDS accesses around a point: LDS operations of one
+// wavefront complete in program order, so only the compiler must not move
+// accesses across it.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-    // code table -> LDS
-    if (lut_bytes >= 4) {
-        for (uint32_t i = tid; i < lut_words; i += 256) lut_w[i] = reinterpret_cast<const uint32_t*>(a.dlut)[i];
-    } else if (tid == 0) {
-        uint32_t v = 0;
-        for (uint32_t i = 0; i < lut_bytes; ++i) v |= uint32_t(a.dlut[i]) << (8 * i);
-        lut_w[0] = v;
-    }
-    // nibble pair -> (FULL) two exponents in bf16 position, (EXP) two exponent bytes
-    {
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
+// LDS word at a byte address (the tables start at LDS address 0)
+__device__ __forceinline__ uint32_t lds_ld(uint32_t addr) {
+    return *reinterpret_cast<const lds_u32*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ void lds_st(uint32_t addr, uint32_t v) {
+    *reinterpret_cast<lds_u32*>(static_cast<uintptr_t>(addr)) = v;
+}
+
+// Stream word w (any index; words outside [0, nbytes) read as zero bytes)
+__device__ __forceinline__ uint32_t load_word_any(const uint8_t* s, int64_t w, uint64_t nbytes) {
+    return w < 0 ? 0u : load_word(s, uint32_t(w), nbytes);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a) {
+    extern __shared__ uint32_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile metadata in scalar loads
+    const int lmax = a.lmax;
+    const uint32_t bw = uint32_t(a.buf_words);   // multiple of 4
+    uint32_t* mlut = lds;                        // multi-symbol table at LDS address 0
+    uint32_t* ptab = lds + kMlutEntries;         // 256 entries indexed by a nibble pair
+    uint32_t* buf = ptab + 256 + wave * (bw + 64 * kSlot);
+    // byte addresses: the wave's stream buffer, its 64 symbol slots
+    const uint32_t buf_a = __builtin_amdgcn_readfirstlane(uint32_t((kMlutEntries + 256 + wave * (bw + 64 * kSlot)) * 4));
+    const uint32_t slots_a = buf_a + bw * 4;
+    const uint32_t ptab_a = kMlutEntries * 4;
+
+    for (int i = tid; i < kMlutEntries / 4; i += 64 * kDecWaves)
+        reinterpret_cast<u32x4_t*>(mlut)[i] = reinterpret_cast<const u32x4_t*>(a.mlut)[i];
+    if (tid < 256) {
+        // nibble pair -> (FULL) two exponents in bf16 position, (EXP, PAL) two exponent bytes
         uint32_t lo = pal_byte(a, tid & 15), hi = pal_byte(a, tid >> 4);
         ptab[tid] = MODE == MODE_FULL ? (lo << 7) | (hi << 23) : lo | (hi << 8);
     }
     __syncthreads();
-    const uint8_t* lutb = reinterpret_cast<const uint8_t*>(lut_w);
-    const uint32_t lim = uint32_t(a.buf_words) - 1;
-    const int rs = 64 - (lmax > 0 ? lmax : 1);
+    const uint32_t lim = bw - 2;
+    const int fb_shift = 32 - (lmax > 0 ? lmax : 1);
+    const bool vec_ok = a.stream_bytes >= 16;
+    const int64_t N = a.G * 64;
 
-    for (int64_t tb = int64_t(blockIdx.x) * kDecWaves; tb < a.T; tb += int64_t(gridDim.x) * kDecWaves) {
-        const int64_t t = tb + wave;
-        const bool tile_ok = t < a.T;
-        uint32_t off0 = 0, off1 = 0, vbase = 0;
-        uint64_t word = 0;
-        if (tile_ok) {
-            off0 = a.tile_off[t];
-            off1 = a.tile_off[t + 1];
-            word = a.bitmap[t];
-            vbase = a.tile_vbase[t];
-        }
-        // stage the tile's stream (dword aligned) plus two zero words
-        const uint32_t w0 = off0 >> 2;
-        uint32_t nw = tile_ok ? ((off1 + 3) >> 2) - w0 : 0;
-        nw = min(nw, uint32_t(a.buf_words) - 2);
-        for (uint32_t i = lane; i < nw + 2; i += 64) buf[i] = i < nw ? load_word(a.stream, w0 + i, a.stream_bytes) : 0u;
-        __syncthreads();
-
+    // waves take tiles independently (no workgroup barrier in the loop)
+    for (int64_t t = int64_t(blockIdx.x) * kDecWaves + wave; t < a.T; t += int64_t(gridDim.x) * kDecWaves) {
+        const uint32_t off0 = a.tile_off[t], off1 = a.tile_off[t + 1], vbase = a.tile_vbase[t];
+        const uint64_t word = a.bitmap[t];
         const int64_t g = t * 64 + lane;
-        const bool gvalid = tile_ok && g < a.G;
-        const uint32_t gl = gvalid ? a.glen[g] : 0u;
+        const bool gvalid = g < a.G;
+        const uint32_t gl0 = a.glen[gvalid ? g : 0];   // unconditional: no wait inside a branch
+        const uint32_t gl = gvalid ? gl0 : 0u;
+        const bool verb = (word >> lane) & 1ull;
+        // output phase: lane handles elements 512k + 8*lane .. +7 of the tile
+        const int64_t e0 = t * 4096 + 8 * lane;
+        // the tile's first two verbatim groups (if any), one element per lane;
+        // a third and later ones (rare) are loaded when written
+        const uint64_t w1 = word & (word - 1);
+        const uint32_t vg0 = word ? uint32_t(__builtin_ctzll(word)) : 64u;
+        const uint32_t vg1 = w1 ? uint32_t(__builtin_ctzll(w1)) : 64u;
+        uint32_t ve0 = 0, ve1 = 0, vs0 = 0, vs1 = 0;
+        if (MODE != MODE_PAL && word && t * 64 + vg0 < a.G) {
+            ve0 = a.vexp[uint64_t(vbase) * 64 + lane];
+            if (MODE == MODE_FULL) vs0 = a.sm[(t * 64 + vg0) * 64 + lane];
+            if (w1 && t * 64 + vg1 < a.G) {
+                ve1 = a.vexp[uint64_t(vbase + 1) * 64 + lane];
+                if (MODE == MODE_FULL) vs1 = a.sm[(t * 64 + vg1) * 64 + lane];
+            }
+        }
+
+        // stage stream words w0-1 .. w0+nw into buf[0 .. nw+1]: a lead word
+        // (never decisive: the window of bit position p reads words
+        // (p+31)/32 and the next one), the tile, one lookahead word; words
+        // past the tile only ever feed codewords that are discarded
+        const uint32_t w0 = off0 >> 2;
+        const uint32_t nw = off1 > off0 ? ((off1 + 3) >> 2) - w0 : 0;
+        const uint32_t need = min(nw + 2, bw);
+        wave_lds_sync();     // the previous tile's reads of buf and slots are done
+        auto stage = [&](uint32_t base) {
+            u32x4_t v[kStageRounds];
+#pragma unroll
+            for (int r = 0; r < kStageRounds; ++r) {
+                const int64_t wi = int64_t(w0) - 1 + base + 256 * r + 4 * lane;
+                const bool fast = vec_ok && wi >= 0 && uint64_t(wi) * 4 + 16 <= a.stream_bytes;
+                // no access at all for lanes past the stream (it may be empty and NULL)
+                v[r] = fast ? *reinterpret_cast<const u32x4_a4*>(a.stream + uint64_t(wi) * 4) : u32x4_t{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int r = 0; r < kStageRounds; ++r) {
+                const uint32_t i = base + 256 * r + 4 * lane;
+                if (i < need) {
+                    const int64_t wi = int64_t(w0) - 1 + i;
+                    if (!(vec_ok && wi >= 0 && uint64_t(wi) * 4 + 16 <= a.stream_bytes)) {   // stream ends
+#pragma unroll 1
+                        for (int k = 0; k < 4; ++k) v[r][k] = load_word_any(a.stream, wi + k, a.stream_bytes);
+                    }
+                    *reinterpret_cast<u32x4_t*>(buf + i) =
+                        u32x4_t{bswap32(v[r][0]), bswap32(v[r][1]), bswap32(v[r][2]), bswap32(v[r][3])};
+                }
+            }
+        };
+        // one pass covers 4 KiB, every tile of these codes; longer ones loop
+        stage(0);
+        for (uint32_t base = 256 * kStageRounds; base < need; base += 256 * kStageRounds) stage(base);
+        wave_lds_sync();
+
         uint32_t incl = gl;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             uint32_t v = __shfl_up(incl, d, 64);
             if (lane >= d) incl += v;
         }
-        const uint32_t start = incl - gl + ((off0 & 3u) << 3);
-        const bool verb = (word >> lane) & 1ull;
 
-        if (gvalid && !verb) {
-            uint32_t wp = start >> 5;
-            const uint32_t sh = start & 31;
-            uint64_t win = (uint64_t(bswap32(buf[min(wp, lim)])) << 32) | bswap32(buf[min(wp + 1, lim)]);
-            win <<= sh;
-            int avail = 64 - int(sh);
-            wp += 2;
-            uint32_t nib[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < 64; ++j) {
-                if (avail < 32) {
-                    win |= uint64_t(bswap32(buf[min(wp, lim)])) << (32 - avail);
-                    ++wp;
-                    avail += 32;
-                }
-                const uint32_t ent = lutb[uint32_t(win >> rs)];
-                const uint32_t len = ent & 15u;
-                nib[j >> 3] |= (ent >> 4) << (4 * (j & 7));
-                win <<= len;
-                avail -= int(len);
+        // q = 31 + bit position from buf[1]; nc4 = 4 x symbols decoded (256 = done)
+        uint32_t q = incl - gl + ((off0 & 3u) << 3) + 31;
+        uint32_t nc4 = (gvalid && !verb && lmax > 0) ? 0u : 256u;
+        uint32_t oa = slots_a + lane * (kSlot * 4);
+        uint64_t acc = 0;
+        while (nc4 < 256u) {
+            const uint32_t wa = buf_a + min(q >> 5, lim) * 4;
+            const uint32_t win = __builtin_amdgcn_alignbit(lds_ld(wa), lds_ld(wa + 4), ~q);
+            uint32_t e = lds_ld((win >> 18) & 0x3FFCu);
+            if (e == 0) {                   // first codeword longer than 12 bits
+                const uint32_t d = a.dlut[win >> fb_shift];
+                e = (d & 15u) | (4u << 8) | ((d >> 4) << 16);
             }
-            if (MODE == MODE_PAL) {
-                uint8_t* o = static_cast<uint8_t*>(a.out) + g * 32;
-                store16(o, u32x4_t{nib[0], nib[1], nib[2], nib[3]});
-                store16(o + 16, u32x4_t{nib[4], nib[5], nib[6], nib[7]});
-            } else if (MODE == MODE_EXP) {
-                uint8_t* o = static_cast<uint8_t*>(a.out) + g * 64;
+            q += e & 0xFFu;
+            acc |= uint64_t(e >> 16) << (nc4 & 31u);
+            lds_st(oa, uint32_t(acc));
+            lds_st(oa + 4, uint32_t(acc >> 32));
+            const uint32_t nn = nc4 + ((e >> 8) & 0xFFu);
+            const uint32_t c = (nn ^ nc4) & 32u;   // a word of 8 nibbles completed
+            acc >>= c;
+            oa += c >> 3;
+            nc4 = nn;
+        }
+
+        if (MODE == MODE_PAL) {
+            // own slot: 32 contiguous bytes per lane
+            if (gvalid) {
+                const uint32_t sa = slots_a + lane * (kSlot * 4);
+                uint32_t nib[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t d[4];
+                for (int k = 0; k < 8; ++k) nib[k] = verb ? 0u : lds_ld(sa + 4 * k);
+                uint8_t* out = static_cast<uint8_t*>(a.out) + g * 32;
+                store16(out, u32x4_t{nib[0], nib[1], nib[2], nib[3]});
+                store16(out + 16, u32x4_t{nib[4], nib[5], nib[6], nib[7]});
+            }
+        } else {
+            wave_lds_sync();     // slots are read across lanes
+            // sign/mantissa bytes of the lane's elements (loaded here rather
+            // than before the decode loop: keeps the kernel within 80 VGPRs,
+            // 6 waves per SIMD)
+            u32x2_t smv[8];
+            if (MODE == MODE_FULL) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int k = q * 8 + i * 2;   // nibble-pair bytes k, k+1
-                        const uint32_t b0 = (nib[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                        const uint32_t b1 = (nib[(k + 1) >> 2] >> (8 * ((k + 1) & 3))) & 0xFFu;
-                        d[i] = ptab[b0] | (ptab[b1] << 16);
-                    }
-                    store16(o + 16 * q, u32x4_t{d[0], d[1], d[2], d[3]});
-                }
-            } else {
-                const uint8_t* smg = a.sm + g * 64;
-                uint16_t* o = static_cast<uint16_t*>(a.out) + g * 64;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const u32x4_t s4 = load_stream16(smg + 16 * q);
-                    uint32_t d[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const int k = q * 8 + i;       // nibble-pair byte k = elements 2k, 2k+1
-                        const uint32_t nb = (nib[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-                        d[i] = (i & 1) ? join_pair<1>(s4[i >> 1], ptab[nb]) : join_pair<0>(s4[i >> 1], ptab[nb]);
-                    }
-                    store16(o + 16 * q, u32x4_t{d[0], d[1], d[2], d[3]});
-                    store16(o + 16 * q + 8, u32x4_t{d[4], d[5], d[6], d[7]});
+                for (int k = 0; k < 8; ++k) {
+                    const int64_t e = e0 + 512 * k;
+                    smv[k] = load_stream8(a.sm + (e < N ? e : 0));
                 }
             }
-        } else if (gvalid) {
-            const uint32_t slot = verbatim_slot(word, uint32_t(lane), vbase);
-            const uint8_t* vx = a.vexp + uint64_t(slot) * 64;
-            if (MODE == MODE_PAL) {
-                uint8_t* o = static_cast<uint8_t*>(a.out) + g * 32;
-                store16(o, u32x4_t{0, 0, 0, 0});
-                store16(o + 16, u32x4_t{0, 0, 0, 0});
-            } else if (MODE == MODE_EXP) {
-                uint8_t* o = static_cast<uint8_t*>(a.out) + g * 64;
+            // non-verbatim groups: 8 elements per lane, 512 per instruction
 #pragma unroll
-                for (int q = 0; q < 4; ++q) store16(o + 16 * q, load16(vx + 16 * q));
-            } else {
-                const uint8_t* smg = a.sm + g * 64;
-                uint16_t* o = static_cast<uint16_t*>(a.out) + g * 64;
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t gi = 8 * k + (lane >> 3);
+                const int64_t e = e0 + 512 * k;
+                if (e >= N || ((word >> gi) & 1ull)) continue;
+                const uint32_t nw32 = lds_ld(slots_a + gi * (kSlot * 4) + 4 * (lane & 7));
+                uint32_t pr[4];     // ptab entries of the 4 nibble pairs
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const u32x4_t s4 = load_stream16(smg + 16 * q);
-                    const u32x4_t e4 = load16(vx + 16 * q);
-                    uint32_t d[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        d[i] = (i & 1) ? join_pair<1>(s4[i >> 1], exp_pair<1>(e4[i >> 1]))
-                                       : join_pair<0>(s4[i >> 1], exp_pair<0>(e4[i >> 1]));
-                    store16(o + 16 * q, u32x4_t{d[0], d[1], d[2], d[3]});
-                    store16(o + 16 * q + 8, u32x4_t{d[4], d[5], d[6], d[7]});
+                for (int i = 0; i < 4; ++i) pr[i] = lds_ld(ptab_a + ((nw32 >> (8 * i)) & 0xFFu) * 4);
+                if (MODE == MODE_EXP) {
+                    *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.out) + e) =
+                        u32x2_t{pr[0] | (pr[1] << 16), pr[2] | (pr[3] << 16)};
+                } else {
+                    const u32x2_t s8 = smv[k];
+                    store16(static_cast<uint16_t*>(a.out) + e,
+                            u32x4_t{join_pair<0>(s8[0], pr[0]), join_pair<1>(s8[0], pr[1]),
+                                    join_pair<0>(s8[1], pr[2]), join_pair<1>(s8[1], pr[3])});
                 }
+            }
+            // verbatim groups: the whole wave writes one group, lane = element
+            uint64_t rest = word;
+            for (uint32_t r = 0; rest; ++r, rest &= rest - 1) {
+                const uint32_t gi = uint32_t(__builtin_ctzll(rest));
+                if (t * 64 + gi >= a.G) break;       // bits past the last group (invalid input)
+                const int64_t e = (t * 64 + gi) * 64 + lane;
+                uint32_t ev, sv = 0;
+                if (r == 0) {
+                    ev = ve0;
+                    sv = vs0;
+                } else if (r == 1) {
+                    ev = ve1;
+                    sv = vs1;
+                } else {
+                    ev = a.vexp[uint64_t(vbase + r) * 64 + lane];
+                    if (MODE == MODE_FULL) sv = a.sm[e];
+                }
+                if (MODE == MODE_EXP) static_cast<uint8_t*>(a.out)[e] = uint8_t(ev);
+                else static_cast<uint16_t*>(a.out)[e] = uint16_t(((sv & 0x80u) << 8) | (ev << 7) | (sv & 0x7Fu));
             }
         }
-        __syncthreads();
     }
 }
 
 }  // namespace
 
-size_t decode_lds_bytes(int lmax, int* buf_words) {
-    // a tile holds at most 64 groups x 64 codes x lmax bits = 512*lmax bytes;
-    // +1 word for a misaligned start, +2 zero words for the lookahead window
-    const int bw = 128 * (lmax > 0 ? lmax : 1) + 4;
+size_t decode_lds_bytes(int lmax, uint32_t max_tile_bytes, int* buf_words) {
+    // the longest tile, +1 word for a misaligned start, the lead word, one
+    // lookahead word, rounded to whole 16-byte rows
+    (void)lmax;
+    const int bw = ((int(max_tile_bytes) + 3) / 4 + 3 + 3) & ~3;
     if (buf_words) *buf_words = bw;
-    const size_t lut_words = ((size_t(1) << lmax) + 3) / 4;
-    return (lut_words + 256 + size_t(kDecWaves) * bw) * 4;
+    return (size_t(kMlutEntries) + 256 + size_t(kDecWaves) * (bw + 64 * kSlot)) * 4;
 }
 
 hipError_t launch_decode(int mode, const DecodeArgs& a0, hipStream_t s) {
     DecodeArgs a = a0;
-    const size_t lds = decode_lds_bytes(a.lmax, &a.buf_words);
-    const int64_t blocks = (a.T + kDecWaves - 1) / kDecWaves;
-    const unsigned grid = unsigned(blocks < 1024 ? (blocks > 0 ? blocks : 1) : 1024);
+    const size_t lds = decode_lds_bytes(a.lmax, a.max_tile_bytes, &a.buf_words);
     if (a.T == 0) return hipSuccess;
+    // persistent grid: as many workgroups as fit on the chip at once (LDS
+    // and 2048 threads per CU), each looping over tiles
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int per_cu = std::max(1, std::min(2048 / (64 * kDecWaves), int((160u * 1024u) / lds)));
+    const int64_t blocks = (a.T + kDecWaves - 1) / kDecWaves;
+    const unsigned grid = unsigned(std::max<int64_t>(1, std::min<int64_t>(blocks, int64_t(cus) * per_cu)));
+    const dim3 block(64 * kDecWaves);
     switch (mode) {
-        case MODE_FULL: decode_kernel<MODE_FULL><<<grid, 256, lds, s>>>(a); break;
-        case MODE_EXP: decode_kernel<MODE_EXP><<<grid, 256, lds, s>>>(a); break;
-        default: decode_kernel<MODE_PAL><<<grid, 256, lds, s>>>(a); break;
+        case MODE_FULL: decode_kernel<MODE_FULL><<<grid, block, lds, s>>>(a); break;
+        case MODE_EXP: decode_kernel<MODE_EXP><<<grid, block, lds, s>>>(a); break;
+        default: decode_kernel<MODE_PAL><<<grid, block, lds, s>>>(a); break;
     }
     return hipGetLastError();
 }

@@ -19,7 +19,9 @@ struct DecodeArgs {
     const uint8_t* vexp;
     const uint64_t* bitmap;
     const uint8_t* dlut;
+    const uint32_t* mlut;
     uint64_t stream_bytes;
+    uint32_t max_tile_bytes;
     int64_t G, T;
     int32_t lmax;
     int32_t buf_words;   // LDS dwords per wave for one staged tile stream
@@ -55,7 +57,7 @@ bool mfma_gemv_supported(const MatArgs& a);
 hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, uint16_t* h, hipStream_t s);
 
 // LDS bytes the decoder needs for a code of longest length lmax.
-size_t decode_lds_bytes(int lmax, int* buf_words);
+size_t decode_lds_bytes(int lmax, uint32_t max_tile_bytes, int* buf_words);
 
 // Kernel timer: while enabled, each matmul kernel launch takes the next
 // (start, stop) event pair, recorded by the launch itself around the kernel.

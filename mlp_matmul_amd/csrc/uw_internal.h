@@ -31,6 +31,7 @@ struct uw_blob {
     uint64_t hist[256] = {};
     bool has_nib = false;
     std::vector<uint8_t> sm, stream, vexp, nib, dlut;
+    std::vector<uint32_t> mlut;
     std::vector<uint16_t> glen;
     std::vector<uint32_t> tile_off, tile_vbase;
     std::vector<uint64_t> bitmap;
@@ -41,6 +42,10 @@ namespace uw {
 void canonical_codes(const uint8_t lengths[16], uint16_t codes[16]);
 // Decode table of 2^lmax entries: (symbol << 4) | length.
 void build_dlut(uw_blob& b);
+// Multi-symbol table over 12-bit strings (layout in unweight.h), built from
+// the decode table; requires build_dlut first.
+constexpr int kMlutBits = 12;
+void build_mlut(uw_blob& b);
 // Direct-palette nibbles from the exponent of every element.
 void build_nibbles(uw_blob& b, const uint8_t* e, int threads);
 }  // namespace uw

@@ -37,8 +37,47 @@ def _same_as_oracle(w, threads=0):
         covered = llen > 0
         assert np.array_equal(dl[covered] >> 4, lsym[covered])
         assert np.array_equal(dl[covered] & 15, llen[covered])
+    _check_multi_symbol_table(b.section("mlut"), lsym, llen, lmax)
     b.validate()
     return b, ref
+
+
+def _check_multi_symbol_table(ml, lsym, llen, lmax):
+    """Entry v of the 12-bit multi-symbol table must hold exactly the codewords
+    that the oracle's one-codeword table decodes one after another from the
+    string v while each lies wholly inside it, at most four: their total
+    length (bits 0-7), four times their count (bits 8-15) and their symbols
+    (4 bits each from bit 16).  Strings the oracle's table does not cover
+    (possible only with one coded symbol) are checked up to that point."""
+    assert ml.dtype == np.uint32 and ml.size == 4096
+    if lmax == 0:
+        assert not ml.any()
+        return
+    v = np.arange(4096, dtype=np.int64)
+    used = np.zeros_like(v)
+    n = np.zeros_like(v)
+    syms = np.zeros_like(v)
+    alive = np.ones(v.size, bool)
+    covered = np.ones(v.size, bool)
+    for _ in range(4):
+        rest = (v << used) & 0xFFF
+        idx = rest >> (12 - lmax) if lmax <= 12 else rest << (lmax - 12)
+        ln = llen[idx]
+        covered &= ~(alive & (ln == 0))
+        take = alive & (ln > 0) & (used + ln <= 12)
+        syms = np.where(take, syms | (lsym[idx] << (16 + 4 * n)), syms)
+        used = np.where(take, used + ln, used)
+        n = np.where(take, n + 1, n)
+        alive &= take
+    got = ml.astype(np.int64)
+    assert np.array_equal(got[covered], (used | (4 * n) << 8 | syms)[covered])
+    # uncovered strings: the symbols decoded before the gap agree
+    keep = (1 << 16) * ((1 << (4 * n)) - 1)
+    assert ((got >> 8 & 0xFF)[~covered] >= 4 * n[~covered]).all()
+    assert np.array_equal((got & keep)[~covered], syms[~covered])
+    # with two or more coded symbols the code is complete: every string decodes
+    if (llen > 0).any() and len(set(lsym[llen > 0].tolist())) >= 2:
+        assert covered.all()
 
 
 def test_small_workload_identical():
@@ -115,6 +154,7 @@ def test_serialize_roundtrip_and_add_palette():
     for name in SEC:
         assert np.array_equal(b.section(name), b2.section(name)), name
     assert np.array_equal(b.section("dlut"), b2.section("dlut"))
+    assert np.array_equal(b.section("mlut"), b2.section("mlut"))
     b2.add_palette()
     assert np.array_equal(b2.section("nib"), codec.encode(w).nib)
     b3 = uw.Blob.deserialize(b2.serialize())
