@@ -62,7 +62,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
-// LDS word at a byte address (the tables start at LDS address 0)
+// LDS word at a byte address
 __device__ __forceinline__ uint32_t lds_ld(uint32_t addr) {
     return *reinterpret_cast<const lds_u32*>(static_cast<uintptr_t>(addr));
 }
@@ -82,13 +82,24 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile metadata in scalar loads
     const int lmax = a.lmax;
     const uint32_t bw = uint32_t(a.buf_words);   // multiple of 4
-    uint32_t* mlut = lds;                        // multi-symbol table at LDS address 0
-    uint32_t* ptab = lds + kMlutEntries;         // 256 entries indexed by a nibble pair
-    uint32_t* buf = ptab + 256 + wave * (bw + 64 * kSlot);
-    // byte addresses: the wave's stream buffer, its 64 symbol slots
-    const uint32_t buf_a = __builtin_amdgcn_readfirstlane(uint32_t((kMlutEntries + 256 + wave * (bw + 64 * kSlot)) * 4));
+    // LDS: the multi-symbol table (at address 0) and the nibble-pair table
+    // shared by the workgroup, then per wave [stream buffer | 64 symbol slots]
+    const uint32_t wave_words = bw + 64 * kSlot;
+    uint32_t* mlut = lds;
+    uint32_t* ptab = lds + kMlutEntries;
+    uint32_t* buf = ptab + 256 + wave * wave_words;
+    // byte addresses; the empty asm keeps the wave's base one opaque scalar
+    // so that each window read needs a single address instruction
+    uint32_t buf_a = uint32_t((kMlutEntries + 256 + wave * wave_words) * 4);
+    asm("" : "+s"(buf_a));
     const uint32_t slots_a = buf_a + bw * 4;
     const uint32_t ptab_a = kMlutEntries * 4;
+
+    const uint32_t lim = bw - 2;
+    const int fb_shift = 32 - (lmax > 0 ? lmax : 1);
+    const bool vec_ok = a.stream_bytes >= 16;
+    const int64_t N = a.G * 64;
+    const int64_t S = int64_t(gridDim.x) * kDecWaves;     // tile stride of a wave
 
     for (int i = tid; i < kMlutEntries / 4; i += 64 * kDecWaves)
         reinterpret_cast<u32x4_t*>(mlut)[i] = reinterpret_cast<const u32x4_t*>(a.mlut)[i];
@@ -98,13 +109,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
         ptab[tid] = MODE == MODE_FULL ? (lo << 7) | (hi << 23) : lo | (hi << 8);
     }
     __syncthreads();
-    const uint32_t lim = bw - 2;
-    const int fb_shift = 32 - (lmax > 0 ? lmax : 1);
-    const bool vec_ok = a.stream_bytes >= 16;
-    const int64_t N = a.G * 64;
 
     // waves take tiles independently (no workgroup barrier in the loop)
-    for (int64_t t = int64_t(blockIdx.x) * kDecWaves + wave; t < a.T; t += int64_t(gridDim.x) * kDecWaves) {
+    for (int64_t t = int64_t(blockIdx.x) * kDecWaves + wave; t < a.T; t += S) {
         const uint32_t off0 = a.tile_off[t], off1 = a.tile_off[t + 1], vbase = a.tile_vbase[t];
         const uint64_t word = a.bitmap[t];
         const int64_t g = t * 64 + lane;
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
         while (nc4 < 256u) {
             const uint32_t wa = buf_a + min(q >> 5, lim) * 4;
             const uint32_t win = __builtin_amdgcn_alignbit(lds_ld(wa), lds_ld(wa + 4), ~q);
-            uint32_t e = lds_ld((win >> 18) & 0x3FFCu);
+            uint32_t e = lds_ld((win >> 18) & 0x3FFCu);      // table entry win>>20
             if (e == 0) {                   // first codeword longer than 12 bits
                 const uint32_t d = a.dlut[win >> fb_shift];
                 e = (d & 15u) | (4u << 8) | ((d >> 4) << 16);
