@@ -197,16 +197,24 @@ int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_S
 /* Pipeline 1 preprocessing ("Four ways to use compressed weights", full
  * Huffman decode): rebuild every bf16 weight into out_bf16 [rows, cols].
  * One wavefront per 64-group tile; lanes find their group's first bit by a
- * prefix sum of GLEN; the tile's stream and the decode table sit in LDS. */
+ * prefix sum of GLEN and decode up to four codewords per lookup of MLUT; the
+ * tile's stream and MLUT sit in LDS, the stream buffer sized by the
+ * descriptor's max_tile_bytes.  UW_EINVAL when a section the decoder reads is
+ * NULL, a section or the output is not 16-byte aligned, or max_tile_bytes is
+ * 0 for a nonempty stream or above 512*lmax+1 (no tile of lmax-bit codes is
+ * longer).  A STREAM whose tiles exceed max_tile_bytes decodes wrongly but
+ * is never read or written out of bounds. */
 int uw_decode_full(const uw_dmat* d, uint16_t* out_bf16, void* stream);
 
 /* Pipeline 2 preprocessing (exponent-only decode): the exponent byte of every
- * weight, verbatim groups included, into out_e [rows, cols] uint8. */
+ * weight, verbatim groups included, into out_e [rows, cols] uint8.  Same
+ * decoder, layout rules and errors as uw_decode_full (SM is not read). */
 int uw_decode_exponents(const uw_dmat* d, uint8_t* out_e, void* stream);
 
 /* Pipeline 3 preprocessing (palette transcode), also the load-time producer of
  * pipeline 4's form: 4-bit palette indices into out_nib [rows*cols/2], byte
- * layout of the NIB section (0 in verbatim groups). */
+ * layout of the NIB section (0 in verbatim groups).  Same decoder, layout
+ * rules and errors as uw_decode_full (SM is not read). */
 int uw_transcode_palette(const uw_dmat* d, uint8_t* out_nib, void* stream);
 
 /* ---------------------------------------------------------------- matmuls */

@@ -352,8 +352,22 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
     const int wpg = env_int("UW_MFMA_WPG", a.B > 128 ? 8 : 4);
     const int pd = env_int("UW_MFMA_PD", 1);
     if (rbw <= 2) {
-        if (wpg <= 4) return nb <= 4 ? launch_cfg<SRC, 4, 1, 2, 4>(a, s) : launch_cfg<SRC, 8, 1, 2, 4>(a, s);
-        return nb <= 4 ? launch_cfg<SRC, 4, 1, 2, 8>(a, s) : launch_cfg<SRC, 8, 1, 2, 8>(a, s);
+        if (wpg <= 4) {
+            if (nb <= 4) {
+                if (pd <= 1) return launch_cfg<SRC, 4, 1, 2, 4>(a, s);
+                if (pd == 2) return launch_cfg<SRC, 4, 2, 2, 4>(a, s);
+                return launch_cfg<SRC, 4, 3, 2, 4>(a, s);
+            }
+            if (pd <= 1) return launch_cfg<SRC, 8, 1, 2, 4>(a, s);
+            return launch_cfg<SRC, 8, 2, 2, 4>(a, s);
+        }
+        if (nb <= 4) {
+            if (pd <= 1) return launch_cfg<SRC, 4, 1, 2, 8>(a, s);
+            if (pd == 2) return launch_cfg<SRC, 4, 2, 2, 8>(a, s);
+            return launch_cfg<SRC, 4, 3, 2, 8>(a, s);
+        }
+        if (pd <= 1) return launch_cfg<SRC, 8, 1, 2, 8>(a, s);
+        return launch_cfg<SRC, 8, 2, 2, 8>(a, s);
     }
     if (nb <= 4) {
         if (pd <= 1) return launch_cfg<SRC, 4, 1, 4, 4>(a, s);

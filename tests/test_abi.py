@@ -51,3 +51,38 @@ def test_no_fallback_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(_capi, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         _capi.lib()
+
+
+def _fake_dmat(blob, drop=(), **override):
+    """A descriptor whose device pointers are aligned placeholders: the calls
+    below must reject it during argument checks, before any launch."""
+    import ctypes as ct
+    info = blob.info()
+    ptrs = (ct.c_void_p * _capi.UW_NUM_SECTIONS)()
+    for i, name in enumerate(_capi.SECTION_NAMES):
+        if name not in drop:
+            ptrs[i] = 0x10000 * (i + 1)
+    d = _capi.uw_dmat()
+    assert uw.lib().uw_dmat_init(ct.byref(d), ct.byref(info), ptrs) == 0
+    for k, v in override.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_decoders_check_descriptors_before_launch():
+    import ctypes as ct
+    import workloads
+    L = uw.lib()
+    b = uw.compress(workloads.small_matrix()[0])
+    inf = b.info()
+    assert 0 < inf.max_tile_bytes <= 512 * inf.lmax
+    # the multi-symbol table is required by every decoder
+    d = _fake_dmat(b, drop=("mlut",))
+    assert L.uw_transcode_palette(ct.byref(d), ct.c_void_p(0x100000), None) == _capi.UW_EINVAL
+    assert b"NULL" in L.uw_last_error()
+    # a longest-tile size no tile of lmax-bit codes can reach sizes no LDS buffer
+    d = _fake_dmat(b, max_tile_bytes=512 * inf.lmax + 2)
+    assert L.uw_decode_full(ct.byref(d), ct.c_void_p(0x100000), None) == _capi.UW_EINVAL
+    assert b"max_tile_bytes" in L.uw_last_error()
+    d = _fake_dmat(b, max_tile_bytes=0)
+    assert L.uw_decode_exponents(ct.byref(d), ct.c_void_p(0x100000), None) == _capi.UW_EINVAL
