@@ -182,14 +182,10 @@ void mfma_kernel(MatArgs a, int tiles_n, int split) {
         for (int nb = 0; nb < NB; ++nb) acc[rb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](uint32_t buf, const Step<SRC, NB, RBW, WPG>& st) {
-        // B fragments of the step: batch block nb, substep sub (8 columns)
-        bf16x8_t Bf[2][NB];
-        const uint16_t* xb = &xs[buf][rl * kXST + 16u * q];
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                Bf[sub][nb] = *reinterpret_cast<const bf16x8_t*>(xb + nb * 16 * kXST + 8 * sub);
+        // A operands of every row block first, then per substep (8 K columns)
+        // the NB activation fragments and their MFMAs: only one substep's
+        // fragments are live, which leaves registers for deeper prefetch
+        bf16x8_t Asub[kRBW][2];
 #pragma unroll
         for (int rb = 0; rb < kRBW; ++rb) {
             const AStep<SRC>& f = st.r[rb];
@@ -220,15 +216,23 @@ void mfma_kernel(MatArgs a, int tiles_n, int split) {
                 for (int p = 0; p < 8; ++p)
                     w[p] = (p & 1) ? join_pair<1>(f.sm[p >> 1], e7[p]) : join_pair<0>(f.sm[p >> 1], e7[p]);
             }
-            const bf16x8_t Asub[2] = {__builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]}),
-                                      __builtin_bit_cast(bf16x8_t, u32x4_t{w[4], w[5], w[6], w[7]})};
-            // substep outer: consecutive MFMAs update different accumulators
-            // (a dependent pair back to back waits out the MFMA latency)
+            Asub[rb][0] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[0], w[1], w[2], w[3]});
+            Asub[rb][1] = __builtin_bit_cast(bf16x8_t, u32x4_t{w[4], w[5], w[6], w[7]});
+        }
+        const uint16_t* xb = &xs[buf][rl * kXST + 16u * q];
 #pragma unroll
-            for (int sub = 0; sub < 2; ++sub)
+        for (int sub = 0; sub < 2; ++sub) {
+            bf16x8_t Bf[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                Bf[nb] = *reinterpret_cast<const bf16x8_t*>(xb + nb * 16 * kXST + 8 * sub);
+            // consecutive MFMAs update different accumulators (a dependent
+            // pair back to back waits out the MFMA latency)
+#pragma unroll
+            for (int rb = 0; rb < kRBW; ++rb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Asub[sub], Bf[sub][nb], acc[rb][nb], 0, 0, 0);
+                    acc[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Asub[rb][sub], Bf[nb], acc[rb][nb], 0, 0, 0);
         }
     };
 
@@ -341,16 +345,17 @@ int env_int(const char* name, int dflt) {
 }
 
 // Batch blocks per workgroup (4 up to batch 64, else 8), row blocks per
-// wave (2), waves per workgroup (4, 8 above batch 128) and prefetch depth
-// (1), as measured on the Llama MLP shapes at batch 64-256; UW_MFMA_NB /
-// _RBW / _WPG / _PD override for tuning.  Combinations that do not fit the register file
-// are never instantiated.
+// wave (2), waves per workgroup (8 above batch 128 for matrices under 8192
+// rows, else 4) and prefetch depth (3 for the 4-block tiles of the
+// rebuilding sources, else 1), as measured on the Llama MLP shapes at batch
+// 32-256; UW_MFMA_NB / _RBW / _WPG / _PD override for tuning.  Combinations
+// that do not fit the register file are never instantiated.
 template <int SRC>
 hipError_t launch_src(const MatArgs& a, hipStream_t s) {
     const int nb = env_int("UW_MFMA_NB", a.B <= 64 ? 4 : 8);
     const int rbw = env_int("UW_MFMA_RBW", 2);
-    const int wpg = env_int("UW_MFMA_WPG", a.B > 128 ? 8 : 4);
-    const int pd = env_int("UW_MFMA_PD", 1);
+    const int wpg = env_int("UW_MFMA_WPG", a.B > 128 && a.R < 8192 ? 8 : 4);
+    const int pd = env_int("UW_MFMA_PD", nb <= 4 && SRC != SRC_BF16 ? 3 : 1);
     if (rbw <= 2) {
         if (wpg <= 4) {
             if (nb <= 4) {
