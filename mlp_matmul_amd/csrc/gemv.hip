@@ -68,7 +68,7 @@ struct Chunk {
 // the up matrix (up), over the same staged activations; the second group's
 // epilogue writes h[b][r] = bf16(SiLU(g) * u), and g and u themselves when
 // a.Y / up.Y are not null.
-template <int SRC, int MB, int NRW, bool EXACT, bool XLDS, bool DUAL>
+template <int SRC, int MB, int NRW, bool EXACT, bool XLDS, bool DUAL, int DEPTH>
 __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16_t* H) {
     __shared__ uint32_t lut[DUAL ? 512 : 256];                   // nibble pair -> exponents in place
     extern __shared__ uint32_t lds[];
@@ -225,15 +225,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16
     };
 
     auto next = [&](Item it) { return it.s + 1 == iters ? Item{it.g + 1, 0} : Item{it.g, it.s + 1}; };
-    Chunk<SRC, MB> set0[NRW], set1[NRW];
+    Chunk<SRC, MB> sets[DEPTH + 1][NRW];
     const Item it0{0, 0};
     // item 0's weight loads go out first; the verbatim tables of every tile
     // the wave's rows touch (one per lane) follow, then item 0's verbatim
     // loads, then the activations are staged.  (Issuing item 1 here as well,
     // ahead of the staging, measured slower.)
     if (live) {
-        issue_x(it0, set0);
-        issue_w(it0, set0);
+        issue_x(it0, sets[0]);
+        issue_w(it0, sets[0]);
         if (SRC == SRC_PAL) {
             const int64_t t_end = max(((rl0 + wrows) * C + 4095) >> 12, t_first + 1);
             const int64_t tl = min(t_first + lane, t_end - 1);
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16
                 my_vbase1 = up.tile_vbase[tl];
             }
         }
-        issue_v(it0, set0);
+        issue_v(it0, sets[0]);
     }
     if (XLDS) {
         const int64_t n16 = int64_t(B) * C / 8;
@@ -365,28 +365,38 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16
         }
     };
 
-    // ping-pong over two register sets: the loads of item t+1 are issued
-    // before item t is computed.  Past the end the last item is re-issued (an
-    // L2 hit) so the body has no conditional load; the body holds both halves
-    // with no exit between them (an odd last item is computed after the
-    // loop): a mid-body exit lets the compiler fold the two identical halves
-    // into one with register copies, which must wait for every load in flight.
-    int t = 0;
-    Item i0 = it0;
-    for (; t + 1 < total; t += 2) {
-        const Item i1 = next(i0);
-        const Item i2 = t + 2 < total ? next(i1) : i1;
-        issue(i1, set1);
-        compute(i0, set0);
-        finish(i0);
-        issue(i2, set0);
-        compute(i1, set1);
-        finish(i1);
-        i0 = i2;
+    // a ring of DEPTH+1 register sets: the loads of item t+DEPTH are issued
+    // before item t is computed (DEPTH 2 keeps two items in flight, for long
+    // rows).  Items past the end read the wave's first row again (cache hits),
+    // so no load is conditional; the body holds all DEPTH+1 steps with no exit
+    // between them (leftover items are computed after the loop): a mid-body
+    // exit lets the compiler fold identical steps into one with register
+    // copies, which must wait for every load in flight.
+    constexpr int NS = DEPTH + 1;
+    Item ring[NS];
+    ring[0] = it0;
+#pragma unroll
+    for (int j = 1; j < DEPTH; ++j) {
+        ring[j] = next(ring[j - 1]);
+        issue(ring[j], sets[j]);
     }
-    if (t < total) {
-        compute(i0, set0);
-        finish(i0);
+    int t = 0;
+    for (; t + NS - 1 < total; t += NS) {
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            const int jn = (j + DEPTH) % NS;
+            ring[jn] = next(ring[(j + DEPTH - 1) % NS]);
+            issue(ring[jn], sets[jn]);
+            compute(ring[j], sets[j]);
+            finish(ring[j]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j) {
+        if (t + j < total) {
+            compute(ring[j], sets[j]);
+            finish(ring[j]);
+        }
     }
 }
 
@@ -416,12 +426,23 @@ void launch_cfg(const MatArgs& a0, hipStream_t s) {
     const int64_t waves = (a.R + int64_t(NRW) * ng - 1) / (int64_t(NRW) * ng);
     const unsigned grid = unsigned((waves + 3) / 4);
     const size_t lds = XLDS ? size_t(a.B * a.C * 2) : 0;
+    // two items in flight per wave at batch 1-2 (measured on MI355X: the
+    // batch-1 fused gate/up launch 32.9 -> 31.4 us); UW_GEMV_DEPTH=1 for one
+    static const int depth_env = env_int("UW_GEMV_DEPTH", 0);
+    const int depth = MB <= 2 ? (depth_env > 0 ? depth_env : 2) : 1;
+    uint16_t* const no_h = nullptr;
+    if (depth >= 2 && MB <= 2) {
+        constexpr int D = MB <= 2 ? 2 : 1;
+        if (a.C % kSlab == 0)
+            launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS, false, D>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
+        else
+            launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS, false, D>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
+        return;
+    }
     if (a.C % kSlab == 0)
-        launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS, false>, dim3(grid), dim3(256), lds, s, a, MatArgs{},
-                     static_cast<uint16_t*>(nullptr));
+        launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS, false, 1>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
     else
-        launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS, false>, dim3(grid), dim3(256), lds, s, a, MatArgs{},
-                     static_cast<uint16_t*>(nullptr));
+        launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS, false, 1>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
 }
 
 template <int SRC, int MB, int NRW>
@@ -467,10 +488,19 @@ void launch_gateup_mb(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream
     a.row_groups = 1;
     const unsigned grid = unsigned((a.R + 3) / 4);
     const size_t lds = size_t(a.B * a.C * 2);
+    static const int depth_env = env_int("UW_GEMV_DEPTH", 0);
+    if ((depth_env == 0 || depth_env >= 2) && MB <= 2) {
+        constexpr int D = MB <= 2 ? 2 : 1;
+        if (a.C % kSlab == 0)
+            launch_timed(gemv_kernel<SRC_PAL, MB, 1, true, true, true, D>, dim3(grid), dim3(256), lds, s, a, u, h);
+        else
+            launch_timed(gemv_kernel<SRC_PAL, MB, 1, false, true, true, D>, dim3(grid), dim3(256), lds, s, a, u, h);
+        return;
+    }
     if (a.C % kSlab == 0)
-        launch_timed(gemv_kernel<SRC_PAL, MB, 1, true, true, true>, dim3(grid), dim3(256), lds, s, a, u, h);
+        launch_timed(gemv_kernel<SRC_PAL, MB, 1, true, true, true, 1>, dim3(grid), dim3(256), lds, s, a, u, h);
     else
-        launch_timed(gemv_kernel<SRC_PAL, MB, 1, false, true, true>, dim3(grid), dim3(256), lds, s, a, u, h);
+        launch_timed(gemv_kernel<SRC_PAL, MB, 1, false, true, true, 1>, dim3(grid), dim3(256), lds, s, a, u, h);
 }
 
 }  // namespace
