@@ -89,6 +89,22 @@ def test_decoders_edge_cases(torch_cuda, case):
     _check_decoders(dm, w)
 
 
+def test_decoders_long_tile(torch_cuda):
+    """A tile whose stream is longer than the 4 KiB the decoders stage in one
+    pass, coded with 13-15-bit codewords (past the 12-bit multi-symbol
+    table): all three decoders stay bit-exact, and so does the reconstructive
+    GEMV that consumes the transcoded nibbles."""
+    print_case("decoders long tile (geometric exponent frequencies)")
+    w = workloads.geometric_exponent_matrix()
+    b = uw.compress(w)
+    assert b.info().max_tile_bytes > 4096 and b.info().lmax == 15
+    dm = b.to_device()
+    _, _, nib = _check_decoders(dm, w)
+    x = workloads.gaussian_activations(np.random.default_rng(3), 1, w.shape[1])
+    Y = uw.gemm_recon_pal(dm, nib, to_dev_bf16(x), kernel=uw.UW_KERNEL_GEMV)
+    assert_matmul_close(Y.cpu().numpy(), w, x, what="long tile: palette transcode + GEMV")
+
+
 @pytest.mark.parametrize("wl,m", [(2, 0), (2, 2), (4, 1), (5, 2)])
 def test_decoders_full_size(torch_cuda, wl, m):
     print_case(f"decoders full size workload {wl} matrix {m}")

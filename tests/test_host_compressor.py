@@ -139,6 +139,16 @@ def test_golden_examples_through_cpp(golden_dir):
         assert b.section("vexp").tobytes().hex() == e["vexp_hex"], name
 
 
+def test_long_tile_identical():
+    """Geometric exponent frequencies give 15-bit codewords and one tile far
+    longer than the average (more than 4 KiB of stream): same bytes as the
+    oracle encoder, and the longest tile is what the blob reports."""
+    b, ref = _same_as_oracle(workloads.geometric_exponent_matrix())
+    inf = b.info()
+    assert inf.lmax == 15 and inf.verbatim_groups == 0
+    assert inf.max_tile_bytes == int(np.diff(ref.tile_off.astype(np.int64)).max()) > 4096
+
+
 def test_rejects_bad_shape():
     with pytest.raises(uw.UnweightError):
         uw.compress(np.zeros((2, 96), np.uint16))

@@ -129,3 +129,32 @@ def layer_activation(workload: int, layer: int, m: int, batch: int, cols=None) -
 def random_bf16_bits(seed: int, n: int) -> np.ndarray:
     """Uniformly random 16-bit patterns: every exponent, NaNs and subnormals."""
     return np.random.default_rng(seed).integers(0, 1 << 16, size=n, dtype=np.uint16)
+
+
+def geometric_exponent_matrix(rows: int = 1024, cols: int = 4096, long_tile: int = 3, seed: int = 12):
+    """bf16 bits whose 16 exponents (110..125) occur with counts N/2, N/4, ...,
+    N/2^15, N/2^15 (N = rows*cols, a power of two), so every exponent is in
+    the top-16 palette and no group is verbatim, and the frequencies are
+    geometric.  Tile ``long_tile`` (4096 consecutive elements) holds only
+    exponents of the ten rarest classes, in proportion to their counts; the
+    rest are shuffled over the other tiles.  Sign and mantissa are uniform.
+    A stress input for stream layout: the rarest classes are the longest
+    codewords, so that tile's stream is much longer than the average tile."""
+    n = rows * cols
+    assert n & (n - 1) == 0 and n >= 1 << 16
+    rng = np.random.default_rng(seed)
+    exps = np.arange(110, 126, dtype=np.int64)
+    counts = np.array([n >> k for k in range(1, 16)] + [n >> 15], dtype=np.int64)
+    rare = np.arange(7, 16)                                   # the nine rarest classes
+    # 4096 elements of the rare classes, drawn without replacement
+    pool = np.repeat(exps[rare], counts[rare])
+    pick = rng.permutation(pool.size)[:4096]
+    tile_e = pool[pick]
+    left = np.concatenate([np.repeat(exps, counts)[np.repeat(np.arange(16), counts) < 7],
+                           np.delete(pool, pick)])
+    left = left[rng.permutation(left.size)]
+    t0 = long_tile * 4096
+    e = np.concatenate([left[:t0], tile_e, left[t0:]])
+    sm = rng.integers(0, 256, size=n, dtype=np.int64)
+    bits = ((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)
+    return bits.astype(np.uint16).reshape(rows, cols)
