@@ -129,7 +129,8 @@ class Step:
         self.h = torch.empty((batch, F), dtype=torch.bfloat16, device="cuda")
         self.y = torch.empty((batch, H), dtype=torch.float32, device="cuda")
         sp = pipe if pipe not in (uw.UW_PIPE_AUTO, uw.UW_PIPE_BF16) else uw.UW_PIPE_FULL
-        nscr = max(uw.scratch_bytes(sp, F, H, batch, 4), uw.scratch_bytes(sp, H, F, batch, 4))
+        nscr = max(uw.scratch_bytes(sp, F, H, batch, 0), uw.scratch_bytes(sp, H, F, batch, 0),
+                   uw.scratch_bytes(sp, F, H, batch, 4), uw.scratch_bytes(sp, H, F, batch, 4))
         self.scratch = torch.empty(nscr, dtype=torch.uint8, device="cuda")
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         L = uw.lib()
@@ -147,11 +148,12 @@ class Step:
                 xin, yout = outs[m]
                 if pipe == uw.UW_PIPE_BF16:
                     R, C = lay.bf16[m].shape
-                    k, sk = (bf16_choice or {}).get((R, C), (0, 1))
+                    k, sk = (bf16_choice or {}).get((R, C), (0, 0))
                     row.append(functools.partial(L.uw_gemm_bf16, P(lay.bf16[m]), R, C, xin, batch, yout, k, sk,
                                                  scr, nsc, st))
                 else:
-                    row.append(functools.partial(L.uw_matmul, ct.byref(lay.mats[m].dmat), pipe, 0, 1, xin,
+                    # kernel and split-K: the plan's (AUTO) or the library's choice
+                    row.append(functools.partial(L.uw_matmul, ct.byref(lay.mats[m].dmat), pipe, 0, 0, xin,
                                                  batch, yout, scr, nsc, st))
             silu = functools.partial(L.uw_silu_mul_bf16, P(self.g), P(self.u), batch * F, P(self.h), st)
             self.fused = (fuse and batch <= 4 and batch * H * 2 <= 32768

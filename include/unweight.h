@@ -220,9 +220,9 @@ int uw_transcode_palette(const uw_dmat* d, uint8_t* out_nib, void* stream);
 /* ---------------------------------------------------------------- matmuls */
 /* Kernel family selector for the matmuls (the autotuner's search space). */
 enum {
-    UW_KERNEL_AUTO = 0,    /* GEMV below batch 4, SKINNY up to 64 (when supported), MFMA above */
+    UW_KERNEL_AUTO = 0,    /* GEMV below batch 4, SKINNY up to 16 (when supported), MFMA above */
     UW_KERNEL_GEMV = 1,    /* wavefront-reduction GEMV (v_dot2 bf16), batch <= 16 */
-    UW_KERNEL_MFMA = 2,    /* bf16 MFMA, 64 rows x 64 or 128 batch columns per wave, any batch; cols <= 65536 */
+    UW_KERNEL_MFMA = 2,    /* bf16 MFMA, 32 rows x 64 or 128 batch columns per wave, any batch; cols <= 65536 */
     UW_KERNEL_SKINNY = 3   /* bf16 MFMA, 16 rows x one K-slice per wave, batch tiles of <= 64;
                               needs cols % 128 == 0 and cols <= 32768 (else UW_EUNSUPPORTED) */
 };
@@ -232,7 +232,10 @@ enum {
  * Y[batch, rows] = X[batch, cols] . W[rows, cols]^T, fp32 accumulate.
  * `kernel` is a UW_KERNEL_* value; split_k > 1 (MFMA only) needs
  * uw_scratch_bytes(UW_PIPE_BF16, ...) bytes of scratch, else scratch may be
- * NULL. */
+ * NULL.  split_k 0 lets the library choose: for the tiled MFMA kernel the
+ * smallest power of two up to 8 that gives about one workgroup per compute
+ * unit, lowered to what the scratch holds; 1 for the other kernels.  The
+ * reconstructive matmuls below take split_k the same way. */
 int uw_gemm_bf16(const uint16_t* W, int64_t rows, int64_t cols,
                  const uint16_t* X, int64_t batch, float* Y,
                  int kernel, int split_k, void* scratch, uint64_t scratch_bytes,
@@ -265,14 +268,17 @@ enum {
     UW_PIPE_BF16 = 5      /* uncompressed weights (baseline; not for uw_matmul) */
 };
 
-/* Scratch bytes uw_matmul needs for (pipeline, shape, batch, split_k).
- * Returns the size (>= 0) or a negative error code. */
+/* Scratch bytes uw_matmul needs for (pipeline, shape, batch, split_k);
+ * split_k 0: for the split the library would choose with UW_KERNEL_AUTO on
+ * the current device.  Returns the size (>= 0) or a negative error code. */
 int64_t uw_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch, int split_k);
 
 /* One matmul through a pipeline ("Four ways to use compressed weights").
  * UW_PIPE_AUTO looks up (rows, cols, batch) in the plan table and falls
- * back to UW_PIPE_DIRECT (or UW_PIPE_PAL without a NIB section).  scratch
- * must hold uw_scratch_bytes(...) bytes.  UW_EINVAL on a too-small scratch. */
+ * back to UW_PIPE_DIRECT (or UW_PIPE_PAL without a NIB section) with
+ * UW_KERNEL_AUTO and split_k 0.  scratch must hold uw_scratch_bytes(...)
+ * bytes (with split_k 0: at least the split-1 size; a larger split is used
+ * as far as the scratch allows).  UW_EINVAL on a too-small scratch. */
 int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k,
               const uint16_t* X, int64_t batch, float* Y,
               void* scratch, uint64_t scratch_bytes, void* stream);

@@ -89,6 +89,32 @@ int run_decode(const uw_dmat* d, void* out, int mode, void* stream, const char* 
     return e == hipSuccess ? UW_OK : hip_fail(e, who);
 }
 
+// Compute units of the current device (256 if it cannot be queried).
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    return cus;
+}
+
+// The kernel family UW_KERNEL_AUTO picks for a shape (measured on MI355X on
+// the Llama MLP shapes: the GEMV below batch 4, the skinny MFMA kernel up to
+// batch 16, the tiled MFMA kernel from batch 17, which is faster than the
+// skinny kernel at batch 32 and 64 on both shapes).
+int auto_kernel(const uwk::MatArgs& a) {
+    return a.B < 4 ? UW_KERNEL_GEMV : (a.B <= 16 && uwk::mfma_gemv_supported(a) ? UW_KERNEL_SKINNY : UW_KERNEL_MFMA);
+}
+
+// split_k 0: the library's choice, K-slices for the tiled MFMA kernel that
+// fill the chip (1 for the other kernels).
+int resolve_split(const uwk::MatArgs& a, int kernel, int split_k) {
+    if (split_k != 0) return split_k;
+    return kernel == UW_KERNEL_MFMA ? uwk::mfma_default_split(a, device_cus()) : 1;
+}
+
 // Common checks and dispatch of one matmul.
 int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* scratch, uint64_t scratch_bytes,
                void* stream, const char* who) {
@@ -105,16 +131,21 @@ int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* s
         return uw::fail(UW_EINVAL, std::string(who) + ": sign/mantissa plane missing");
     if (src == uwk::SRC_PAL && a.R * a.C && (!a.bitmap || !a.tile_vbase))
         return uw::fail(UW_EINVAL, std::string(who) + ": verbatim tables missing");
-    if (kernel == UW_KERNEL_AUTO)
-        kernel = a.B < 4 ? UW_KERNEL_GEMV
-                         : (a.B <= 64 && uwk::mfma_gemv_supported(a) ? UW_KERNEL_SKINNY : UW_KERNEL_MFMA);
+    if (kernel == UW_KERNEL_AUTO) kernel = auto_kernel(a);
     if (kernel == UW_KERNEL_GEMV && a.B > 16)
         return uw::fail(UW_EINVAL, std::string(who) + ": the GEMV kernel takes batch <= 16");
     if (kernel == UW_KERNEL_SKINNY && !uwk::mfma_gemv_supported(a))
         return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": the skinny MFMA kernel needs cols % 128 == 0 and cols <= 32768");
     if (kernel < UW_KERNEL_GEMV || kernel > UW_KERNEL_SKINNY)
         return uw::fail(UW_EINVAL, std::string(who) + ": unknown kernel");
-    if (split_k < 1 || split_k > 64) return uw::fail(UW_EINVAL, std::string(who) + ": split_k must be 1..64");
+    if (split_k < 0 || split_k > 64) return uw::fail(UW_EINVAL, std::string(who) + ": split_k must be 0..64");
+    if (split_k == 0) {
+        // the library's choice, as large as the scratch the caller gave allows
+        split_k = resolve_split(a, kernel, 0);
+        while (split_k > 1 && (!scratch || !aligned16(scratch) ||
+                               scratch_bytes < uint64_t(split_k) * uint64_t(a.B) * uint64_t(a.R) * 4))
+            split_k >>= 1;
+    }
     if (kernel == UW_KERNEL_MFMA && !uwk::mfma_supported(a))
         return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": the tiled MFMA kernel takes cols <= 65536");
     hipError_t e;
@@ -241,8 +272,16 @@ int uw_gemm_recon_pal(const uw_dmat* d, const uint8_t* nib, const uint16_t* X, i
 
 int64_t uw_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch, int split_k) {
     uw::clear_error();
-    if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_BF16 || rows < 0 || cols < 0 || batch < 0 || split_k < 1)
+    if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_BF16 || rows < 0 || cols < 0 || batch < 0 || split_k < 0)
         return uw::fail(UW_EINVAL, "uw_scratch_bytes: bad argument");
+    if (split_k == 0) {
+        // what split_k 0 resolves to with the kernel UW_KERNEL_AUTO picks
+        uwk::MatArgs a{};
+        a.R = rows;
+        a.C = cols;
+        a.B = batch;
+        split_k = cols % uw::kGroup ? 1 : resolve_split(a, auto_kernel(a), 0);
+    }
     uint64_t n = align256(decoded_bytes(pipeline, rows, cols));
     if (split_k > 1) n += align256(uint64_t(split_k) * uint64_t(batch) * uint64_t(rows) * 4);
     return int64_t(n);
@@ -262,7 +301,7 @@ int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k, const uin
         } else {
             pipeline = d->nib ? UW_PIPE_DIRECT : UW_PIPE_PAL;
             kernel = UW_KERNEL_AUTO;
-            split_k = 1;
+            split_k = 0;
         }
         uw::clear_error();
     }
@@ -270,7 +309,8 @@ int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k, const uin
         return uw::fail(UW_EINVAL, "uw_matmul: pipeline must be UW_PIPE_AUTO or FULL/EXP/PAL/DIRECT");
     if (pipeline == UW_PIPE_DIRECT && d->groups && !d->nib)
         return uw::fail(UW_EINVAL, "uw_matmul: direct palette needs the NIB section on the device");
-    const int64_t need = uw_scratch_bytes(pipeline, d->rows, d->cols, batch, split_k);
+    // split_k 0 shrinks to what the scratch holds: only the decoded plane is required
+    const int64_t need = uw_scratch_bytes(pipeline, d->rows, d->cols, batch, split_k == 0 ? 1 : split_k);
     if (need < 0) return int(need);
     if (uint64_t(need) > scratch_bytes || (need > 0 && (!scratch || !aligned16(scratch))))
         return uw::fail(UW_EINVAL, "uw_matmul: scratch smaller than uw_scratch_bytes()");

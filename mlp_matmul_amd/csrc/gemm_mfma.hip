@@ -350,11 +350,18 @@ int env_int(const char* name, int dflt) {
 // rebuilding sources, else 1), as measured on the Llama MLP shapes at batch
 // 32-256; UW_MFMA_NB / _RBW / _WPG / _PD override for tuning.  Combinations
 // that do not fit the register file are never instantiated.
+struct Tiling {
+    int nb, rbw, wpg;
+};
+Tiling tiling_of(const MatArgs& a) {
+    return {env_int("UW_MFMA_NB", a.B <= 64 ? 4 : 8), env_int("UW_MFMA_RBW", 2),
+            env_int("UW_MFMA_WPG", a.B > 128 && a.R < 8192 ? 8 : 4)};
+}
+
 template <int SRC>
 hipError_t launch_src(const MatArgs& a, hipStream_t s) {
-    const int nb = env_int("UW_MFMA_NB", a.B <= 64 ? 4 : 8);
-    const int rbw = env_int("UW_MFMA_RBW", 2);
-    const int wpg = env_int("UW_MFMA_WPG", a.B > 128 && a.R < 8192 ? 8 : 4);
+    const Tiling tl = tiling_of(a);
+    const int nb = tl.nb, rbw = tl.rbw, wpg = tl.wpg;
     const int pd = env_int("UW_MFMA_PD", nb <= 4 && SRC != SRC_BF16 ? 3 : 1);
     if (rbw <= 2) {
         if (wpg <= 4) {
@@ -384,6 +391,22 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// K-slices that give the launch about one workgroup per CU: the smallest
+// power of two (at most 8, each slice at least 4 steps) for which tiles x
+// slices reaches three quarters of the CUs (measured on the Llama MLP
+// shapes at batch 32-256, this is the split the autotuner picks).
+int mfma_default_split(const MatArgs& a, int cus) {
+    if (a.R <= 0 || a.B <= 0 || a.C <= 0) return 1;
+    const Tiling tl = tiling_of(a);
+    const int64_t mt = 16 * int64_t(tl.rbw <= 2 ? 2 : 4) * (tl.wpg <= 4 ? 4 : 8);
+    const int64_t nt = 16 * int64_t(tl.nb <= 4 ? 4 : 8);
+    const int64_t tiles = ((a.R + mt - 1) / mt) * ((a.B + nt - 1) / nt);
+    const int64_t steps = a.C / kKS;
+    int split = 1;
+    while (split < 8 && tiles * split * 4 < int64_t(cus) * 3 && steps / (2 * split) >= 4) split *= 2;
+    return split;
+}
 
 // The kernel keeps a lane's row segment of one step in one 64-column group
 // and stages the verbatim tables of a 256-row band in LDS (at most 48 KiB).

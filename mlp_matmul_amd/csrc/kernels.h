@@ -52,6 +52,8 @@ bool gemv_gateup_supported(const MatArgs& gate, const MatArgs& up);
 hipError_t launch_gemv_gateup(const MatArgs& gate, const MatArgs& up, uint16_t* h, hipStream_t s);
 hipError_t launch_mfma(int src, const MatArgs& a, hipStream_t s);
 bool mfma_supported(const MatArgs& a);
+// Split-K that fills the chip for the tiled MFMA kernel on `cus` compute units.
+int mfma_default_split(const MatArgs& a, int cus);
 hipError_t launch_mfma_gemv(int src, const MatArgs& a, hipStream_t s);
 bool mfma_gemv_supported(const MatArgs& a);
 hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, uint16_t* h, hipStream_t s);

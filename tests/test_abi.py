@@ -86,3 +86,15 @@ def test_decoders_check_descriptors_before_launch():
     assert b"max_tile_bytes" in L.uw_last_error()
     d = _fake_dmat(b, max_tile_bytes=0)
     assert L.uw_decode_exponents(ct.byref(d), ct.c_void_p(0x100000), None) == _capi.UW_EINVAL
+
+
+def test_scratch_for_library_split_choice():
+    """split_k 0 sizes scratch for the split the library would pick: none for
+    the GEMV batches, eight K-slices for a 4096x14336 matrix at batch 256
+    (the CU count falls back to 256 without a device)."""
+    L = uw.lib()
+    P = _capi.UW_PIPE_DIRECT
+    assert L.uw_scratch_bytes(P, 4096, 14336, 1, 0) == 0
+    assert L.uw_scratch_bytes(P, 4096, 14336, 256, 0) == 8 * 256 * 4096 * 4
+    assert L.uw_scratch_bytes(P, 14336, 4096, 256, 0) == 0
+    assert L.uw_scratch_bytes(P, 4096, 14336, 256, -1) == _capi.UW_EINVAL

@@ -278,6 +278,30 @@ def test_mfma_split_k(torch_cuda, split):
     assert_matmul_close(Y.cpu().numpy(), w, x, what=f"split {split}")
 
 
+def test_split_k_library_choice(torch_cuda):
+    """split_k 0: the library picks the K-slices (8 for this short, wide
+    matrix at batch 256) and lowers them to what the scratch holds; the
+    result is within tolerance with the full scratch, a scratch for two
+    slices, and none."""
+    print_case("split_k 0 (library choice), R=512 C=4096 B=256")
+    R, C, B = 512, 4096, 256
+    w = workloads.layer_weight(2, 4, 2, shape=(R, C))
+    x = _x(5, B, C)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    full = uw.scratch_bytes(uw.UW_PIPE_DIRECT, R, C, B, 0)
+    assert full == uw.scratch_bytes(uw.UW_PIPE_DIRECT, R, C, B, 8) > 0
+    for n in (full, uw.scratch_bytes(uw.UW_PIPE_DIRECT, R, C, B, 2), 0):
+        scratch = uw._torch().empty(max(n, 16), dtype=uw._torch().uint8, device="cuda")
+        Y = uw.matmul(dm, X, pipeline=uw.UW_PIPE_DIRECT, kernel=uw.UW_KERNEL_AUTO, split_k=0,
+                      scratch=scratch if n else None)
+        assert_matmul_close(Y.cpu().numpy(), w, x, what=f"split 0 with {n} bytes of scratch")
+    # the no-plan fallback of UW_PIPE_AUTO takes the same route
+    assert uw.plan_lookup(R, C, B) is None
+    Y = uw.matmul(dm, X, scratch=uw._torch().empty(full, dtype=uw._torch().uint8, device="cuda"))
+    assert_matmul_close(Y.cpu().numpy(), w, x, what="auto, no plan")
+
+
 @pytest.mark.parametrize("R,C,B,split", [(300, 128, 20, 4), (257, 64, 70, 3), (513, 1024, 129, 16)])
 def test_mfma_split_k_short_slices(torch_cuda, R, C, B, split):
     """Split-K with empty and one-step K slices, a band past R, a batch tile
