@@ -387,6 +387,54 @@ def layer_steps(layers, batches, stream, steps=30, warmup=5):
     return rows
 
 
+def layer_overlap(layers, batches, stream, steps=20, warmup=3):
+    """One MLP block per call (uw_mlp_layer) through the decoding pipelines,
+    every step on one stream against the decodes on a second stream that
+    overlap the matmuls; 4 rotated layers, microseconds per layer."""
+    import ctypes as ct
+    import functools
+    import torch
+    import mlp_matmul_amd as uw
+    import workloads
+    F, H = workloads.LLAMA_FFN, workloads.LLAMA_HIDDEN
+    aux = torch.cuda.Stream()
+    L = uw.lib()
+    rows = []
+    for b in batches:
+        X = [torch.from_numpy(workloads.layer_activation(2, i, 0, b).view(np.int16)).view(torch.bfloat16).cuda()
+             for i in range(len(layers))]
+        y = torch.empty((b, H), dtype=torch.float32, device="cuda")
+        row = {"batch": b}
+        for name in ("full", "exp", "pal", "direct"):
+            p = {"full": uw.UW_PIPE_FULL, "exp": uw.UW_PIPE_EXP, "pal": uw.UW_PIPE_PAL, "direct": uw.UW_PIPE_DIRECT}[name]
+            scratch = torch.empty(uw.mlp_scratch_bytes(p, F, H, b), dtype=torch.uint8, device="cuda")
+            res = {}
+            for mode, a in (("one_stream", None), ("two_streams", ct.c_void_p(aux.cuda_stream))):
+                if name == "direct" and a is not None:
+                    continue                      # nothing to decode
+                calls = [functools.partial(L.uw_mlp_layer, ct.byref(lay.mats[0].dmat), ct.byref(lay.mats[1].dmat),
+                                           ct.byref(lay.mats[2].dmat), p, ct.c_void_p(X[i].data_ptr()), b,
+                                           ct.c_void_p(y.data_ptr()), ct.c_void_p(scratch.data_ptr()),
+                                           ct.c_uint64(scratch.numel()), ct.c_void_p(stream.cuda_stream), a)
+                         for i, lay in enumerate(layers)]
+                for i in range(warmup):
+                    uw.check(calls[i % len(calls)](), "uw_mlp_layer")
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(steps):
+                    uw.check(calls[i % len(calls)](), "uw_mlp_layer")
+                e1.record(stream)
+                e1.synchronize()
+                res[mode] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+            if "two_streams" in res:
+                res["speedup"] = round(res["one_stream"] / res["two_streams"], 3)
+            row[name] = res
+            del scratch
+        rows.append(row)
+        log(f"layer overlap B={b}: {row}")
+    return rows
+
+
 def time_pipeline(copies, pipeline, kernel, split_k, X, reps=20, warmup=3, stream=None):
     """Seconds per uw_matmul call (pipeline, kernel, split_k), rotating copies."""
     import torch
@@ -789,6 +837,9 @@ def main():
     if not a.no_config34 and not a.no_compare:
         out["layer_steps"] = {"workload": "llama3.1-8b-mlp-layer, direct palette vs bf16, batch 4 and 16",
                               "rows": layer_steps(layers, [4, 16], stream)}
+        out["layer_overlap"] = {"workload": "llama3.1-8b-mlp-layer through uw_mlp_layer, us per layer: decodes on the "
+                                            "layer's stream vs on a second stream overlapping the matmuls",
+                                "rows": layer_overlap(layers, [1, 16], stream)}
         out["per_row_sigma"] = {"workload": "llama3.1-8b gate/down shapes, per-row sigma log-U[0.005,0.05], "
                                             "4 copies rotated",
                                 "rows": config4([64, 128, 256])}

@@ -304,6 +304,32 @@ int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, voi
 int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, int64_t batch,
                    uint16_t* h, float* g_out, float* u_out, void* stream);
 
+/* Scratch bytes of uw_mlp_layer for gate and up of shape [rows, cols] and
+ * down of shape [cols, rows] (rows, cols multiples of 64): one decoded plane
+ * per matrix, g and u (fp32), h (bf16), split-K partials.  Returns the size
+ * or a negative error code. */
+int64_t uw_mlp_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch);
+
+/* One SwiGLU MLP block through one pipeline ("Four ways to use compressed
+ * weights"), y = down . bf16(SiLU(X . gate^T) * (X . up^T)):
+ * gate, up [F, H], down [H, F]; X bf16 bits [batch, H]; y fp32 [batch, F].
+ * Each matmul runs with UW_KERNEL_AUTO and the library's split-K choice;
+ * UW_PIPE_DIRECT fuses gate/up into one launch where uw_mlp_gate_up applies.
+ * With aux_stream NULL every step runs on `stream`.  With an aux_stream (a
+ * second stream of the caller's) and a decoding pipeline (FULL, EXP, PAL),
+ * the three decodes run there, ordered after the work already on `stream`,
+ * and each matmul waits only for its own matrix's decode, so decoding the
+ * next matrix overlaps the current matmul (the page's "Why no single
+ * pipeline wins": preprocessing adds to latency unless it overlaps).  All
+ * results are ordered on `stream` when the call returns; y is bit-identical
+ * to the one-stream order.  scratch: uw_mlp_scratch_bytes() bytes, device,
+ * 16-byte aligned, caller-owned; calls that share a scratch must be ordered
+ * on one `stream`.  Errors: UW_EINVAL (shapes, pipeline, NULL/misaligned
+ * pointers, small scratch), UW_EHIP. */
+int uw_mlp_layer(const uw_dmat* gate, const uw_dmat* up, const uw_dmat* down, int pipeline,
+                 const uint16_t* X, int64_t batch, float* y,
+                 void* scratch, uint64_t scratch_bytes, void* stream, void* aux_stream);
+
 /* ----------------------------------------------------------- kernel timer */
 /* Per-launch durations of the matmul kernels (GEMV and MFMA), for measuring
  * them on their own stream.  While enabled, each matmul kernel launch takes

@@ -255,6 +255,30 @@ def mlp_gate_up(gate: DeviceMatrix, up: DeviceMatrix, X, h=None, g=None, u=None,
     return h
 
 
+def mlp_scratch_bytes(pipeline, rows, cols, batch) -> int:
+    n = lib().uw_mlp_scratch_bytes(pipeline, rows, cols, batch)
+    if n < 0:
+        check(int(n), "uw_mlp_scratch_bytes")
+    return int(n)
+
+
+def mlp_layer(gate: DeviceMatrix, up: DeviceMatrix, down: DeviceMatrix, X, pipeline=UW_PIPE_DIRECT, y=None,
+              scratch=None, stream=None, aux_stream=None):
+    """y = down . bf16(SiLU(X.gate^T) * (X.up^T)) through one pipeline; with an
+    aux_stream the decodes overlap the matmuls (uw_mlp_layer)."""
+    torch = _torch()
+    batch = X.shape[0]
+    if y is None:
+        y = torch.empty((batch, down.rows), dtype=torch.float32, device="cuda")
+    if scratch is None:
+        scratch = torch.empty(max(mlp_scratch_bytes(pipeline, gate.rows, gate.cols, batch), 16), dtype=torch.uint8,
+                              device="cuda")
+    aux = ct.c_void_p(aux_stream) if aux_stream is not None else None
+    check(lib().uw_mlp_layer(ct.byref(gate.dmat), ct.byref(up.dmat), ct.byref(down.dmat), pipeline, _ptr(X), batch,
+                             _ptr(y), _ptr(scratch), scratch.numel(), _stream(stream), aux), "uw_mlp_layer")
+    return y
+
+
 def silu_mul_bf16(g, u, h=None, stream=None):
     torch = _torch()
     if h is None:

@@ -80,6 +80,9 @@ SIGNATURES = {
     "uw_matmul": (_INT, [ct.POINTER(uw_dmat), _INT, _INT, _INT, _P, _I64, _P, _P, _U64, _P]),
     "uw_silu_mul_bf16": (_INT, [_P, _P, _I64, _P, _P]),
     "uw_mlp_gate_up": (_INT, [ct.POINTER(uw_dmat), ct.POINTER(uw_dmat), _P, _I64, _P, _P, _P, _P]),
+    "uw_mlp_scratch_bytes": (_I64, [_INT, _I64, _I64, _I64]),
+    "uw_mlp_layer": (_INT, [ct.POINTER(uw_dmat), ct.POINTER(uw_dmat), ct.POINTER(uw_dmat), _INT, _P, _I64, _P, _P,
+                             _U64, _P, _P]),
     "uw_kernel_timer_enable": (_INT, [_INT]),
     "uw_kernel_timer_disable": (_INT, []),
     "uw_kernel_timer_reset": (_INT, []),

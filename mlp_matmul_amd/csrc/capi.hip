@@ -7,6 +7,8 @@
 //   exp       exponent-only decode -> u8 in scratch -> reconstructive matmul
 //   pal       palette transcode -> nibbles in scratch -> reconstructive matmul
 //   direct    reconstructive matmul on nibbles made once at load time
+#include <algorithm>
+#include <map>
 #include <cstring>
 #include <string>
 
@@ -195,6 +197,91 @@ uint64_t decoded_bytes(int pipeline, int64_t rows, int64_t cols) {
 
 }  // namespace
 
+// ------------------------------------------------------- one MLP block
+// Scratch of uw_mlp_layer: a decoded plane per matrix (so the next matrix's
+// decode can run while the current matmul reads its own), g and u (fp32),
+// h (bf16), then the split-K partials of the matmuls (shared: they run one
+// after another on the layer's stream).
+struct MlpLayout {
+    uint64_t dec[3], g, u, h, part, part_bytes, total;
+};
+
+MlpLayout mlp_layout(int pipeline, int64_t F, int64_t H, int64_t B) {
+    MlpLayout l{};
+    uint64_t off = 0;
+    for (int m = 0; m < 3; ++m) {
+        l.dec[m] = off;
+        off += align256(decoded_bytes(pipeline, F, H));
+    }
+    l.g = off;
+    off += align256(uint64_t(B) * uint64_t(F) * 4);
+    l.u = off;
+    off += align256(uint64_t(B) * uint64_t(F) * 4);
+    l.h = off;
+    off += align256(uint64_t(B) * uint64_t(F) * 2);
+    l.part = off;
+    // the split-K partials the library's split choice needs for either shape
+    const int64_t pg = uw_scratch_bytes(UW_PIPE_DIRECT, F, H, B, 0), pd = uw_scratch_bytes(UW_PIPE_DIRECT, H, F, B, 0);
+    l.part_bytes = align256(uint64_t(std::max<int64_t>(0, std::max(pg, pd))));
+    l.total = off + l.part_bytes;
+    return l;
+}
+
+int decode_for(const uw_dmat* d, int pipeline, void* dec, void* s) {
+    switch (pipeline) {
+        case UW_PIPE_FULL: return uw_decode_full(d, static_cast<uint16_t*>(dec), s);
+        case UW_PIPE_EXP: return uw_decode_exponents(d, static_cast<uint8_t*>(dec), s);
+        case UW_PIPE_PAL: return uw_transcode_palette(d, static_cast<uint8_t*>(dec), s);
+        default: return UW_OK;
+    }
+}
+
+// One matmul of the block from its decoded plane (UW_KERNEL_AUTO, split-K
+// the library's choice within the partials area).
+int matmul_from(const uw_dmat* d, int pipeline, const void* dec, const uint16_t* X, int64_t B, float* Y, void* part,
+                uint64_t part_bytes, void* s) {
+    switch (pipeline) {
+        case UW_PIPE_FULL:
+            return uw_gemm_bf16(static_cast<const uint16_t*>(dec), d->rows, d->cols, X, B, Y, UW_KERNEL_AUTO, 0, part,
+                                part_bytes, s);
+        case UW_PIPE_EXP:
+            return uw_gemm_recon_exp(d, static_cast<const uint8_t*>(dec), X, B, Y, UW_KERNEL_AUTO, 0, part, part_bytes, s);
+        case UW_PIPE_PAL:
+            return uw_gemm_recon_pal(d, static_cast<const uint8_t*>(dec), X, B, Y, UW_KERNEL_AUTO, 0, part, part_bytes, s);
+        default:
+            return uw_gemm_recon_pal(d, d->nib, X, B, Y, UW_KERNEL_AUTO, 0, part, part_bytes, s);
+    }
+}
+
+// Events that order the decode stream against the layer's stream: created
+// once per host thread and device, re-recorded by every call (a wait takes
+// the record made before it, so reuse across calls is safe).
+struct LayerEvents {
+    hipEvent_t start = nullptr, dec[3] = {nullptr, nullptr, nullptr};
+};
+
+int layer_events(LayerEvents** out) {
+    thread_local std::map<int, LayerEvents> per_device;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "uw_mlp_layer");
+    LayerEvents& ev = per_device[dev];
+    if (!ev.start) {
+        hipEvent_t made[4] = {};
+        for (int i = 0; i < 4; ++i) {
+            e = hipEventCreateWithFlags(&made[i], hipEventDisableTiming);
+            if (e != hipSuccess) {
+                for (int j = 0; j < i; ++j) (void)hipEventDestroy(made[j]);
+                return hip_fail(e, "uw_mlp_layer");
+            }
+        }
+        ev.start = made[0];
+        for (int m = 0; m < 3; ++m) ev.dec[m] = made[m + 1];
+    }
+    *out = &ev;
+    return UW_OK;
+}
+
 extern "C" {
 
 int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_SECTIONS]) {
@@ -358,6 +445,93 @@ int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, in
     uwk::MatArgs u = compressed_args(up, up->nib, X, batch, u_out);
     hipError_t e = uwk::launch_gemv_gateup(g, u, h, as_stream(stream));
     return e == hipSuccess ? UW_OK : hip_fail(e, who);
+}
+
+int64_t uw_mlp_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch) {
+    uw::clear_error();
+    if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_DIRECT || rows < 0 || cols < 0 || batch < 0 ||
+        cols % uw::kGroup || rows % uw::kGroup)
+        return uw::fail(UW_EINVAL, "uw_mlp_scratch_bytes: bad argument (rows and cols must be multiples of 64)");
+    return int64_t(mlp_layout(pipeline, rows, cols, batch).total);
+}
+
+int uw_mlp_layer(const uw_dmat* gate, const uw_dmat* up, const uw_dmat* down, int pipeline, const uint16_t* X,
+                 int64_t batch, float* y, void* scratch, uint64_t scratch_bytes, void* stream, void* aux_stream) {
+    uw::clear_error();
+    const char* who = "uw_mlp_layer";
+    if (!gate || !up || !down) return uw::fail(UW_EINVAL, std::string(who) + ": NULL matrix");
+    const int64_t F = gate->rows, H = gate->cols;
+    if (up->rows != F || up->cols != H || down->rows != H || down->cols != F || F % uw::kGroup || H % uw::kGroup ||
+        F < 0 || H < 0)
+        return uw::fail(UW_EINVAL, std::string(who) + ": gate and up must be [F, H] and down [H, F], F and H multiples of 64");
+    if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_DIRECT)
+        return uw::fail(UW_EINVAL, std::string(who) + ": pipeline must be UW_PIPE_FULL, EXP, PAL or DIRECT");
+    if (batch < 0) return uw::fail(UW_EINVAL, std::string(who) + ": negative batch");
+    if (batch == 0 || H == 0) return UW_OK;
+    if (!X || !y || !aligned16(X) || !aligned16(y))
+        return uw::fail(UW_EINVAL, std::string(who) + ": NULL or misaligned X or y");
+    const MlpLayout l = mlp_layout(pipeline, F, H, batch);
+    if (scratch_bytes < l.total || !scratch || !aligned16(scratch))
+        return uw::fail(UW_EINVAL, std::string(who) + ": scratch smaller than uw_mlp_scratch_bytes()");
+    uint8_t* base = static_cast<uint8_t*>(scratch);
+    float* g = reinterpret_cast<float*>(base + l.g);
+    float* u = reinterpret_cast<float*>(base + l.u);
+    uint16_t* h = reinterpret_cast<uint16_t*>(base + l.h);
+    void* part = base + l.part;
+    const uw_dmat* mats[3] = {gate, up, down};
+    void* dec[3] = {base + l.dec[0], base + l.dec[1], base + l.dec[2]};
+    int rc;
+
+    if (pipeline == UW_PIPE_DIRECT) {
+        // nothing to decode; gate/up fused into one launch where it applies
+        bool fused = false;
+        if (batch <= 4 && batch * H * 2 <= 32768 && H <= 60 * 4096) {
+            rc = uw_mlp_gate_up(gate, up, X, batch, h, nullptr, nullptr, stream);
+            if (rc && rc != UW_EUNSUPPORTED) return rc;
+            fused = rc == UW_OK;
+        }
+        if (!fused) {
+            if ((rc = matmul_from(gate, pipeline, nullptr, X, batch, g, part, l.part_bytes, stream))) return rc;
+            if ((rc = matmul_from(up, pipeline, nullptr, X, batch, u, part, l.part_bytes, stream))) return rc;
+            if ((rc = uw_silu_mul_bf16(g, u, batch * F, h, stream))) return rc;
+        }
+        return matmul_from(down, pipeline, nullptr, h, batch, y, part, l.part_bytes, stream);
+    }
+
+    if (!aux_stream) {
+        // one stream: each matrix decoded right before its matmul
+        for (int m = 0; m < 3; ++m) {
+            if ((rc = decode_for(mats[m], pipeline, dec[m], stream))) return rc;
+            const uint16_t* xin = m < 2 ? X : h;
+            float* yout = m == 0 ? g : (m == 1 ? u : y);
+            if ((rc = matmul_from(mats[m], pipeline, dec[m], xin, batch, yout, part, l.part_bytes, stream))) return rc;
+            if (m == 1 && (rc = uw_silu_mul_bf16(g, u, batch * F, h, stream))) return rc;
+        }
+        return UW_OK;
+    }
+
+    // two streams: the three decodes run back to back on aux_stream (after
+    // everything already on stream, which may still read this scratch), each
+    // matmul on stream waits only for its own matrix's decode, so the decode
+    // of up and down overlaps the gate and up matmuls
+    LayerEvents* ev = nullptr;
+    if ((rc = layer_events(&ev))) return rc;
+    hipStream_t s = as_stream(stream), a = as_stream(aux_stream);
+    hipError_t e = hipEventRecord(ev->start, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(a, ev->start, 0);
+    if (e != hipSuccess) return hip_fail(e, who);
+    for (int m = 0; m < 3; ++m) {
+        if ((rc = decode_for(mats[m], pipeline, dec[m], aux_stream))) return rc;
+        if ((e = hipEventRecord(ev->dec[m], a)) != hipSuccess) return hip_fail(e, who);
+    }
+    for (int m = 0; m < 3; ++m) {
+        if ((e = hipStreamWaitEvent(s, ev->dec[m], 0)) != hipSuccess) return hip_fail(e, who);
+        const uint16_t* xin = m < 2 ? X : h;
+        float* yout = m == 0 ? g : (m == 1 ? u : y);
+        if ((rc = matmul_from(mats[m], pipeline, dec[m], xin, batch, yout, part, l.part_bytes, stream))) return rc;
+        if (m == 1 && (rc = uw_silu_mul_bf16(g, u, batch * F, h, stream))) return rc;
+    }
+    return UW_OK;
 }
 
 int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, void* stream) {

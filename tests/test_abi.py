@@ -98,3 +98,16 @@ def test_scratch_for_library_split_choice():
     assert L.uw_scratch_bytes(P, 4096, 14336, 256, 0) == 8 * 256 * 4096 * 4
     assert L.uw_scratch_bytes(P, 14336, 4096, 256, 0) == 0
     assert L.uw_scratch_bytes(P, 4096, 14336, 256, -1) == _capi.UW_EINVAL
+
+
+def test_mlp_scratch_bytes():
+    """Scratch of one MLP block: a decoded plane per matrix, g, u, h and the
+    split-K partials; rejects shapes that are not whole 64-element groups."""
+    L = uw.lib()
+    F, H, B = 14336, 4096, 1
+    planes = {_capi.UW_PIPE_FULL: 2 * F * H, _capi.UW_PIPE_EXP: F * H, _capi.UW_PIPE_PAL: F * H // 2,
+              _capi.UW_PIPE_DIRECT: 0}
+    for p, n in planes.items():
+        assert L.uw_mlp_scratch_bytes(p, F, H, B) == 3 * n + 2 * B * F * 4 + 256 * ((B * F * 2 + 255) // 256)
+    assert L.uw_mlp_scratch_bytes(_capi.UW_PIPE_AUTO, F, H, B) == _capi.UW_EINVAL
+    assert L.uw_mlp_scratch_bytes(_capi.UW_PIPE_PAL, F, 100, B) == _capi.UW_EINVAL

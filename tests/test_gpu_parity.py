@@ -446,6 +446,57 @@ def test_mlp_layer_chain(torch_cuda, B):
     assert_matmul_close(y.cpu().numpy(), wd, hb, what="down")
 
 
+@pytest.mark.parametrize("pipeline", ["full", "exp", "pal", "direct"])
+@pytest.mark.parametrize("B", [1, 5, 24])
+def test_mlp_layer_one_and_two_streams(torch_cuda, pipeline, B):
+    """uw_mlp_layer on one stream and with the decodes on a second stream
+    gives, bit for bit, what the single-matrix calls give for the same block
+    (decode + matmul per matrix with the library's kernel and split-K
+    choice, SiLU product between); that chain is checked against the fp64
+    oracle on the GPU's h (reduced-width layer shapes)."""
+    import torch
+    print_case(f"mlp layer {pipeline} B={B}")
+    F, H = 1536, 512
+    wg = workloads.layer_weight(3, 1, 0, shape=(F, H))
+    wu = workloads.layer_weight(3, 1, 1, shape=(F, H))
+    wd = workloads.layer_weight(3, 1, 2, shape=(H, F))
+    x = workloads.layer_activation(3, 1, 0, B, cols=H)
+    dms = [uw.compress(m).to_device() for m in (wg, wu, wd)]
+    p = uw.PIPELINES[pipeline]
+    X = to_dev_bf16(x)
+    scr = lambda R, C: uw.alloc_scratch(p, R, C, B, 0)
+    g = uw.matmul(dms[0], X, pipeline=p, kernel=uw.UW_KERNEL_AUTO, split_k=0, scratch=scr(F, H))
+    u = uw.matmul(dms[1], X, pipeline=p, kernel=uw.UW_KERNEL_AUTO, split_k=0, scratch=scr(F, H))
+    h = uw.silu_mul_bf16(g, u)
+    y_ref = uw.matmul(dms[2], h, pipeline=p, kernel=uw.UW_KERNEL_AUTO, split_k=0, scratch=scr(H, F))
+    y1 = uw.mlp_layer(*dms, X, pipeline=p)
+    aux = torch.cuda.Stream()
+    y2 = uw.mlp_layer(*dms, X, pipeline=p, aux_stream=aux.cuda_stream)
+    y3 = uw.mlp_layer(*dms, X, pipeline=p, aux_stream=aux.cuda_stream)     # events reused
+    torch.cuda.synchronize()
+    yr = y_ref.cpu().numpy()
+    for name, yy in (("one stream", y1), ("two streams", y2), ("two streams, again", y3)):
+        assert np.array_equal(yy.cpu().numpy().view(np.uint32), yr.view(np.uint32)), name
+    assert_matmul_close(yr, wd, from_dev_bits(h), what=f"{pipeline} down on the GPU's h")
+
+
+def test_mlp_layer_rejects(torch_cuda):
+    print_case("mlp layer argument checks")
+    rng = np.random.default_rng(2)
+    dg = uw.compress(workloads.gaussian_weights(rng, 128, 64, 0.02)).to_device()
+    dd = uw.compress(workloads.gaussian_weights(rng, 64, 128, 0.02)).to_device()
+    X = to_dev_bf16(_x(1, 2, 64))
+    with pytest.raises(uw.UnweightError, match="down"):
+        uw.mlp_layer(dg, dg, dg, X)                       # down must be [H, F]
+    import torch
+    big = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    with pytest.raises(uw.UnweightError, match="pipeline"):
+        uw.mlp_layer(dg, dg, dd, X, pipeline=uw.UW_PIPE_AUTO, scratch=big)
+    small = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(uw.UnweightError, match="scratch"):
+        uw.mlp_layer(dg, dg, dd, X, scratch=small)
+
+
 # ----------------------------------------------------- fused gate/up + SiLU
 def _bf16_key(b):
     b = b.astype(np.int64)
