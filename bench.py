@@ -435,6 +435,95 @@ def layer_overlap(layers, batches, stream, steps=20, warmup=3):
     return rows
 
 
+def attention_bench(batches, n_layers=6, steps=30, warmup=4):
+    """The second workload on the codec: Llama-3.1-8B attention projections
+    (q, o 4096x4096; k, v 1024x4096) of 6 seeded layers.  One step runs the
+    four projections of one layer, steps rotate over the layers (495 MB of
+    bf16, 378 MB compressed: more than the 256 MiB Infinity Cache, so a
+    layer's weights come from HBM as in a decode pass).  Direct palette with
+    the library's kernel and split choice against the hand-written bf16
+    kernels (the fastest per shape) and torch.matmul."""
+    import ctypes as ct
+    import functools
+    import torch
+    import mlp_matmul_amd as uw
+    import workloads
+    L = uw.lib()
+    names = list(workloads.ATTN_SHAPES)
+    dev, bf, sizes = [], [], {}
+    for i in range(n_layers):
+        dl, bl = {}, {}
+        for name in names:
+            w = workloads.attention_weight(i, name)
+            blob = uw.compress(w, emit_palette=True)
+            dl[name] = blob.to_device(("sm", "nib", "vexp", "bitmap", "tile_vbase"))
+            bl[name] = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).cuda()
+            if i == 0:
+                inf = blob.info()
+                R, C = w.shape
+                sizes[name] = {"shape": [R, C], "bf16_bytes": 2 * R * C,
+                               "huffman_ratio": round(inf.huffman_form_bytes / (2 * R * C), 4),
+                               "palette_ratio": round(inf.palette_form_bytes / (2 * R * C), 4)}
+        dev.append(dl)
+        bf.append(bl)
+    bf16_bytes = sum(v["bf16_bytes"] for v in sizes.values())
+    stream = torch.cuda.current_stream()
+    st = ct.c_void_p(stream.cuda_stream)
+    rows = []
+    for b in batches:
+        X = {n: torch.from_numpy(workloads.attention_activation(0, n, b).view(np.int16)).view(torch.bfloat16).cuda()
+             for n in names}
+        Y = {n: torch.empty((b, workloads.ATTN_SHAPES[n][0]), dtype=torch.float32, device="cuda") for n in names}
+        scr = torch.empty(max(max(uw.scratch_bytes(uw.UW_PIPE_DIRECT, *workloads.ATTN_SHAPES[n], b, 0) for n in names),
+                              8 * 4 * b * 4096 + 256), dtype=torch.uint8, device="cuda")
+        P = lambda t: ct.c_void_p(t.data_ptr())
+        # the bf16 kernel per shape: the fastest hand-written one
+        choice = {}
+        for n in names:
+            _, kname, k, sk = time_bf16([bl[n] for bl in bf], X[n])
+            choice[n] = (k, sk, kname)
+        direct = [[functools.partial(L.uw_matmul, ct.byref(dl[n].dmat), uw.UW_PIPE_DIRECT, 0, 0, P(X[n]), b, P(Y[n]),
+                                     P(scr), ct.c_uint64(scr.numel()), st) for n in names] for dl in dev]
+        hand = [[functools.partial(L.uw_gemm_bf16, P(bl[n]), *workloads.ATTN_SHAPES[n], P(X[n]), b, P(Y[n]),
+                                   choice[n][0], choice[n][1], P(scr), ct.c_uint64(scr.numel()), st) for n in names]
+                for bl in bf]
+
+        def run(calls):
+            for i in range(warmup):
+                for f in calls[i % n_layers]:
+                    uw.check(f(), "attention")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                for f in calls[i % n_layers]:
+                    uw.check(f(), "attention")
+            e1.record(stream)
+            e1.synchronize()
+            return e0.elapsed_time(e1) / steps * 1e3
+
+        t_d, t_b = run(direct), run(hand)
+        with torch.no_grad():
+            tc = [[functools.partial(torch.matmul, X[n], bl[n].t()) for n in names] for bl in bf]
+            for i in range(warmup):
+                for f in tc[i % n_layers]:
+                    f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                for f in tc[i % n_layers]:
+                    f()
+            e1.record(stream)
+            e1.synchronize()
+            t_t = e0.elapsed_time(e1) / steps * 1e3
+        rows.append({"batch": b, "direct_us": round(t_d, 2), "bf16_us": round(t_b, 2), "torch_bf16_us": round(t_t, 2),
+                     "speedup_vs_bf16": round(t_b / t_d, 3), "speedup_vs_torch_bf16": round(t_t / t_d, 3),
+                     "bf16_kernels": {n: choice[n][2] for n in names},
+                     "bf16_equiv_GBps": round(bf16_bytes / t_d / 1e3, 1)})
+        log(f"attention q/k/v/o step B={b}: {rows[-1]}")
+    del dev, bf
+    return {"sizes": sizes, "rows": rows}
+
+
 def time_pipeline(copies, pipeline, kernel, split_k, X, reps=20, warmup=3, stream=None):
     """Seconds per uw_matmul call (pipeline, kernel, split_k), rotating copies."""
     import torch
@@ -837,6 +926,9 @@ def main():
     if not a.no_config34 and not a.no_compare:
         out["layer_steps"] = {"workload": "llama3.1-8b-mlp-layer, direct palette vs bf16, batch 4 and 16",
                               "rows": layer_steps(layers, [4, 16], stream)}
+        out["attention"] = {"workload": "llama3.1-8b attention projections q/k/v/o, one step per layer, 6 seeded "
+                                        "layers rotated",
+                            **attention_bench([1, 4, 16])}
         out["layer_overlap"] = {"workload": "llama3.1-8b-mlp-layer through uw_mlp_layer, us per layer: decodes on the "
                                             "layer's stream vs on a second stream overlapping the matmuls",
                                 "rows": layer_overlap(layers, [1, 16], stream)}

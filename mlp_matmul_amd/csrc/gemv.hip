@@ -418,9 +418,11 @@ void launch_cfg(const MatArgs& a0, hipStream_t s) {
     // activation staging); the wave's tiles must fit one per lane (<= 60)
     static const int ng_env = env_int("UW_GEMV_NG", 0);
     MatArgs a = a0;
-    // measured on MI355X at batch 1: short rows (4096) run best as one row per
-    // group and two groups per wave, long rows (14336) as one row, one group
-    int ng = ng_env > 0 ? ng_env : (NRW == 1 && a.C < 8192 ? 2 : 1);
+    // measured on MI355X at batch 1: short rows (4096) of a tall matrix
+    // (14336 rows) run best as one row per group and two groups per wave;
+    // long rows (14336), and matrices under 8192 rows (attention
+    // projections: more waves to fill the chip), as one row, one group
+    int ng = ng_env > 0 ? ng_env : (NRW == 1 && a.C < 8192 && a.R >= 8192 ? 2 : 1);
     while (ng > 1 && int64_t(ng) * NRW * a.C > 60 * 4096) --ng;
     a.row_groups = ng;
     const int64_t waves = (a.R + int64_t(NRW) * ng - 1) / (int64_t(NRW) * ng);

@@ -105,6 +105,25 @@ def test_decoders_long_tile(torch_cuda):
     assert_matmul_close(Y.cpu().numpy(), w, x, what="long tile: palette transcode + GEMV")
 
 
+@pytest.mark.parametrize("name", ["q", "k", "v", "o"])
+def test_attention_projections_full_size(torch_cuda, name):
+    """The second workload on the same codec: Llama-3.1-8B attention
+    projections at full size.  Decoders bit-exact (K only, the other shapes
+    add nothing new to the decoders), direct-palette matmul through the
+    library's kernel choice within tolerance at batch 1, 4 and 16."""
+    print_case(f"attention projection {name} full size")
+    w = workloads.attention_weight(0, name)
+    dm = uw.compress(w).to_device()
+    if name == "k":
+        _check_decoders(dm, w)
+    for B in (1, 4, 16):
+        x = workloads.attention_activation(0, name, B)
+        Y = uw.matmul(dm, to_dev_bf16(x), pipeline=uw.UW_PIPE_DIRECT, kernel=uw.UW_KERNEL_AUTO, split_k=0,
+                      scratch=uw.alloc_scratch(uw.UW_PIPE_DIRECT, w.shape[0], w.shape[1], B, 0))
+        rows = np.random.default_rng(B).choice(w.shape[0], 256, replace=False)
+        assert_matmul_close(Y.cpu().numpy()[:, rows], w, x, rows=rows, what=f"{name} B={B}")
+
+
 @pytest.mark.parametrize("wl,m", [(2, 0), (2, 2), (4, 1), (5, 2)])
 def test_decoders_full_size(torch_cuda, wl, m):
     print_case(f"decoders full size workload {wl} matrix {m}")

@@ -139,6 +139,12 @@ def test_golden_examples_through_cpp(golden_dir):
         assert b.section("vexp").tobytes().hex() == e["vexp_hex"], name
 
 
+def test_attention_shape_identical():
+    """The second workload (an attention projection, 1024x4096): same bytes as
+    the oracle encoder."""
+    _same_as_oracle(workloads.attention_weight(0, "k"))
+
+
 def test_long_tile_identical():
     """Geometric exponent frequencies give 15-bit codewords and one tile far
     longer than the average (more than 4 KiB of stream): same bytes as the

@@ -158,3 +158,30 @@ def geometric_exponent_matrix(rows: int = 1024, cols: int = 4096, long_tile: int
     sm = rng.integers(0, 256, size=n, dtype=np.int64)
     bits = ((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)
     return bits.astype(np.uint16).reshape(rows, cols)
+
+
+# ------------------------------------------------------------- attention
+# Llama-3.1-8B attention projections (grouped-query: 8 KV heads of 128), the
+# second workload on the same codec.  The page compresses only the MLP
+# weights; no statistics of the attention weights are given, so they are
+# drawn like the MLP's (N(0,0.02) with 0.05 % N(0,0.5) outliers).
+ATTN_SHAPES = {
+    "q": (4096, 4096),
+    "k": (1024, 4096),
+    "v": (1024, 4096),
+    "o": (4096, 4096),
+}
+ATTN_IDS = {"q": 0, "k": 1, "v": 2, "o": 3}
+
+
+def attention_weight(layer: int, name: str, shape=None) -> np.ndarray:
+    """bf16 bits of one attention projection, default_rng([6, layer, id, 0])."""
+    rows, cols = shape if shape is not None else ATTN_SHAPES[name]
+    rng = np.random.default_rng([6, layer, ATTN_IDS[name], 0])
+    return gaussian_weights(rng, rows, cols, 0.02, 5e-4, 0.5)
+
+
+def attention_activation(layer: int, name: str, batch: int) -> np.ndarray:
+    """bf16 bits [batch, cols] fed to one attention projection."""
+    rng = np.random.default_rng([6, layer, ATTN_IDS[name], 1])
+    return gaussian_activations(rng, batch, ATTN_SHAPES[name][1])
