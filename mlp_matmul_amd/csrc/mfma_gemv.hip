@@ -38,14 +38,25 @@ constexpr int kMaxSlice = 4096;  // columns of one wave's K-slice: its row segme
 
 __device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) { return pal_byte(a.pal, uint32_t(i)); }
 
-template <int SRC, int NB, int RB>
+template <int SRC, int NB, int RB, int XQ>
 struct Step {
     u32x4_t w[RB][4];   // BF16: 32 weights; EXP: w[.][0..1] = exponents; PAL: w[.][0] = nibbles
     u32x4_t sm[RB][2];  // EXP, PAL: sign/mantissa bytes
     u32x4_t vx[RB][2];  // PAL: verbatim exponents
     uint32_t verb[RB];  // PAL
-    u32x4_t x[4][NB];   // B fragments: substep s, 16-column block nb (shared by the RB row blocks)
+    u32x4_t x[XQ];      // the wave's activation tile, 16 contiguous bytes per lane and load
 };
+
+// A wave's activation tile in LDS: NB*16 batch rows x one step of columns,
+// rows padded by 16 bytes (conflict-free 16-byte fragment reads and writes).
+constexpr int kXS = kKStep + 8;
+
+// Orders a wave's LDS writes before its (cross-lane) reads and vice versa.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 // 8 rebuilt bf16 pairs (16 weights) from 16 sign/mantissa bytes and exponents.
 __device__ __forceinline__ void join8(const u32x4_t& sm, const uint32_t e7[8], uint32_t out[8]) {
@@ -56,10 +67,17 @@ __device__ __forceinline__ void join8(const u32x4_t& sm, const uint32_t e7[8], u
 // KW wavefronts per workgroup split K; a wavefront owns RB blocks of 16 rows
 // (sharing the activation fragments); PD steps of loads are kept in flight
 // ahead of the step being rebuilt (PD + 1 register sets).
-template <int SRC, int NB, int KW, int PD, int RB>
+// XQ: quads of activation rows loaded per step (4*NB, or fewer when the
+// batch leaves the rest of the 16-row tile empty).
+template <int SRC, int NB, int KW, int PD, int RB, int XQ>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
+    static_assert(XQ >= 1 && XQ <= 4 * NB, "activation row quads");
     __shared__ uint32_t lut[256];
-    __shared__ f32x4_t part[KW][RB][NB][64];
+    // per-wave activation tiles during the K loop; the K-slices' partial
+    // tiles afterwards
+    constexpr int kXBytes = KW * NB * 16 * kXS * 2, kPBytes = KW * RB * NB * 64 * 16;
+    __shared__ __align__(16) uint8_t smem[kXBytes > kPBytes ? kXBytes : kPBytes];
+    auto part = reinterpret_cast<f32x4_t(*)[RB][NB][64]>(smem);
     const int tid = threadIdx.x;
     if (SRC == SRC_PAL)
         for (int i = tid; i < 256; i += 64 * KW) lut[i] = (palb(a, i & 15) << 7) | (palb(a, i >> 4) << 23);
@@ -79,13 +97,16 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
         const uint32_t row = row0 + 16 * r + rl;
         rowc[r] = row < R ? row : 0u;
     }
-    // B rows past the batch read row 0; their output columns are never stored
-    uint32_t xrow[NB];
+    // activation rows of the lane's tile loads (piece j: row 4j + q, 16 bytes
+    // at column 8*(lane%16)); rows past the batch read row 0, their output
+    // columns are never stored
+    uint32_t xrow[XQ];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-        const uint32_t b = nb0 + n * 16 + rl;
-        xrow[n] = b < B ? b : 0u;
+    for (int j = 0; j < XQ; ++j) {
+        const uint32_t b = nb0 + 4 * j + q;
+        xrow[j] = b < B ? b : 0u;
     }
+    uint16_t* const xw = reinterpret_cast<uint16_t*>(smem) + wave * (NB * 16 * kXS);
 
     // verbatim tables of the (at most two) tiles each row segment touches
     uint64_t word0[RB], word1[RB];
@@ -110,7 +131,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
 
     // Plain (cache-retained) loads: a step reads half of each 128-byte line of
     // the 4-bit plane and the next step the other half.
-    auto issue = [&](uint32_t s, Step<SRC, NB, RB>& st) {
+    auto issue = [&](uint32_t s, Step<SRC, NB, RB, XQ>& st) {
         const uint32_t k = s * kKStep + q * 32;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
@@ -138,10 +159,11 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
                 st.vx[r][1] = load16(vb_ptr + voff + 16);
             }
         }
+        // the activation tile of the step: XQ quads of rows x 256 contiguous
+        // bytes (quads past the batch are not loaded: their output columns
+        // are never stored)
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-            for (int n = 0; n < NB; ++n) st.x[sub][n] = load16(a.X + xrow[n] * C + k + 8 * sub);
+        for (int j = 0; j < XQ; ++j) st.x[j] = load16(a.X + xrow[j] * C + s * kKStep + 8 * rl);
         // keep every load of the step here: the scheduler must not sink one
         // into a later rebuild, whose wait would then cover it
         __builtin_amdgcn_sched_barrier(0);
@@ -153,7 +175,20 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
 #pragma unroll
         for (int n = 0; n < NB; ++n) acc[r][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const Step<SRC, NB, RB>& st) {
+    auto compute = [&](const Step<SRC, NB, RB, XQ>& st) {
+        // stage the activation tile (the previous step's fragment reads are
+        // done), then read this step's B fragments: batch row 16n + l%16,
+        // the lane's K run
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < XQ; ++j) *reinterpret_cast<u32x4_t*>(xw + (4 * j + q) * kXS + 8 * rl) = st.x[j];
+        wave_lds_sync();
+        u32x4_t xf[4][NB];
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                xf[sub][n] = *reinterpret_cast<const u32x4_t*>(xw + (16 * n + rl) * kXS + 32 * q + 8 * sub);
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             uint32_t w[16];   // 32 weights as bf16 pairs
@@ -195,7 +230,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
                                                                         w[4 * sub + 3]});
 #pragma unroll
                 for (int n = 0; n < NB; ++n)
-                    acc[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, st.x[sub][n]),
+                    acc[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, xf[sub][n]),
                                                                         acc[r][n], 0, 0, 0);
             }
         }
@@ -211,7 +246,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
         const uint32_t last = s_hi - 1;
         uint32_t s = s_lo;
         if (PD == 1) {
-            Step<SRC, NB, RB> s0, s1;
+            Step<SRC, NB, RB, XQ> s0, s1;
             issue(s_lo, s0);
             for (; s + 1 < s_hi; s += 2) {
                 issue(s + 1, s1);
@@ -221,7 +256,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
             }
             if (s < s_hi) compute(s0);
         } else {
-            Step<SRC, NB, RB> s0, s1, s2;
+            Step<SRC, NB, RB, XQ> s0, s1, s2;
             issue(s_lo, s0);
             issue(min(s_lo + 1, last), s1);
             for (; s + 2 < s_hi; s += 3) {
@@ -236,7 +271,10 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
             if (s + 1 < s_hi) compute(s1);
         }
     }
-    // sum the K-slices: D layout, lane l holds batch column l%16, rows 4*(l/16)..+3
+    // sum the K-slices (their tiles overlay the activation tiles: every wave
+    // is done with its own first): D layout, lane l holds batch column l%16,
+    // rows 4*(l/16)..+3
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -277,7 +315,7 @@ Shape choose_shape(const MatArgs& a) {
     int kw = env_int("UW_SKINNY_KW", 2);
     int pd = env_int("UW_SKINNY_PD", 1);
     int rb = env_int("UW_SKINNY_RB", a.R >= 8192 && a.B <= 32 ? 2 : 1);
-    kw = kw <= 2 ? 2 : (kw <= 4 ? 4 : 8);
+    kw = kw <= 2 ? 2 : (kw <= 4 ? 4 : (kw <= 8 ? 8 : 16));
     while (kw < 8 && (steps + kw - 1) / kw * kKStep > kMaxSlice) kw *= 2;
     pd = pd >= 2 ? 2 : 1;
     rb = rb >= 2 ? 2 : 1;
@@ -287,7 +325,10 @@ Shape choose_shape(const MatArgs& a) {
 template <int SRC, int NB, int KW, int PD, int RB>
 hipError_t launch_shape(const MatArgs& a, hipStream_t s) {
     dim3 grid(unsigned((a.R + 16 * RB - 1) / (16 * RB)), unsigned((a.B + NB * 16 - 1) / (NB * 16)));
-    launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB>, grid, dim3(64 * KW), 0, s, a);
+    // one 16-row batch tile: load only the row quads the batch fills
+    if (NB == 1 && a.B <= 4) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 1>, grid, dim3(64 * KW), 0, s, a);
+    else if (NB == 1 && a.B <= 8) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 2>, grid, dim3(64 * KW), 0, s, a);
+    else launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 4 * NB>, grid, dim3(64 * KW), 0, s, a);
     return hipGetLastError();
 }
 
@@ -295,12 +336,18 @@ hipError_t launch_shape(const MatArgs& a, hipStream_t s) {
 // two batch tiles take a third step set or a second row block, not both.
 template <int SRC, int NB, int KW>
 hipError_t launch_kw(const MatArgs& a, const Shape& sh, hipStream_t s) {
-    if (NB == 4) return launch_shape<SRC, NB, KW, 1, 1>(a, s);
-    constexpr int kNB = NB == 4 ? 1 : NB;                 // keeps the instantiations below well formed
-    if (sh.rb == 1)
-        return sh.pd == 1 ? launch_shape<SRC, kNB, KW, 1, 1>(a, s) : launch_shape<SRC, kNB, KW, 2, 1>(a, s);
-    if (NB == 2 || sh.pd == 1) return launch_shape<SRC, kNB, KW, 1, 2>(a, s);
-    return launch_shape<SRC, kNB, KW, (NB == 1 ? 2 : 1), 2>(a, s);
+    // sixteen waves per workgroup: one batch tile, one row block, one step set
+    // (128 registers at most)
+    if constexpr (KW == 16) {
+        return launch_shape<SRC, 1, 16, 1, 1>(a, s);
+    } else {
+        if (NB == 4) return launch_shape<SRC, NB, KW, 1, 1>(a, s);
+        constexpr int kNB = NB == 4 ? 1 : NB;             // keeps the instantiations below well formed
+        if (sh.rb == 1)
+            return sh.pd == 1 ? launch_shape<SRC, kNB, KW, 1, 1>(a, s) : launch_shape<SRC, kNB, KW, 2, 1>(a, s);
+        if (NB == 2 || sh.pd == 1) return launch_shape<SRC, kNB, KW, 1, 2>(a, s);
+        return launch_shape<SRC, kNB, KW, (NB == 1 ? 2 : 1), 2>(a, s);
+    }
 }
 
 template <int SRC, int NB>
@@ -308,7 +355,10 @@ hipError_t launch_nb(const MatArgs& a, const Shape& sh, hipStream_t s) {
     switch (sh.kw) {
         case 2: return launch_kw<SRC, NB, 2>(a, sh, s);
         case 4: return launch_kw<SRC, NB, 4>(a, sh, s);
-        default: return launch_kw<SRC, NB, 8>(a, sh, s);
+        case 8: return launch_kw<SRC, NB, 8>(a, sh, s);
+        default:
+            if constexpr (NB == 1) return launch_kw<SRC, NB, 16>(a, sh, s);
+            else return launch_kw<SRC, NB, 8>(a, sh, s);
     }
 }
 

@@ -198,7 +198,7 @@ def test_mfma_small_workload(torch_cuda, B):
         assert_matmul_close(Y.cpu().numpy(), w, x, what=f"mfma {name} B={B}")
 
 
-@pytest.mark.parametrize("B", [2, 3, 4, 7, 16, 17, 31, 33, 48, 64, 65, 100])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 31, 33, 48, 64, 65, 100])
 def test_skinny_small_workload(torch_cuda, B):
     print_case(f"skinny small workload B={B}")
     w, _ = workloads.small_matrix()
@@ -230,18 +230,18 @@ def test_skinny_ragged_shapes(torch_cuda, R, C, B):
         assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny {name}")
 
 
-@pytest.mark.parametrize("kw", [2, 4, 8])
+@pytest.mark.parametrize("kw", [2, 4, 8, 16])
 @pytest.mark.parametrize("pd", [1, 2])
 @pytest.mark.parametrize("rb", [1, 2])
 def test_skinny_launch_shapes(torch_cuda, monkeypatch, kw, pd, rb):
     """Every K-split width, prefetch depth and row-block count the launcher
     can pick (the tuning overrides UW_SKINNY_KW / _PD / _RB), on slices of
-    1..9 steps with row segments that straddle tiles, rows past R and each
-    batch-tile count."""
+    1..9 steps with row segments that straddle tiles, rows past R, each
+    batch-tile count and each count of loaded activation row quads."""
     monkeypatch.setenv("UW_SKINNY_KW", str(kw))
     monkeypatch.setenv("UW_SKINNY_PD", str(pd))
     monkeypatch.setenv("UW_SKINNY_RB", str(rb))
-    for R, C, B in [(45, 1152, 5), (33, 4096 + 512, 20), (17, 9216, 64)]:
+    for R, C, B in [(29, 2048 + 256, 3), (45, 1152, 5), (33, 4096 + 512, 20), (17, 9216, 64)]:
         print_case(f"skinny kw={kw} pd={pd} rb={rb} R={R} C={C} B={B}")
         w = workloads.gaussian_weights(np.random.default_rng(R + C + kw + pd), R, C, 0.02, 0.004, 1.0)
         x = _x(C + B, B, C)
