@@ -156,7 +156,7 @@ class Step:
                     row.append(functools.partial(L.uw_matmul, ct.byref(lay.mats[m].dmat), pipe, 0, 0, xin,
                                                  batch, yout, scr, nsc, st))
             silu = functools.partial(L.uw_silu_mul_bf16, P(self.g), P(self.u), batch * F, P(self.h), st)
-            self.fused = (fuse and batch <= 4 and batch * H * 2 <= 32768
+            self.fused = (fuse and batch <= 2 and batch * H * 2 <= 32768
                           and self._plans_direct_gemv(uw, pipe, F, H, batch))
             if self.fused:
                 # gate, up and the SiLU product in one launch (h only)
@@ -173,14 +173,16 @@ class Step:
     def _plans_direct_gemv(uw, pipe, F, H, batch):
         """Gate/up may be fused when they would run as direct-palette GEMVs:
         asked for directly, or what the plan table holds for the gate shape
-        at this batch (no entry: direct palette, GEMV below batch 4)."""
+        at this batch (no entry: direct palette, GEMV at batch 1; the fused
+        launch also beats the separate ones at batch 2, not at 4 where the
+        skinny MFMA kernel takes gate and up)."""
         if pipe == uw.UW_PIPE_DIRECT:
             return True
         if pipe != uw.UW_PIPE_AUTO:
             return False
         plan = uw.plan_lookup(F, H, batch)
         if plan is None:
-            return batch < 4
+            return batch <= 2
         p, k, _ = plan
         return p in (uw.UW_PIPE_DIRECT, uw.UW_PIPE_AUTO) and k == uw.UW_KERNEL_GEMV
 
@@ -382,7 +384,13 @@ def layer_steps(layers, batches, stream, steps=30, warmup=5):
         rows.append({"batch": b, "direct_ms": round(t_d * 1e3, 5), "bf16_ms": round(t_b * 1e3, 5),
                      "speedup_vs_bf16": round(t_b / t_d, 4), "gate_up_fused": sd.fused,
                      "bf16_equiv_GBps": round(3 * 2 * 14336 * 4096 / t_d / 1e9, 1)})
-        log(f"layer step B={b}: direct {rows[-1]['direct_ms']} ms, bf16 {rows[-1]['bf16_ms']} ms")
+        if sd.fused:
+            # the same step with gate and up as separate matmuls and the SiLU product
+            su = Step(layers, b, "direct", stream=stream, fuse=False)
+            rows[-1]["direct_unfused_ms"] = round(time_steps(su, steps, warmup) * 1e3, 5)
+            del su
+        log(f"layer step B={b}: direct {rows[-1]['direct_ms']} ms, bf16 {rows[-1]['bf16_ms']} ms, "
+            f"unfused {rows[-1].get('direct_unfused_ms')}")
         del sd, sb
     return rows
 
@@ -924,8 +932,8 @@ def main():
         out["batch_sweep"] = batch_sweep(layers, batches)
         out["plan"] = [{"shape": r["shape"], "batch": r["batch"], **(r["best"] or {})} for r in out["batch_sweep"]]
     if not a.no_config34 and not a.no_compare:
-        out["layer_steps"] = {"workload": "llama3.1-8b-mlp-layer, direct palette vs bf16, batch 4 and 16",
-                              "rows": layer_steps(layers, [4, 16], stream)}
+        out["layer_steps"] = {"workload": "llama3.1-8b-mlp-layer, direct palette vs bf16, batch 2, 4, 8 and 16",
+                              "rows": layer_steps(layers, [2, 4, 8, 16], stream)}
         out["attention"] = {"workload": "llama3.1-8b attention projections q/k/v/o, one step per layer, 6 seeded "
                                         "layers rotated",
                             **attention_bench([1, 4, 16])}

@@ -220,7 +220,7 @@ int uw_transcode_palette(const uw_dmat* d, uint8_t* out_nib, void* stream);
 /* ---------------------------------------------------------------- matmuls */
 /* Kernel family selector for the matmuls (the autotuner's search space). */
 enum {
-    UW_KERNEL_AUTO = 0,    /* GEMV below batch 4, SKINNY up to 16 (when supported), MFMA above */
+    UW_KERNEL_AUTO = 0,    /* GEMV at batch 1 (below 4 for bf16 weights), SKINNY up to 16 (when supported), MFMA above */
     UW_KERNEL_GEMV = 1,    /* wavefront-reduction GEMV (v_dot2 bf16), batch <= 16 */
     UW_KERNEL_MFMA = 2,    /* bf16 MFMA, 32 rows x 64 or 128 batch columns per wave, any batch; cols <= 65536 */
     UW_KERNEL_SKINNY = 3   /* bf16 MFMA, 16 rows x one K-slice per wave, batch tiles of <= 64;
@@ -314,7 +314,7 @@ int64_t uw_mlp_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t b
  * weights"), y = down . bf16(SiLU(X . gate^T) * (X . up^T)):
  * gate, up [F, H], down [H, F]; X bf16 bits [batch, H]; y fp32 [batch, F].
  * Each matmul runs with UW_KERNEL_AUTO and the library's split-K choice;
- * UW_PIPE_DIRECT fuses gate/up into one launch where uw_mlp_gate_up applies.
+ * UW_PIPE_DIRECT fuses gate/up into one launch (uw_mlp_gate_up) at batch 1-2.
  * With aux_stream NULL every step runs on `stream`.  With an aux_stream (a
  * second stream of the caller's) and a decoding pipeline (FULL, EXP, PAL),
  * the three decodes run there, ordered after the work already on `stream`,

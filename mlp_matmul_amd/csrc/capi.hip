@@ -106,8 +106,12 @@ int device_cus() {
 // the Llama MLP shapes: the GEMV below batch 4, the skinny MFMA kernel up to
 // batch 16, the tiled MFMA kernel from batch 17, which is faster than the
 // skinny kernel at batch 32 and 64 on both shapes).
-int auto_kernel(const uwk::MatArgs& a) {
-    return a.B < 4 ? UW_KERNEL_GEMV : (a.B <= 16 && uwk::mfma_gemv_supported(a) ? UW_KERNEL_SKINNY : UW_KERNEL_MFMA);
+// Measured on MI355X (Llama MLP shapes): the GEMV wins at batch 1 (below
+// batch 4 for bf16 weights), the skinny MFMA kernel from there through 16.
+int auto_kernel(int src, const uwk::MatArgs& a) {
+    const int64_t gemv_below = src == uwk::SRC_BF16 ? 4 : 2;
+    return a.B < gemv_below ? UW_KERNEL_GEMV
+                            : (a.B <= 16 && uwk::mfma_gemv_supported(a) ? UW_KERNEL_SKINNY : UW_KERNEL_MFMA);
 }
 
 // split_k 0: the library's choice, K-slices for the tiled MFMA kernel that
@@ -133,7 +137,7 @@ int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* s
         return uw::fail(UW_EINVAL, std::string(who) + ": sign/mantissa plane missing");
     if (src == uwk::SRC_PAL && a.R * a.C && (!a.bitmap || !a.tile_vbase))
         return uw::fail(UW_EINVAL, std::string(who) + ": verbatim tables missing");
-    if (kernel == UW_KERNEL_AUTO) kernel = auto_kernel(a);
+    if (kernel == UW_KERNEL_AUTO) kernel = auto_kernel(src, a);
     if (kernel == UW_KERNEL_GEMV && a.B > 16)
         return uw::fail(UW_EINVAL, std::string(who) + ": the GEMV kernel takes batch <= 16");
     if (kernel == UW_KERNEL_SKINNY && !uwk::mfma_gemv_supported(a))
@@ -367,7 +371,7 @@ int64_t uw_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch
         a.R = rows;
         a.C = cols;
         a.B = batch;
-        split_k = cols % uw::kGroup ? 1 : resolve_split(a, auto_kernel(a), 0);
+        split_k = cols % uw::kGroup ? 1 : resolve_split(a, auto_kernel(uwk::SRC_PAL, a), 0);
     }
     uint64_t n = align256(decoded_bytes(pipeline, rows, cols));
     if (split_k > 1) n += align256(uint64_t(split_k) * uint64_t(batch) * uint64_t(rows) * 4);
@@ -483,9 +487,10 @@ int uw_mlp_layer(const uw_dmat* gate, const uw_dmat* up, const uw_dmat* down, in
     int rc;
 
     if (pipeline == UW_PIPE_DIRECT) {
-        // nothing to decode; gate/up fused into one launch where it applies
+        // nothing to decode; gate/up fused into one launch at batch 1-2 (at
+        // batch 4 separate skinny MFMA launches measured faster on MI355X)
         bool fused = false;
-        if (batch <= 4 && batch * H * 2 <= 32768 && H <= 60 * 4096) {
+        if (batch <= 2 && batch * H * 2 <= 32768 && H <= 60 * 4096) {
             rc = uw_mlp_gate_up(gate, up, X, batch, h, nullptr, nullptr, stream);
             if (rc && rc != UW_EUNSUPPORTED) return rc;
             fused = rc == UW_OK;

@@ -11,19 +11,27 @@
 // stream, so the kernel is laid out for parallelism and coalescing rather
 // than reuse: a wavefront owns 16 weight rows and one K-slice (the 2, 4 or 8
 // wavefronts of a workgroup split K and sum their partial tiles in LDS), so a
-// Llama matrix runs several thousand wavefronts.  Per step of 128 columns,
-// lane l holds 32 consecutive weights of row l%16 (columns 32*(l/16)..+32):
-// their compressed bytes are loaded with 16-byte loads, rebuilt to bf16 in
-// registers and fed, 8 at a time, as the A operand of four
-// v_mfma_f32_16x16x32_bf16.  The K order inside an MFMA is a free
-// permutation when A and B agree, so each lane's B fragments are the
-// matching 8-element runs of the activation rows, read straight from L2 (the
-// activations of a launch are a few hundred KiB and stay cache resident).
-// All loads of steps t+1..t+PD are issued before step t is rebuilt (PD + 1
-// register sets, no data-dependent branch around a load); the verbatim bitmap words and
-// bases of the (at most two) tiles a lane's row segment touches are loaded
-// once, so the verbatim flag and slot of every step are register arithmetic
-// and a verbatim lane's 32 raw exponents come with the step's other loads.
+// Llama matrix runs thousands of wavefronts.  Per step of 128 columns, lane
+// l feeds row l%16 and columns 32*(l/16)..+32 into four
+// v_mfma_f32_16x16x32_bf16 (the K order inside an MFMA is a free permutation
+// when A and B agree, so each lane's B fragments are the matching 8-element
+// runs of the activation rows).
+//   Loads.  That operand layout puts consecutive lanes on consecutive rows,
+// and a 16-byte load whose lanes sit in different rows costs the L1 one
+// access per lane: loaded that way, the weight planes and the activation
+// fragments kept the L1 saturated (measured on MI355X at batch 16: the
+// address unit stalled on it most of the kernel).  So every plane of a step
+// is loaded as contiguous row runs (a 128-byte sign/mantissa row by 8 lanes
+// side by side, the 4-bit row by 4, the activation rows by 16) into
+// registers, written to a wave-private LDS region and read back in the MFMA
+// layout, first the weight planes, then the activation tile over the same
+// region; only the activation rows the batch fills are loaded.  The weights
+// are rebuilt to bf16 in registers from there.  All loads of steps
+// t+1..t+PD are issued before step t is rebuilt (PD + 1 register sets, no
+// data-dependent branch around a load); the verbatim bitmap words and bases
+// of the (at most two) tiles a lane's row segment touches are loaded once, so
+// the verbatim flag and slot of every step are register arithmetic, and a
+// verbatim lane's 32 raw exponents come with the step's other loads.
 #include <cstdlib>
 
 #include "device_common.h"
@@ -38,11 +46,23 @@ constexpr int kMaxSlice = 4096;  // columns of one wave's K-slice: its row segme
 
 __device__ __forceinline__ uint32_t palb(const MatArgs& a, int i) { return pal_byte(a.pal, uint32_t(i)); }
 
+// Weight planes of a source, each staged per step as 16 rows x bpr bytes:
+// bf16 (256 bytes a row); exponents (128) + sign/mantissa (128); 4-bit
+// indices (64) + sign/mantissa (128).
+template <int SRC>
+struct Planes {
+    static constexpr int n = SRC == SRC_BF16 ? 1 : 2;
+    static constexpr int bpr0 = SRC == SRC_BF16 ? 256 : (SRC == SRC_EXP ? 128 : 64);
+    static constexpr int bpr1 = 128;
+    static constexpr int pieces = (bpr0 + (n > 1 ? bpr1 : 0)) / 64;   // 16-byte loads per lane and row block
+    // LDS bytes of one row block's planes (rows padded by 16 bytes)
+    static constexpr int bytes = 16 * (bpr0 + 16) + (n > 1 ? 16 * (bpr1 + 16) : 0);
+};
+
 template <int SRC, int NB, int RB, int XQ>
 struct Step {
-    u32x4_t w[RB][4];   // BF16: 32 weights; EXP: w[.][0..1] = exponents; PAL: w[.][0] = nibbles
-    u32x4_t sm[RB][2];  // EXP, PAL: sign/mantissa bytes
-    u32x4_t vx[RB][2];  // PAL: verbatim exponents
+    u32x4_t w[RB][Planes<SRC>::pieces];   // weight planes, contiguous row runs (not the MFMA layout)
+    u32x4_t vx[RB][2];  // PAL: verbatim exponents (MFMA layout)
     uint32_t verb[RB];  // PAL
     u32x4_t x[XQ];      // the wave's activation tile, 16 contiguous bytes per lane and load
 };
@@ -73,9 +93,13 @@ template <int SRC, int NB, int KW, int PD, int RB, int XQ>
 __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
     static_assert(XQ >= 1 && XQ <= 4 * NB, "activation row quads");
     __shared__ uint32_t lut[256];
-    // per-wave activation tiles during the K loop; the K-slices' partial
-    // tiles afterwards
-    constexpr int kXBytes = KW * NB * 16 * kXS * 2, kPBytes = KW * RB * NB * 64 * 16;
+    // a region per wave during the K loop, holding a step's weight planes and
+    // then its activation tile; the K-slices' partial tiles afterwards
+    using PL = Planes<SRC>;
+    constexpr int kWBytes = RB * PL::bytes, kXTBytes = NB * 16 * kXS * 2;
+    constexpr int kRegion = kWBytes > kXTBytes ? kWBytes : kXTBytes;
+    constexpr int kXBytes = KW * kRegion, kPBytes = KW * RB * NB * 64 * 16;
+    static_assert(kXBytes <= 150 * 1024 && kPBytes <= 150 * 1024, "LDS");
     __shared__ __align__(16) uint8_t smem[kXBytes > kPBytes ? kXBytes : kPBytes];
     auto part = reinterpret_cast<f32x4_t(*)[RB][NB][64]>(smem);
     const int tid = threadIdx.x;
@@ -106,7 +130,8 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
         const uint32_t b = nb0 + 4 * j + q;
         xrow[j] = b < B ? b : 0u;
     }
-    uint16_t* const xw = reinterpret_cast<uint16_t*>(smem) + wave * (NB * 16 * kXS);
+    uint8_t* const region = smem + wave * kRegion;
+    uint16_t* const xw = reinterpret_cast<uint16_t*>(region);
 
     // verbatim tables of the (at most two) tiles each row segment touches
     uint64_t word0[RB], word1[RB];
@@ -129,25 +154,31 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
     const uint16_t* wb = static_cast<const uint16_t*>(a.w);
     const uint8_t* w8 = static_cast<const uint8_t*>(a.w);
 
-    // Plain (cache-retained) loads: a step reads half of each 128-byte line of
-    // the 4-bit plane and the next step the other half.
+    // The weight planes of a step go out as contiguous runs of each row (the
+    // MFMA layout puts consecutive lanes on consecutive rows, which would cost
+    // an L1 access per lane): piece i of plane bpr covers 16 bytes, lanes
+    // 16/bpr.. of a row side by side.  Plain (cache-retained) loads.
+    const uint8_t* const plane0 = SRC == SRC_BF16 ? reinterpret_cast<const uint8_t*>(wb) : w8;
+    auto plane_piece = [&](const uint8_t* base, int bpr, int r, int i, uint32_t s) {
+        const uint32_t p = uint32_t(i) * 64u + uint32_t(lane), cpr = uint32_t(bpr) / 16u;
+        const uint32_t row = p / cpr, chunk = p % cpr;
+        uint32_t rowg = row0 + 16u * uint32_t(r) + row;
+        rowg = rowg < R ? rowg : 0u;
+        return load16(base + uint64_t(rowg) * (uint64_t(bpr) * C / kKStep) + uint64_t(s) * bpr + chunk * 16u);
+    };
     auto issue = [&](uint32_t s, Step<SRC, NB, RB, XQ>& st) {
         const uint32_t k = s * kKStep + q * 32;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const uint32_t pos = rowc[r] * C + k;
-            if (SRC == SRC_BF16) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) st.w[r][i] = load16(wb + pos + 8 * i);
-            } else if (SRC == SRC_EXP) {
-                st.w[r][0] = load16(w8 + pos);
-                st.w[r][1] = load16(w8 + pos + 16);
-                st.sm[r][0] = load16(a.sm + pos);
-                st.sm[r][1] = load16(a.sm + pos + 16);
-            } else {
-                st.w[r][0] = load16(w8 + pos / 2);
-                st.sm[r][0] = load16(a.sm + pos);
-                st.sm[r][1] = load16(a.sm + pos + 16);
+            for (int i = 0; i < PL::bpr0 / 64; ++i) st.w[r][i] = plane_piece(plane0, PL::bpr0, r, i, s);
+            if (PL::n > 1) {
+#pragma unroll
+                for (int i = 0; i < PL::bpr1 / 64; ++i)
+                    st.w[r][PL::bpr0 / 64 + i] = plane_piece(a.sm, PL::bpr1, r, i, s);
+            }
+            if (SRC == SRC_PAL) {
+                const uint32_t pos = rowc[r] * C + k;
                 const bool second = (pos >> 12) != t0[r];
                 const uint64_t word = second ? word1[r] : word0[r];
                 const uint32_t vbase = second ? vb1[r] : vb0[r];
@@ -176,9 +207,45 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
         for (int n = 0; n < NB; ++n) acc[r][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const Step<SRC, NB, RB, XQ>& st) {
-        // stage the activation tile (the previous step's fragment reads are
-        // done), then read this step's B fragments: batch row 16n + l%16,
-        // the lane's K run
+        // the weight planes through the wave's region (the previous step's
+        // reads of it are done), read back in the MFMA layout: lane l, row
+        // l%16, the lane's run of 32 weights
+        wave_lds_sync();
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            uint8_t* const rb = region + r * PL::bytes;
+#pragma unroll
+            for (int i = 0; i < PL::pieces; ++i) {
+                const bool p1 = i >= PL::bpr0 / 64;
+                const int bpr = p1 ? PL::bpr1 : PL::bpr0;
+                const uint32_t pp = uint32_t(p1 ? i - PL::bpr0 / 64 : i) * 64u + uint32_t(lane);
+                const uint32_t cpr = uint32_t(bpr) / 16u;
+                uint8_t* const dst = rb + (p1 ? 16 * (PL::bpr0 + 16) : 0) + (pp / cpr) * (bpr + 16) + (pp % cpr) * 16u;
+                *reinterpret_cast<u32x4_t*>(dst) = st.w[r][i];
+            }
+        }
+        wave_lds_sync();
+        u32x4_t wl[RB][4], sml[RB][2];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const uint8_t* const rb = region + r * PL::bytes;
+            if (SRC == SRC_BF16) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wl[r][j] = *reinterpret_cast<const u32x4_t*>(rb + rl * 272u + 64u * q + 16u * j);
+            } else {
+                const uint8_t* const p1 = rb + 16 * (PL::bpr0 + 16);
+                if (SRC == SRC_EXP) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) wl[r][j] = *reinterpret_cast<const u32x4_t*>(rb + rl * 144u + 32u * q + 16u * j);
+                } else {
+                    wl[r][0] = *reinterpret_cast<const u32x4_t*>(rb + rl * 80u + 16u * q);
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) sml[r][j] = *reinterpret_cast<const u32x4_t*>(p1 + rl * 144u + 32u * q + 16u * j);
+            }
+        }
+        // then the activation tile over the same region, and this step's B
+        // fragments: batch row 16n + l%16, the lane's K run
         wave_lds_sync();
 #pragma unroll
         for (int j = 0; j < XQ; ++j) *reinterpret_cast<u32x4_t*>(xw + (4 * j + q) * kXS + 8 * rl) = st.x[j];
@@ -194,15 +261,15 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
             uint32_t w[16];   // 32 weights as bf16 pairs
             if (SRC == SRC_BF16) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) w[i] = st.w[r][i >> 2][i & 3];
+                for (int i = 0; i < 16; ++i) w[i] = wl[r][i >> 2][i & 3];
             } else if (SRC == SRC_EXP) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     uint32_t e7[8];
 #pragma unroll
                     for (int p = 0; p < 8; ++p)
-                        e7[p] = (p & 1) ? exp_pair<1>(st.w[r][h][p >> 1]) : exp_pair<0>(st.w[r][h][p >> 1]);
-                    join8(st.sm[r][h], e7, w + 8 * h);
+                        e7[p] = (p & 1) ? exp_pair<1>(wl[r][h][p >> 1]) : exp_pair<0>(wl[r][h][p >> 1]);
+                    join8(sml[r][h], e7, w + 8 * h);
                 }
             } else {
 #pragma unroll
@@ -210,7 +277,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
                     uint32_t e7[8];
 #pragma unroll
                     for (int p = 0; p < 8; ++p) {
-                        const uint32_t nbyte = (st.w[r][0][2 * h + (p >> 2)] >> (8 * (p & 3))) & 0xFFu;
+                        const uint32_t nbyte = (wl[r][0][2 * h + (p >> 2)] >> (8 * (p & 3))) & 0xFFu;
                         e7[p] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + (nbyte << 2));
                     }
                     if (__builtin_amdgcn_ballot_w64(st.verb[r] != 0)) {   // rare: raw exponents for verbatim lanes
@@ -221,7 +288,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
                             e7[p] = st.verb[r] ? er : e7[p];
                         }
                     }
-                    join8(st.sm[r][h], e7, w + 8 * h);
+                    join8(sml[r][h], e7, w + 8 * h);
                 }
             }
 #pragma unroll
@@ -305,18 +372,20 @@ int env_int(const char* name, int dflt) {
     return e && *e ? atoi(e) : dflt;
 }
 
-// K-split width, prefetch depth and row blocks per wavefront (measured on
-// the Llama MLP shapes at batch 2..64; UW_SKINNY_KW / _PD / _RB override for
+// K-split width, prefetch depth and row blocks per wavefront, as measured on
+// the Llama MLP shapes at batch 2..16 (UW_SKINNY_KW / _PD / _RB override for
 // tuning).  The slice of one wave must stay within kMaxSlice columns, which
-// sets the smallest K-split; two row blocks per wave halve the activation
-// traffic but also the number of workgroups, so only tall matrices take them.
+// sets the smallest K-split, and the smallest is best; one row block per
+// wave (with the tiles staged through LDS a second block saves little
+// activation traffic and halves the workgroups); two steps in flight for long
+// slices (>= 24 steps) at batch <= 8.
 Shape choose_shape(const MatArgs& a) {
     const int64_t steps = a.C / kKStep;
     int kw = env_int("UW_SKINNY_KW", 2);
-    int pd = env_int("UW_SKINNY_PD", 1);
-    int rb = env_int("UW_SKINNY_RB", a.R >= 8192 && a.B <= 32 ? 2 : 1);
-    kw = kw <= 2 ? 2 : (kw <= 4 ? 4 : (kw <= 8 ? 8 : 16));
+    int rb = env_int("UW_SKINNY_RB", 1);
+    kw = kw <= 2 ? 2 : (kw <= 4 ? 4 : 8);
     while (kw < 8 && (steps + kw - 1) / kw * kKStep > kMaxSlice) kw *= 2;
+    int pd = env_int("UW_SKINNY_PD", a.B <= 8 && steps / kw >= 24 ? 2 : 1);
     pd = pd >= 2 ? 2 : 1;
     rb = rb >= 2 ? 2 : 1;
     return {kw, pd, rb};
@@ -326,27 +395,33 @@ template <int SRC, int NB, int KW, int PD, int RB>
 hipError_t launch_shape(const MatArgs& a, hipStream_t s) {
     dim3 grid(unsigned((a.R + 16 * RB - 1) / (16 * RB)), unsigned((a.B + NB * 16 - 1) / (NB * 16)));
     // one 16-row batch tile: load only the row quads the batch fills
-    if (NB == 1 && a.B <= 4) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 1>, grid, dim3(64 * KW), 0, s, a);
-    else if (NB == 1 && a.B <= 8) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 2>, grid, dim3(64 * KW), 0, s, a);
-    else launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 4 * NB>, grid, dim3(64 * KW), 0, s, a);
+    if constexpr (NB == 1) {
+        if (a.B <= 4) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 1>, grid, dim3(64 * KW), 0, s, a);
+        else if (a.B <= 8) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 2>, grid, dim3(64 * KW), 0, s, a);
+        else launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 4>, grid, dim3(64 * KW), 0, s, a);
+    } else {
+        launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 4 * NB>, grid, dim3(64 * KW), 0, s, a);
+    }
     return hipGetLastError();
 }
 
-// Register budget: four batch tiles take one step set and one row block;
-// two batch tiles take a third step set or a second row block, not both.
+// Register budget (a workgroup of KW waves must fit one CU: 8 waves leave
+// 256 registers a wave): four batch tiles take one step set and one row
+// block, and at most four waves; two batch tiles take a third step set or a
+// second row block, not both; eight waves take one step set, and a second
+// row block only with one batch tile.
 template <int SRC, int NB, int KW>
 hipError_t launch_kw(const MatArgs& a, const Shape& sh, hipStream_t s) {
-    // sixteen waves per workgroup: one batch tile, one row block, one step set
-    // (128 registers at most)
-    if constexpr (KW == 16) {
-        return launch_shape<SRC, 1, 16, 1, 1>(a, s);
+    if constexpr (NB == 4) {
+        return launch_shape<SRC, 4, KW, 1, 1>(a, s);
+    } else if constexpr (KW == 8) {
+        if (NB == 1 && sh.rb == 2) return launch_shape<SRC, 1, 8, 1, 2>(a, s);
+        return launch_shape<SRC, NB, 8, 1, 1>(a, s);
     } else {
-        if (NB == 4) return launch_shape<SRC, NB, KW, 1, 1>(a, s);
-        constexpr int kNB = NB == 4 ? 1 : NB;             // keeps the instantiations below well formed
         if (sh.rb == 1)
-            return sh.pd == 1 ? launch_shape<SRC, kNB, KW, 1, 1>(a, s) : launch_shape<SRC, kNB, KW, 2, 1>(a, s);
-        if (NB == 2 || sh.pd == 1) return launch_shape<SRC, kNB, KW, 1, 2>(a, s);
-        return launch_shape<SRC, kNB, KW, (NB == 1 ? 2 : 1), 2>(a, s);
+            return sh.pd == 1 ? launch_shape<SRC, NB, KW, 1, 1>(a, s) : launch_shape<SRC, NB, KW, 2, 1>(a, s);
+        if (NB == 2 || sh.pd == 1) return launch_shape<SRC, NB, KW, 1, 2>(a, s);
+        return launch_shape<SRC, NB, KW, (NB == 1 ? 2 : 1), 2>(a, s);
     }
 }
 
@@ -355,9 +430,8 @@ hipError_t launch_nb(const MatArgs& a, const Shape& sh, hipStream_t s) {
     switch (sh.kw) {
         case 2: return launch_kw<SRC, NB, 2>(a, sh, s);
         case 4: return launch_kw<SRC, NB, 4>(a, sh, s);
-        case 8: return launch_kw<SRC, NB, 8>(a, sh, s);
         default:
-            if constexpr (NB == 1) return launch_kw<SRC, NB, 16>(a, sh, s);
+            if constexpr (NB == 4) return hipErrorNotSupported;   // never chosen: see launch_src
             else return launch_kw<SRC, NB, 8>(a, sh, s);
     }
 }
@@ -366,7 +440,8 @@ template <int SRC>
 hipError_t launch_src(const MatArgs& a, hipStream_t s) {
     const Shape sh = choose_shape(a);
     if (a.B <= 16) return launch_nb<SRC, 1>(a, sh, s);
-    if (a.B <= 32) return launch_nb<SRC, 2>(a, sh, s);
+    // 64-column batch tiles at most four waves wide; 32-column ones otherwise
+    if (a.B <= 32 || sh.kw > 4) return launch_nb<SRC, 2>(a, sh, s);
     return launch_nb<SRC, 4>(a, sh, s);
 }
 
