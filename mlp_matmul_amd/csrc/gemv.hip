@@ -412,15 +412,6 @@ int env_int(const char* name, int dflt) {
     return e ? atoi(e) : dflt;
 }
 
-template <int SRC, int MB, int NRW, bool XLDS, int D>
-void launch_depth(const MatArgs& a, unsigned grid, size_t lds, hipStream_t s) {
-    uint16_t* const no_h = nullptr;
-    if (a.C % kSlab == 0)
-        launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS, false, D>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
-    else
-        launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS, false, D>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
-}
-
 template <int SRC, int MB, int NRW, bool XLDS>
 void launch_cfg(const MatArgs& a0, hipStream_t s) {
     // row groups per wave: long-lived waves amortise the per-wave start (tables,
@@ -441,10 +432,19 @@ void launch_cfg(const MatArgs& a0, hipStream_t s) {
     // batch-1 fused gate/up launch 32.9 -> 31.4 us); UW_GEMV_DEPTH=1 for one
     static const int depth_env = env_int("UW_GEMV_DEPTH", 0);
     const int depth = MB <= 2 ? (depth_env > 0 ? depth_env : 2) : 1;
-    if (MB == 1 && NRW == 1 && depth >= 4) return launch_depth<SRC, MB, NRW, XLDS, (MB == 1 && NRW == 1) ? 4 : 1>(a, grid, lds, s);
-    if (MB == 1 && NRW == 1 && depth == 3) return launch_depth<SRC, MB, NRW, XLDS, (MB == 1 && NRW == 1) ? 3 : 1>(a, grid, lds, s);
-    if (depth >= 2) return launch_depth<SRC, MB, NRW, XLDS, MB <= 2 ? 2 : 1>(a, grid, lds, s);
-    launch_depth<SRC, MB, NRW, XLDS, 1>(a, grid, lds, s);
+    uint16_t* const no_h = nullptr;
+    if (depth >= 2 && MB <= 2) {
+        constexpr int D = MB <= 2 ? 2 : 1;
+        if (a.C % kSlab == 0)
+            launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS, false, D>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
+        else
+            launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS, false, D>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
+        return;
+    }
+    if (a.C % kSlab == 0)
+        launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS, false, 1>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
+    else
+        launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS, false, 1>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
 }
 
 template <int SRC, int MB, int NRW>
