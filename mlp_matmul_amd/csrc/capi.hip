@@ -8,6 +8,7 @@
 //   pal       palette transcode -> nibbles in scratch -> reconstructive matmul
 //   direct    reconstructive matmul on nibbles made once at load time
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <cstring>
 #include <string>
@@ -93,12 +94,18 @@ int run_decode(const uw_dmat* d, void* out, int mode, void* stream, const char* 
 
 // Compute units of the current device (256 if it cannot be queried).
 int device_cus() {
+    static std::atomic<int> known[64];                 // per device, 0 until queried
     int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                hipSuccess || cus <= 0) {
+    if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
         return 256;
     }
+    if (dev >= 0 && dev < 64 && (cus = known[dev].load(std::memory_order_relaxed)) > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (dev >= 0 && dev < 64) known[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
@@ -152,6 +159,7 @@ int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* s
                                scratch_bytes < uint64_t(split_k) * uint64_t(a.B) * uint64_t(a.R) * 4))
             split_k >>= 1;
     }
+    a.cus = device_cus();
     if (kernel == UW_KERNEL_MFMA && !uwk::mfma_supported(a))
         return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": the tiled MFMA kernel takes cols <= 65536");
     hipError_t e;

@@ -42,6 +42,7 @@ struct MatArgs {
     int64_t R, C, B;
     int32_t split_k;
     int32_t row_groups;         // GEMV: groups of NRW rows one wave walks in turn
+    int32_t cus;                // compute units of the device (launch shapes that fill it); 0: 256
     uint32_t pal[4];
 };
 

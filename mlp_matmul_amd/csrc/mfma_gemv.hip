@@ -373,16 +373,24 @@ int env_int(const char* name, int dflt) {
 }
 
 // K-split width, prefetch depth and row blocks per wavefront, as measured on
-// the Llama MLP shapes at batch 2..16 (UW_SKINNY_KW / _PD / _RB override for
-// tuning).  The slice of one wave must stay within kMaxSlice columns, which
-// sets the smallest K-split, and the smallest is best; one row block per
-// wave (with the tiles staged through LDS a second block saves little
+// the Llama MLP and attention shapes at batch 2..16 (UW_SKINNY_KW / _PD / _RB
+// override for tuning).  The K-split is the smallest that gives about one
+// wave per SIMD (a 14336-row matrix: 2; 4096 rows: 4; 1024 rows: 8), and at
+// least what keeps one wave's slice within kMaxSlice columns; one row block
+// per wave (with the tiles staged through LDS a second block saves little
 // activation traffic and halves the workgroups); two steps in flight for long
 // slices (>= 24 steps) at batch <= 8.
 Shape choose_shape(const MatArgs& a) {
     const int64_t steps = a.C / kKStep;
-    int kw = env_int("UW_SKINNY_KW", 2);
     int rb = env_int("UW_SKINNY_RB", 1);
+    const int kw_env = env_int("UW_SKINNY_KW", 0);
+    int kw = kw_env;
+    if (kw <= 0) {
+        const int64_t simds = 4 * int64_t(a.cus > 0 ? a.cus : 256);
+        const int64_t waves_per_kw = (a.R + 16 * rb - 1) / (16 * rb) * ((a.B + 63) / 64);
+        kw = 2;
+        while (kw < 8 && waves_per_kw * kw < simds) kw *= 2;
+    }
     kw = kw <= 2 ? 2 : (kw <= 4 ? 4 : 8);
     while (kw < 8 && (steps + kw - 1) / kw * kKStep > kMaxSlice) kw *= 2;
     int pd = env_int("UW_SKINNY_PD", a.B <= 8 && steps / kw >= 24 ? 2 : 1);
