@@ -784,6 +784,11 @@ def cpu_baseline(frac_rows=8, min_seconds=10.0):
 
 
 # --------------------------------------------------------------- profiles
+def kernel_source(kernel_tag):
+    """The source file of the kernel a profile tag names (gemv_*, skinny_*, mfma_*)."""
+    return {"gemv": "gemv.hip", "skinny": "mfma_gemv.hip", "mfma": "gemm_mfma.hip"}[kernel_tag.split("_")[0]]
+
+
 def traffic_from_profiles(kernel_tag):
     """HBM bytes per launch from the committed rocprofv3 counter summary (two
     --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), if the
@@ -797,7 +802,7 @@ def traffic_from_profiles(kernel_tag):
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
     if not m or not t:
         return None
-    src = open(os.path.join(ROOT, "mlp_matmul_amd", "csrc", "gemv.hip"), "rb").read()
+    src = open(os.path.join(ROOT, "mlp_matmul_amd", "csrc", kernel_source(kernel_tag)), "rb").read()
     src += open(os.path.join(ROOT, "mlp_matmul_amd", "csrc", "device_common.h"), "rb").read()
     if hashlib.sha256(src).hexdigest()[:16] != m.group(1)[:16]:
         return None
@@ -861,8 +866,10 @@ def main():
     dom = max(range(nl), key=lambda m: per_kernel[m]["total_s"])
     achieved = per_kernel[dom]["bytes"] / per_kernel[dom]["avg_s"] / 1e9
     achieved_all = bytes_.sum() / durs.sum() / 1e9
+    # the kernel family UW_KERNEL_AUTO takes for the rebuilding sources
+    family = "gemv" if B == 1 else ("skinny" if B <= 16 else "mfma")
     kernel_names = (["fused gate/up GEMV + SiLU (palette source)", "down GEMV (palette source)"] if step.fused else
-                    [f"{n} recon matmul ({'gemv' if B < 16 else 'mfma'})" for n in ("gate", "up", "down")])
+                    [f"{n} recon matmul ({family})" for n in ("gate", "up", "down")])
     # the step time is the faster of the two valid timings
     use_graph = graph is not None and graph_ok and graph < eager
     sec = graph if use_graph else eager
@@ -886,8 +893,8 @@ def main():
                            "graph_matches_eager": ok_}
         log(f"ms/step by pipeline: {extra}")
 
-    tag = f"gemv_gateup_pal_llama_mlp_b{B}" if step.fused else f"gemv_recon_pal_llama_mlp_b{B}"
-    traffic = traffic_from_profiles(tag) if B < 16 and a.pipeline == "direct" else None
+    tag = f"gemv_gateup_pal_llama_mlp_b{B}" if step.fused else f"{family}_recon_pal_llama_mlp_b{B}"
+    traffic = traffic_from_profiles(tag) if a.pipeline == "direct" else None
     out = {
         "metric": METRIC,
         "value": round(weights_bf16_bytes / sec / 1e9, 2),
