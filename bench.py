@@ -156,8 +156,7 @@ class Step:
                     row.append(functools.partial(L.uw_matmul, ct.byref(lay.mats[m].dmat), pipe, 0, 0, xin,
                                                  batch, yout, scr, nsc, st))
             silu = functools.partial(L.uw_silu_mul_bf16, P(self.g), P(self.u), batch * F, P(self.h), st)
-            self.fused = (fuse and batch <= 2 and batch * H * 2 <= 32768
-                          and self._plans_direct_gemv(uw, pipe, F, H, batch))
+            self.fused = fuse and batch <= 16 and self._plans_direct(uw, pipe, F, H, batch)
             if self.fused:
                 # gate, up and the SiLU product in one launch (h only)
                 gu = functools.partial(L.uw_mlp_gate_up, ct.byref(lay.mats[0].dmat), ct.byref(lay.mats[1].dmat),
@@ -170,21 +169,22 @@ class Step:
                 self.bytes.append([palette_bytes(lay.info[m], batch) for m in range(3)])
 
     @staticmethod
-    def _plans_direct_gemv(uw, pipe, F, H, batch):
-        """Gate/up may be fused when they would run as direct-palette GEMVs:
-        asked for directly, or what the plan table holds for the gate shape
-        at this batch (no entry: direct palette, GEMV at batch 1; the fused
-        launch also beats the separate ones at batch 2, not at 4 where the
-        skinny MFMA kernel takes gate and up)."""
+    def _plans_direct(uw, pipe, F, H, batch):
+        """Gate/up may be fused (uw_mlp_gate_up: the GEMV pair at batch 1-2,
+        the skinny MFMA pair at 3-16) when they would run on the direct-palette
+        form with those kernels: asked for directly, or what the plan table
+        holds for the gate shape at this batch (no entry: direct palette with
+        the library's kernel choice)."""
         if pipe == uw.UW_PIPE_DIRECT:
             return True
         if pipe != uw.UW_PIPE_AUTO:
             return False
         plan = uw.plan_lookup(F, H, batch)
         if plan is None:
-            return batch <= 2
+            return True
         p, k, _ = plan
-        return p in (uw.UW_PIPE_DIRECT, uw.UW_PIPE_AUTO) and k == uw.UW_KERNEL_GEMV
+        want = uw.UW_KERNEL_GEMV if batch <= 2 else uw.UW_KERNEL_SKINNY
+        return p in (uw.UW_PIPE_DIRECT, uw.UW_PIPE_AUTO) and k in (want, uw.UW_KERNEL_AUTO)
 
     def run(self, i):
         for f in self.calls[i % len(self.layers)]:
@@ -868,8 +868,9 @@ def main():
     achieved_all = bytes_.sum() / durs.sum() / 1e9
     # the kernel family UW_KERNEL_AUTO takes for the rebuilding sources
     family = "gemv" if B == 1 else ("skinny" if B <= 16 else "mfma")
-    kernel_names = (["fused gate/up GEMV + SiLU (palette source)", "down GEMV (palette source)"] if step.fused else
-                    [f"{n} recon matmul ({family})" for n in ("gate", "up", "down")])
+    pair = "GEMV" if B <= 2 else "skinny MFMA"
+    kernel_names = ([f"fused gate/up {pair} + SiLU (palette source)", f"down {family} (palette source)"]
+                    if step.fused else [f"{n} recon matmul ({family})" for n in ("gate", "up", "down")])
     # the step time is the faster of the two valid timings
     use_graph = graph is not None and graph_ok and graph < eager
     sec = graph if use_graph else eager
@@ -893,7 +894,8 @@ def main():
                            "graph_matches_eager": ok_}
         log(f"ms/step by pipeline: {extra}")
 
-    tag = f"gemv_gateup_pal_llama_mlp_b{B}" if step.fused else f"{family}_recon_pal_llama_mlp_b{B}"
+    tag = (f"{'gemv' if B <= 2 else 'skinny'}_gateup_pal_llama_mlp_b{B}" if step.fused
+           else f"{family}_recon_pal_llama_mlp_b{B}")
     traffic = traffic_from_profiles(tag) if a.pipeline == "direct" else None
     out = {
         "metric": METRIC,

@@ -290,17 +290,22 @@ int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, voi
 
 /* Fused gate/up projections of a SwiGLU MLP block on the direct-palette
  * form ("How the reconstructive matmul works": both compressed matrices are
- * rebuilt on chip inside one GEMV launch; the gate, up and down matrices are
- * the ones "How to compress model weights effectively" compresses):
- *   g = X . gate^T,  u = X . up^T  (fp32 accumulation, as uw_matmul with
- *   UW_PIPE_DIRECT and the GEMV kernel), h[b][r] = bf16_rne(SiLU(g) * u)
- * with the same SiLU arithmetic as uw_silu_mul_bf16, so h, g and u are
- * bit-identical to the unfused three calls.
+ * rebuilt on chip inside one launch; the gate, up and down matrices are the
+ * ones "How to compress model weights effectively" compresses):
+ *   g = X . gate^T,  u = X . up^T  (fp32 accumulation), h[b][r] =
+ *   bf16_rne(SiLU(g) * u) with the same SiLU arithmetic as uw_silu_mul_bf16.
+ * Batch 1-2 runs the GEMV pair: g and u equal uw_gemm_recon_pal with
+ * UW_KERNEL_GEMV bit for bit.  Batch 3-16 runs the skinny MFMA pair: g and u
+ * equal uw_gemm_recon_pal with UW_KERNEL_SKINNY bit for bit (same K-split).
+ * h is bit-identical to uw_silu_mul_bf16 on those g, u.
  * gate, up: same shape [rows, cols], both with a NIB section; X bf16 bits
  * [batch, cols]; h bf16 bits [batch, rows]; g_out, u_out fp32 [batch, rows]
  * or NULL (not written).  Device pointers, 16-byte aligned, caller-owned.
  * UW_EINVAL on NULL/misaligned pointers or mismatched shapes;
- * UW_EUNSUPPORTED unless 1 <= batch <= 4 and batch*cols*2 <= 32768. */
+ * UW_EUNSUPPORTED unless 1 <= batch <= 16, cols % 128 == 0, cols <= 32768
+ * and the library splits K at most 4 ways for this shape on the current
+ * device (about one wave per SIMD: at least ~4096 rows on MI355X), or, at
+ * batch 1-2, batch*cols*2 <= 32768 and cols <= 245760. */
 int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, int64_t batch,
                    uint16_t* h, float* g_out, float* u_out, void* stream);
 
@@ -314,7 +319,10 @@ int64_t uw_mlp_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t b
  * weights"), y = down . bf16(SiLU(X . gate^T) * (X . up^T)):
  * gate, up [F, H], down [H, F]; X bf16 bits [batch, H]; y fp32 [batch, F].
  * Each matmul runs with UW_KERNEL_AUTO and the library's split-K choice;
- * UW_PIPE_DIRECT fuses gate/up into one launch (uw_mlp_gate_up) at batch 1-2.
+ * UW_PIPE_DIRECT fuses gate/up into one launch (uw_mlp_gate_up) where it
+ * applies, with the same results except at batch 2, where the fused launch
+ * is the GEMV pair (faster there on MI355X) while UW_KERNEL_AUTO alone would
+ * take the skinny MFMA kernel (the two agree to rounding).
  * With aux_stream NULL every step runs on `stream`.  With an aux_stream (a
  * second stream of the caller's) and a decoding pipeline (FULL, EXP, PAL),
  * the three decodes run there, ordered after the work already on `stream`,

@@ -244,7 +244,7 @@ def matmul(dm: DeviceMatrix, X, pipeline=UW_PIPE_AUTO, kernel=UW_KERNEL_AUTO, sp
 
 def mlp_gate_up(gate: DeviceMatrix, up: DeviceMatrix, X, h=None, g=None, u=None, stream=None):
     """h = bf16(SiLU(X.gate^T) * (X.up^T)) in one fused launch (direct-palette
-    form, batch 1..4); g and u (fp32) are also written when given."""
+    form, batch 1..16); g and u (fp32) are also written when given."""
     torch = _torch()
     batch = X.shape[0]
     if h is None:

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <atomic>
 #include <map>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -445,9 +446,6 @@ int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, in
         return uw::fail(UW_EINVAL, std::string(who) + ": gate and up must have the same shape (cols % 64 == 0)");
     if (batch < 0) return uw::fail(UW_EINVAL, std::string(who) + ": negative batch");
     if (gate->rows == 0 || batch == 0) return UW_OK;
-    if (batch > 4 || batch * gate->cols * 2 > 32768 || gate->cols > 60 * 4096 ||
-        gate->rows * gate->cols >= (int64_t(1) << 31))
-        return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": needs 1 <= batch <= 4 and batch*cols*2 <= 32768");
     if (!X || !h || !aligned16(X) || !aligned16(h) || (g_out && !aligned16(g_out)) || (u_out && !aligned16(u_out)))
         return uw::fail(UW_EINVAL, std::string(who) + ": NULL or misaligned device pointer");
     for (const uw_dmat* d : {gate, up})
@@ -455,7 +453,22 @@ int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, in
             return uw::fail(UW_EINVAL, std::string(who) + ": a matrix lacks its NIB/SM/BITMAP/TILE_VBASE sections");
     uwk::MatArgs g = compressed_args(gate, gate->nib, X, batch, g_out);
     uwk::MatArgs u = compressed_args(up, up->nib, X, batch, u_out);
-    hipError_t e = uwk::launch_gemv_gateup(g, u, h, as_stream(stream));
+    g.cus = u.cus = device_cus();
+    const bool small = gate->rows * gate->cols < (int64_t(1) << 31) && batch * gate->cols < (int64_t(1) << 31);
+    // batch 1-2: the GEMV pair; 3-16: the skinny MFMA pair (measured on MI355X)
+    static const int gemv_max = [] {
+        const char* e = getenv("UW_GATEUP_GEMV_MAX");
+        return e && *e ? atoi(e) : 2;
+    }();
+    hipError_t e;
+    if (small && batch <= gemv_max && uwk::gemv_gateup_supported(g, u))
+        e = uwk::launch_gemv_gateup(g, u, h, as_stream(stream));
+    else if (small && uwk::mfma_gemv_gateup_supported(g, u))
+        e = uwk::launch_mfma_gemv_gateup(g, u, h, as_stream(stream));
+    else
+        return uw::fail(UW_EUNSUPPORTED, std::string(who) +
+                                             ": needs batch 1..16, cols % 128 == 0, cols <= 32768 and a K-split of at "
+                                             "most 4 for the shape (batch 1-2: or batch*cols*2 <= 32768)");
     return e == hipSuccess ? UW_OK : hip_fail(e, who);
 }
 
@@ -495,10 +508,9 @@ int uw_mlp_layer(const uw_dmat* gate, const uw_dmat* up, const uw_dmat* down, in
     int rc;
 
     if (pipeline == UW_PIPE_DIRECT) {
-        // nothing to decode; gate/up fused into one launch at batch 1-2 (at
-        // batch 4 separate skinny MFMA launches measured faster on MI355X)
+        // nothing to decode; gate/up fused into one launch where it applies
         bool fused = false;
-        if (batch <= 2 && batch * H * 2 <= 32768 && H <= 60 * 4096) {
+        if (batch <= 16) {
             rc = uw_mlp_gate_up(gate, up, X, batch, h, nullptr, nullptr, stream);
             if (rc && rc != UW_EUNSUPPORTED) return rc;
             fused = rc == UW_OK;

@@ -57,6 +57,10 @@ bool mfma_supported(const MatArgs& a);
 int mfma_default_split(const MatArgs& a, int cus);
 hipError_t launch_mfma_gemv(int src, const MatArgs& a, hipStream_t s);
 bool mfma_gemv_supported(const MatArgs& a);
+// Fused gate/up on the skinny MFMA kernel with the SiLU product (palette
+// sources, batch 1..16).
+bool mfma_gemv_gateup_supported(const MatArgs& gate, const MatArgs& up);
+hipError_t launch_mfma_gemv_gateup(const MatArgs& gate, const MatArgs& up, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, uint16_t* h, hipStream_t s);
 
 // LDS bytes the decoder needs for a code of longest length lmax.

@@ -89,30 +89,45 @@ __device__ __forceinline__ void join8(const u32x4_t& sm, const uint32_t e7[8], u
 // ahead of the step being rebuilt (PD + 1 register sets).
 // XQ: quads of activation rows loaded per step (4*NB, or fewer when the
 // batch leaves the rest of the 16-row tile empty).
-template <int SRC, int NB, int KW, int PD, int RB, int XQ>
-__global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
+// DUAL (palette source, one row block, one batch tile): the gate/up pair of
+// a SwiGLU MLP.  The workgroup holds 2*KW waves, the first KW on rows of the
+// gate matrix (a0), the others on the same rows of the up matrix, each wave
+// exactly as in a launch of its own matrix; the epilogue sums each matrix's
+// K-slices in the same order and writes H[b][r] = bf16(SiLU(g) * u), and g
+// and u themselves when a0.Y / up.Y are not null.
+template <int SRC, int NB, int KW, int PD, int RB, int XQ, bool DUAL>
+__global__ __launch_bounds__(64 * KW * (DUAL ? 2 : 1)) void mfma_gemv_kernel(MatArgs a0, MatArgs up, uint16_t* H) {
     static_assert(XQ >= 1 && XQ <= 4 * NB, "activation row quads");
-    __shared__ uint32_t lut[256];
+    static_assert(!DUAL || (SRC == SRC_PAL && RB == 1 && NB == 1), "gate/up pair");
+    constexpr int NW = KW * (DUAL ? 2 : 1);                 // waves per workgroup
+    __shared__ uint32_t lut[DUAL ? 512 : 256];
     // a region per wave during the K loop, holding a step's weight planes and
     // then its activation tile; the K-slices' partial tiles afterwards
     using PL = Planes<SRC>;
     constexpr int kWBytes = RB * PL::bytes, kXTBytes = NB * 16 * kXS * 2;
     constexpr int kRegion = kWBytes > kXTBytes ? kWBytes : kXTBytes;
-    constexpr int kXBytes = KW * kRegion, kPBytes = KW * RB * NB * 64 * 16;
+    constexpr int kXBytes = NW * kRegion, kPBytes = NW * RB * NB * 64 * 16;
     static_assert(kXBytes <= 150 * 1024 && kPBytes <= 150 * 1024, "LDS");
     __shared__ __align__(16) uint8_t smem[kXBytes > kPBytes ? kXBytes : kPBytes];
     auto part = reinterpret_cast<f32x4_t(*)[RB][NB][64]>(smem);
     const int tid = threadIdx.x;
     if (SRC == SRC_PAL)
-        for (int i = tid; i < 256; i += 64 * KW) lut[i] = (palb(a, i & 15) << 7) | (palb(a, i >> 4) << 23);
+        for (int i = tid; i < 256; i += 64 * NW) {
+            lut[i] = (palb(a0, i & 15) << 7) | (palb(a0, i >> 4) << 23);
+            if (DUAL) lut[256 + i] = (palb(up, i & 15) << 7) | (palb(up, i >> 4) << 23);
+        }
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    // DUAL: the matrix of this wave (uniform) and its place in that matrix's K-split
+    const int mi = DUAL ? wave / KW : 0, kwi = DUAL ? wave % KW : wave;
+    const MatArgs& a = (DUAL && mi) ? up : a0;
+    const uint32_t* const lutm = lut + (DUAL ? 256 * mi : 0);
     const uint32_t C = uint32_t(a.C);
     const uint32_t R = uint32_t(a.R);
     const uint32_t row0 = blockIdx.x * (16 * RB);         // first row of this workgroup
     const uint32_t nb0 = blockIdx.y * (NB * 16);          // first batch row of this tile
     const uint32_t B = uint32_t(a.B);
     const uint32_t steps = C / kKStep;
-    const uint32_t s_lo = steps * wave / KW, s_hi = steps * (wave + 1) / KW;
+    const uint32_t s_lo = steps * kwi / KW, s_hi = steps * (kwi + 1) / KW;
 
     const uint32_t q = uint32_t(lane) >> 4, rl = uint32_t(lane) & 15u;
     uint32_t rowc[RB];                                    // rows past R read row 0; never stored
@@ -278,7 +293,7 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
 #pragma unroll
                     for (int p = 0; p < 8; ++p) {
                         const uint32_t nbyte = (wl[r][0][2 * h + (p >> 2)] >> (8 * (p & 3))) & 0xFFu;
-                        e7[p] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + (nbyte << 2));
+                        e7[p] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lutm) + (nbyte << 2));
                     }
                     if (__builtin_amdgcn_ballot_w64(st.verb[r] != 0)) {   // rare: raw exponents for verbatim lanes
 #pragma unroll
@@ -347,6 +362,30 @@ __global__ __launch_bounds__(64 * KW) void mfma_gemv_kernel(MatArgs a) {
 #pragma unroll
         for (int n = 0; n < NB; ++n) part[wave][r][n][lane] = acc[r][n];
     __syncthreads();
+    if (DUAL) {
+        for (int l = tid; l < 64; l += 64 * NW) {
+            f32x4_t g = part[0][0][0][l], u = part[KW][0][0][l];
+#pragma unroll
+            for (int w_ = 1; w_ < KW; ++w_) {
+                g += part[w_][0][0][l];
+                u += part[KW + w_][0][0][l];
+            }
+            const uint32_t b = nb0 + (l & 15);
+            const uint32_t rr = row0 + 4 * (l >> 4);
+            if (b < B) {
+                const int64_t o = int64_t(b) * a0.R + rr;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (rr + i < R) {
+                        if (a0.Y) a0.Y[o + i] = g[i];
+                        if (up.Y) up.Y[o + i] = u[i];
+                        H[o + i] = uint16_t(f32_to_bf16_rne(silu_mul1(g[i], u[i])));
+                    }
+                }
+            }
+        }
+        return;
+    }
     for (int idx = tid; idx < RB * NB * 64; idx += 64 * KW) {
         const int r = idx / (NB * 64), n = (idx / 64) % NB, l = idx % 64;
         f32x4_t v = part[0][r][n][l];
@@ -399,16 +438,17 @@ Shape choose_shape(const MatArgs& a) {
     return {kw, pd, rb};
 }
 
-template <int SRC, int NB, int KW, int PD, int RB>
-hipError_t launch_shape(const MatArgs& a, hipStream_t s) {
+template <int SRC, int NB, int KW, int PD, int RB, bool DUAL = false>
+hipError_t launch_shape(const MatArgs& a, hipStream_t s, const MatArgs& up = MatArgs{}, uint16_t* h = nullptr) {
     dim3 grid(unsigned((a.R + 16 * RB - 1) / (16 * RB)), unsigned((a.B + NB * 16 - 1) / (NB * 16)));
+    const dim3 block(64 * KW * (DUAL ? 2 : 1));
     // one 16-row batch tile: load only the row quads the batch fills
     if constexpr (NB == 1) {
-        if (a.B <= 4) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 1>, grid, dim3(64 * KW), 0, s, a);
-        else if (a.B <= 8) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 2>, grid, dim3(64 * KW), 0, s, a);
-        else launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 4>, grid, dim3(64 * KW), 0, s, a);
+        if (a.B <= 4) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 1, DUAL>, grid, block, 0, s, a, up, h);
+        else if (a.B <= 8) launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 2, DUAL>, grid, block, 0, s, a, up, h);
+        else launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 4, DUAL>, grid, block, 0, s, a, up, h);
     } else {
-        launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 4 * NB>, grid, dim3(64 * KW), 0, s, a);
+        launch_timed(mfma_gemv_kernel<SRC, NB, KW, PD, RB, 4 * NB, false>, grid, block, 0, s, a, up, h);
     }
     return hipGetLastError();
 }
@@ -458,6 +498,28 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
 // Supported when the K-slices are whole 128-column steps and, split 8 ways at
 // most, each slice spans at most 4096 columns (so a lane's row segment
 // touches at most two tiles).
+// Gate/up pair (palette sources): batch <= 16, and the K-split the library
+// takes for one of the matrices at most 4 (so a workgroup holds at most 8
+// waves; small matrices that split 8 ways are left to separate launches).
+bool mfma_gemv_gateup_supported(const MatArgs& g, const MatArgs& u) {
+    return g.R == u.R && g.C == u.C && g.B == u.B && g.B >= 1 && g.B <= 16 && g.C > 0 && g.C % kKStep == 0 &&
+           mfma_gemv_supported(g) && choose_shape(g).kw <= 4;
+}
+
+// The K-split of the pair is the library's choice for one of its matrices,
+// so g and u equal what separate skinny launches give, bit for bit.
+hipError_t launch_mfma_gemv_gateup(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
+    if (g.R == 0) return hipSuccess;
+    if (!mfma_gemv_gateup_supported(g, u)) return hipErrorNotSupported;
+    const Shape sh = choose_shape(g);
+    const int kw = sh.kw;
+    if (kw <= 2)
+        return sh.pd == 1 ? launch_shape<SRC_PAL, 1, 2, 1, 1, true>(g, s, u, h)
+                          : launch_shape<SRC_PAL, 1, 2, 2, 1, true>(g, s, u, h);
+    return sh.pd == 1 ? launch_shape<SRC_PAL, 1, 4, 1, 1, true>(g, s, u, h)
+                      : launch_shape<SRC_PAL, 1, 4, 2, 1, true>(g, s, u, h);
+}
+
 bool mfma_gemv_supported(const MatArgs& a) {
     const int64_t steps = a.C / kKStep;
     return a.C > 0 && a.C % kKStep == 0 && (steps + 7) / 8 * kKStep <= kMaxSlice;

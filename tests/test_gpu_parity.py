@@ -499,6 +499,31 @@ def test_mlp_layer_one_and_two_streams(torch_cuda, pipeline, B):
     assert_matmul_close(yr, wd, from_dev_bits(h), what=f"{pipeline} down on the GPU's h")
 
 
+@pytest.mark.parametrize("B", [1, 3, 8, 16])
+def test_mlp_layer_direct_fused_pair(torch_cuda, B):
+    """uw_mlp_layer on the direct-palette form where gate/up run as one fused
+    launch (4096-row gate/up: the GEMV pair at batch 1, the skinny MFMA pair
+    above): bit for bit what the single-matrix calls with the library's
+    kernel choice give."""
+    print_case(f"mlp layer direct fused pair B={B}")
+    F, H = 4096, 512
+    wg = workloads.layer_weight(3, 2, 0, shape=(F, H))
+    wu = workloads.layer_weight(3, 2, 1, shape=(F, H))
+    wd = workloads.layer_weight(3, 2, 2, shape=(H, F))
+    x = workloads.layer_activation(3, 2, 0, B, cols=H)
+    dms = [uw.compress(m).to_device() for m in (wg, wu, wd)]
+    X = to_dev_bf16(x)
+    p = uw.UW_PIPE_DIRECT
+    g = uw.matmul(dms[0], X, pipeline=p, kernel=uw.UW_KERNEL_AUTO, split_k=0)
+    u = uw.matmul(dms[1], X, pipeline=p, kernel=uw.UW_KERNEL_AUTO, split_k=0)
+    h = uw.silu_mul_bf16(g, u)
+    y_ref = uw.matmul(dms[2], h, pipeline=p, kernel=uw.UW_KERNEL_AUTO, split_k=0,
+                      scratch=uw.alloc_scratch(p, H, F, B, 0))
+    y = uw.mlp_layer(*dms, X, pipeline=p)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.cpu().numpy().view(np.uint32))
+    assert_matmul_close(y.cpu().numpy(), wd, from_dev_bits(h), what=f"down on the GPU's h B={B}")
+
+
 def test_mlp_layer_rejects(torch_cuda):
     print_case("mlp layer argument checks")
     rng = np.random.default_rng(2)
@@ -523,9 +548,10 @@ def _bf16_key(b):
 
 
 def _gate_up_case(wg, wu, x, rows=None, what=""):
-    """The fused launch against the unfused three calls (bit for bit) and
-    against the fp64 oracle (g, u within tolerance; h within one bf16 ulp of
-    bf16(SiLU(g)*u) on the GPU's g, u)."""
+    """The fused launch against the unfused three calls with the same kernel
+    family (the GEMV at batch 1-2, the skinny MFMA kernel at 3-16; bit for
+    bit) and against the fp64 oracle (g, u within tolerance; h within one
+    bf16 ulp of bf16(SiLU(g)*u) on the GPU's g, u)."""
     import torch
     dg, du = uw.compress(wg).to_device(), uw.compress(wu).to_device()
     X = to_dev_bf16(x)
@@ -534,8 +560,9 @@ def _gate_up_case(wg, wu, x, rows=None, what=""):
     u = torch.empty_like(g)
     h = uw.mlp_gate_up(dg, du, X, g=g, u=u)
     h_only = uw.mlp_gate_up(dg, du, X)                       # no g/u outputs
-    g2 = uw.gemm_recon_pal(dg, None, X, kernel=uw.UW_KERNEL_GEMV)
-    u2 = uw.gemm_recon_pal(du, None, X, kernel=uw.UW_KERNEL_GEMV)
+    kernel = uw.UW_KERNEL_GEMV if B <= 2 else uw.UW_KERNEL_SKINNY
+    g2 = uw.gemm_recon_pal(dg, None, X, kernel=kernel)
+    u2 = uw.gemm_recon_pal(du, None, X, kernel=kernel)
     h2 = uw.silu_mul_bf16(g2, u2)
     gn, un = g.cpu().numpy(), u.cpu().numpy()
     assert np.array_equal(gn.view(np.uint32), g2.cpu().numpy().view(np.uint32)), what + " g"
@@ -553,18 +580,22 @@ def _gate_up_case(wg, wu, x, rows=None, what=""):
     assert np.abs(_bf16_key(hb) - _bf16_key(href)).max() <= 1
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 9, 16])
 def test_gate_up_fused_small(torch_cuda, B):
+    """Reduced-width gate/up pair (4096 x 512) at every batch the fused
+    launch takes: the GEMV pair at 1-2, the skinny MFMA pair (each quad count
+    of activation rows) at 3-16."""
     print_case(f"fused gate/up small B={B}")
-    wg = workloads.layer_weight(3, 1, 0, shape=(1536, 512))
-    wu = workloads.layer_weight(3, 1, 1, shape=(1536, 512))
+    wg = workloads.layer_weight(3, 1, 0, shape=(4096, 512))
+    wu = workloads.layer_weight(3, 1, 1, shape=(4096, 512))
     _gate_up_case(wg, wu, workloads.layer_activation(3, 1, 0, B, cols=512), what=f"B={B}")
 
 
-@pytest.mark.parametrize("R,C,B", [(1, 64, 1), (37, 1088, 2), (130, 2048 + 64, 3), (5, 8192, 2)])
+@pytest.mark.parametrize("R,C,B", [(1, 64, 1), (37, 1088, 2), (5, 8192, 2), (4100, 1152, 3), (4111, 2176, 16)])
 def test_gate_up_fused_ragged(torch_cuda, R, C, B):
-    """Rows not a multiple of a workgroup, columns not a multiple of a slab,
-    one-row and one-group matrices, outliers forcing verbatim groups."""
+    """Rows not a multiple of a workgroup, columns not a multiple of a slab
+    (GEMV pair) or of the four K-slices (skinny pair: 9 and 17 steps), one-row
+    and one-group matrices, outliers forcing verbatim groups."""
     print_case(f"fused gate/up ragged R={R} C={C} B={B}")
     rng = np.random.default_rng(R * C + B)
     wg = workloads.gaussian_weights(rng, R, C, 0.02, 0.004, 1.0)
@@ -572,13 +603,15 @@ def test_gate_up_fused_ragged(torch_cuda, R, C, B):
     _gate_up_case(wg, wu, _x(R + C, B, C), what=f"R={R} C={C} B={B}")
 
 
-def test_gate_up_fused_full_size(torch_cuda):
-    """Llama-3.1-8B gate and up at batch 1, the benchmark's launch: bitwise
-    equal to the unfused calls, sampled rows against the oracle."""
-    print_case("fused gate/up full size")
+@pytest.mark.parametrize("B", [1, 4, 16])
+def test_gate_up_fused_full_size(torch_cuda, B):
+    """Llama-3.1-8B gate and up in the benchmark's launches (the GEMV pair at
+    batch 1, the skinny MFMA pair at 4 and 16): bitwise equal to the unfused
+    calls, sampled rows against the oracle."""
+    print_case(f"fused gate/up full size B={B}")
     wg, wu = workloads.layer_weight(2, 0, 0), workloads.layer_weight(2, 0, 1)
     rows = np.sort(np.random.default_rng(5).choice(wg.shape[0], 384, replace=False))
-    _gate_up_case(wg, wu, workloads.layer_activation(2, 0, 0, 1), rows=rows, what="llama")
+    _gate_up_case(wg, wu, workloads.layer_activation(2, 0, 0, B), rows=rows, what=f"llama B={B}")
 
 
 def test_gate_up_fused_rejects(torch_cuda):
@@ -587,7 +620,11 @@ def test_gate_up_fused_rejects(torch_cuda):
     wo = workloads.layer_weight(3, 1, 1, shape=(64, 576))
     dg, du, do = (uw.compress(w).to_device() for w in (wg, wu, wo))
     with pytest.raises(uw.UnweightError) as ei:
-        uw.mlp_gate_up(dg, du, to_dev_bf16(_x(1, 5, 512)))
+        uw.mlp_gate_up(dg, du, to_dev_bf16(_x(1, 5, 512)))       # 64 rows split K 8 ways
+    assert ei.value.code == uw.UW_EUNSUPPORTED
+    big_g = uw.compress(workloads.layer_weight(3, 1, 0, shape=(4096, 512))).to_device()
+    with pytest.raises(uw.UnweightError) as ei:
+        uw.mlp_gate_up(big_g, big_g, to_dev_bf16(_x(1, 17, 512)))  # batch above 16
     assert ei.value.code == uw.UW_EUNSUPPORTED
     with pytest.raises(uw.UnweightError) as ei:
         uw.mlp_gate_up(dg, do, to_dev_bf16(_x(1, 1, 512)))
