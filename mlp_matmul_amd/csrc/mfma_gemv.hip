@@ -1,6 +1,7 @@
 // Skinny matmul (batch 2..64) on bf16 MFMA with weights rebuilt in the
 // A-operand registers, for uncompressed, exponent-source and palette-source
-// weights.
+// weights, and the gate/up pair of an MLP block with the SiLU product in the
+// epilogue (palette source, batch up to 16).
 //
 // Method: Cloudflare, "Unweight: how we compressed an LLM 22% without
 // sacrificing quality", "How the reconstructive matmul works": compressed
@@ -171,8 +172,9 @@ __global__ __launch_bounds__(64 * KW * (DUAL ? 2 : 1)) void mfma_gemv_kernel(Mat
 
     // The weight planes of a step go out as contiguous runs of each row (the
     // MFMA layout puts consecutive lanes on consecutive rows, which would cost
-    // an L1 access per lane): piece i of plane bpr covers 16 bytes, lanes
-    // 16/bpr.. of a row side by side.  Plain (cache-retained) loads.
+    // an L1 access per lane): a plane row of bpr bytes is loaded by bpr/16
+    // neighbouring lanes, 16 bytes each, piece i covering rows
+    // 64i/(bpr/16).. of the block.  Plain (cache-retained) loads.
     const uint8_t* const plane0 = SRC == SRC_BF16 ? reinterpret_cast<const uint8_t*>(wb) : w8;
     auto plane_piece = [&](const uint8_t* base, int bpr, int r, int i, uint32_t s) {
         const uint32_t p = uint32_t(i) * 64u + uint32_t(lane), cpr = uint32_t(bpr) / 16u;
@@ -416,12 +418,13 @@ int env_int(const char* name, int dflt) {
 // override for tuning).  The K-split is the smallest that gives about one
 // wave per SIMD (a 14336-row matrix: 2; 4096 rows: 4; 1024 rows: 8), and at
 // least what keeps one wave's slice within kMaxSlice columns; one row block
-// per wave (with the tiles staged through LDS a second block saves little
-// activation traffic and halves the workgroups); two steps in flight for long
-// slices (>= 24 steps) at batch <= 8.
+// per wave up to batch 16 (with the tiles staged through LDS a second block
+// saves little activation traffic and halves the workgroups), two on tall
+// matrices above (gate at batch 32: 29.6 against 30.8 us); two steps in
+// flight for long slices (>= 24 steps) at batch <= 8.
 Shape choose_shape(const MatArgs& a) {
     const int64_t steps = a.C / kKStep;
-    int rb = env_int("UW_SKINNY_RB", 1);
+    int rb = env_int("UW_SKINNY_RB", a.B > 16 && a.R >= 8192 ? 2 : 1);
     const int kw_env = env_int("UW_SKINNY_KW", 0);
     int kw = kw_env;
     if (kw <= 0) {
