@@ -867,7 +867,7 @@ def main():
     achieved = per_kernel[dom]["bytes"] / per_kernel[dom]["avg_s"] / 1e9
     achieved_all = bytes_.sum() / durs.sum() / 1e9
     # the kernel family UW_KERNEL_AUTO takes for the rebuilding sources
-    family = "gemv" if B == 1 else ("skinny" if B <= 16 else "mfma")
+    family = "gemv" if B == 1 else ("skinny" if B <= 32 else "mfma")
     pair = "GEMV" if B <= 2 else "skinny MFMA"
     kernel_names = ([f"fused gate/up {pair} + SiLU (palette source)", f"down {family} (palette source)"]
                     if step.fused else [f"{n} recon matmul ({family})" for n in ("gate", "up", "down")])

@@ -115,11 +115,12 @@ int device_cus() {
 // batch 16, the tiled MFMA kernel from batch 17, which is faster than the
 // skinny kernel at batch 32 and 64 on both shapes).
 // Measured on MI355X (Llama MLP shapes): the GEMV wins at batch 1 (below
-// batch 4 for bf16 weights), the skinny MFMA kernel from there through 16.
+// batch 4 for bf16 weights), the skinny MFMA kernel from there through 32
+// (the autotuner's choice at batch 32 on both shapes), the tiled kernel above.
 int auto_kernel(int src, const uwk::MatArgs& a) {
     const int64_t gemv_below = src == uwk::SRC_BF16 ? 4 : 2;
     return a.B < gemv_below ? UW_KERNEL_GEMV
-                            : (a.B <= 16 && uwk::mfma_gemv_supported(a) ? UW_KERNEL_SKINNY : UW_KERNEL_MFMA);
+                            : (a.B <= 32 && uwk::mfma_gemv_supported(a) ? UW_KERNEL_SKINNY : UW_KERNEL_MFMA);
 }
 
 // split_k 0: the library's choice, K-slices for the tiled MFMA kernel that

@@ -90,7 +90,7 @@ __device__ __forceinline__ void join8(const u32x4_t& sm, const uint32_t e7[8], u
 // ahead of the step being rebuilt (PD + 1 register sets).
 // XQ: quads of activation rows loaded per step (4*NB, or fewer when the
 // batch leaves the rest of the 16-row tile empty).
-// DUAL (palette source, one row block, one batch tile): the gate/up pair of
+// DUAL (palette source, one row block, one batch block): the gate/up pair of
 // a SwiGLU MLP.  The workgroup holds 2*KW waves, the first KW on rows of the
 // gate matrix (a0), the others on the same rows of the up matrix, each wave
 // exactly as in a launch of its own matrix; the epilogue sums each matrix's
@@ -365,14 +365,15 @@ __global__ __launch_bounds__(64 * KW * (DUAL ? 2 : 1)) void mfma_gemv_kernel(Mat
         for (int n = 0; n < NB; ++n) part[wave][r][n][lane] = acc[r][n];
     __syncthreads();
     if (DUAL) {
-        for (int l = tid; l < 64; l += 64 * NW) {
-            f32x4_t g = part[0][0][0][l], u = part[KW][0][0][l];
+        for (int idx = tid; idx < NB * 64; idx += 64 * NW) {
+            const int n = idx / 64, l = idx % 64;
+            f32x4_t g = part[0][0][n][l], u = part[KW][0][n][l];
 #pragma unroll
             for (int w_ = 1; w_ < KW; ++w_) {
-                g += part[w_][0][0][l];
-                u += part[KW + w_][0][0][l];
+                g += part[w_][0][n][l];
+                u += part[KW + w_][0][n][l];
             }
-            const uint32_t b = nb0 + (l & 15);
+            const uint32_t b = nb0 + n * 16 + (l & 15);
             const uint32_t rr = row0 + 4 * (l >> 4);
             if (b < B) {
                 const int64_t o = int64_t(b) * a0.R + rr;
@@ -501,9 +502,12 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
 // Supported when the K-slices are whole 128-column steps and, split 8 ways at
 // most, each slice spans at most 4096 columns (so a lane's row segment
 // touches at most two tiles).
-// Gate/up pair (palette sources): batch <= 16, and the K-split the library
-// takes for one of the matrices at most 4 (so a workgroup holds at most 8
-// waves; small matrices that split 8 ways are left to separate launches).
+// Gate/up pair (palette sources): batch <= 16 (above it the separate
+// launches take two row blocks per wave on tall matrices and measured faster
+// than the pair: Llama gate/up at batch 32, 61.8 against 67.9 us), and the
+// K-split the library takes for one of the matrices at most 4 (so a
+// workgroup holds at most 8 waves; small matrices that split 8 ways are left
+// to separate launches).
 bool mfma_gemv_gateup_supported(const MatArgs& g, const MatArgs& u) {
     return g.R == u.R && g.C == u.C && g.B == u.B && g.B >= 1 && g.B <= 16 && g.C > 0 && g.C % kKStep == 0 &&
            mfma_gemv_supported(g) && choose_shape(g).kw <= 4;

@@ -499,12 +499,12 @@ def test_mlp_layer_one_and_two_streams(torch_cuda, pipeline, B):
     assert_matmul_close(yr, wd, from_dev_bits(h), what=f"{pipeline} down on the GPU's h")
 
 
-@pytest.mark.parametrize("B", [1, 3, 8, 16])
+@pytest.mark.parametrize("B", [1, 3, 8, 16, 24])
 def test_mlp_layer_direct_fused_pair(torch_cuda, B):
-    """uw_mlp_layer on the direct-palette form where gate/up run as one fused
-    launch (4096-row gate/up: the GEMV pair at batch 1, the skinny MFMA pair
-    above): bit for bit what the single-matrix calls with the library's
-    kernel choice give."""
+    """uw_mlp_layer on the direct-palette form (4096-row gate/up: one fused
+    launch at batch 1 (GEMV pair) and 3-16 (skinny MFMA pair), separate
+    skinny launches at 24): bit for bit what the single-matrix calls with the
+    library's kernel choice give."""
     print_case(f"mlp layer direct fused pair B={B}")
     F, H = 4096, 512
     wg = workloads.layer_weight(3, 2, 0, shape=(F, H))
