@@ -532,6 +532,82 @@ def attention_bench(batches, n_layers=6, steps=30, warmup=4):
     return {"sizes": sizes, "rows": rows}
 
 
+def lm_head_bench(batches, copies=2, steps=20, warmup=3):
+    """The embedding-sized matmul of the model: Llama-3.1-8B's output
+    projection (128256 x 4096, 1.05 GB of bf16), one seeded matrix uploaded
+    `copies` times at different addresses (rotating over them keeps the
+    256 MiB Infinity Cache from serving it).  Direct palette with the
+    library's kernel choice against the hand-written bf16 kernels (the
+    fastest) and torch.matmul."""
+    import ctypes as ct
+    import functools
+    import torch
+    import mlp_matmul_amd as uw
+    import workloads
+    L = uw.lib()
+    R, C = workloads.LM_HEAD_SHAPE
+    t0 = time.perf_counter()
+    w = workloads.lm_head_weight()
+    blob = uw.compress(w, emit_palette=True)
+    inf = blob.info()
+    dev = [blob.to_device(("sm", "nib", "vexp", "bitmap", "tile_vbase")) for _ in range(copies)]
+    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16)
+    bf = [wt.cuda() for _ in range(copies)]
+    del w, wt, blob
+    log(f"lm head: generated, compressed and uploaded in {time.perf_counter() - t0:.1f} s")
+    sizes = {"shape": [R, C], "bf16_bytes": 2 * R * C,
+             "huffman_ratio": round(inf.huffman_form_bytes / (2 * R * C), 4),
+             "palette_ratio": round(inf.palette_form_bytes / (2 * R * C), 4),
+             "verbatim_group_frac": round(inf.verbatim_groups / inf.groups, 5)}
+    stream = torch.cuda.current_stream()
+    st = ct.c_void_p(stream.cuda_stream)
+    P = lambda t: ct.c_void_p(t.data_ptr())
+    rows = []
+    for b in batches:
+        X = torch.from_numpy(workloads.lm_head_activation(b).view(np.int16)).view(torch.bfloat16).cuda()
+        Y = torch.empty((b, R), dtype=torch.float32, device="cuda")
+        scr = torch.empty(max(uw.scratch_bytes(uw.UW_PIPE_DIRECT, R, C, b, 0), 16), dtype=torch.uint8, device="cuda")
+        _, kname, k, sk = time_bf16(bf, X)
+        direct = [functools.partial(L.uw_matmul, ct.byref(d.dmat), uw.UW_PIPE_DIRECT, 0, 0, P(X), b, P(Y), P(scr),
+                                    ct.c_uint64(scr.numel()), st) for d in dev]
+        bscr = torch.empty(8 * 4 * b * R + 256, dtype=torch.uint8, device="cuda")
+        hand = [functools.partial(L.uw_gemm_bf16, P(W), R, C, P(X), b, P(Y), k, sk, P(bscr),
+                                  ct.c_uint64(bscr.numel()), st) for W in bf]
+        with torch.no_grad():
+            tch = [functools.partial(torch.matmul, X, W.t()) for W in bf]
+
+        def run(calls, checked=True):
+            for i in range(warmup):
+                r = calls[i % copies]()
+                if checked:
+                    uw.check(r, "lm head")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                r = calls[i % copies]()
+                if checked:
+                    uw.check(r, "lm head")
+            e1.record(stream)
+            e1.synchronize()
+            return e0.elapsed_time(e1) / steps * 1e3
+
+        t_d, t_b = run(direct), run(hand)
+        with torch.no_grad():
+            t_t = run(tch, checked=False)
+        rows.append({"batch": b, "direct_us": round(t_d, 2), "bf16_us": round(t_b, 2), "bf16_kernel": kname,
+                     "torch_bf16_us": round(t_t, 2), "speedup_vs_bf16": round(t_b / t_d, 3),
+                     "speedup_vs_torch_bf16": round(t_t / t_d, 3),
+                     "bf16_equiv_GBps": round(2 * R * C / t_d / 1e3, 1),
+                     "compressed_GBps": round(inf.palette_form_bytes / t_d / 1e3, 1),
+                     "compressed_hbm_frac": round(inf.palette_form_bytes / t_d / 1e3 / HBM_PEAK_GBPS, 4)})
+        log(f"lm head B={b}: {rows[-1]}")
+        del bscr, scr
+    del dev, bf
+    torch.cuda.empty_cache()
+    return {"workload": "llama3.1-8b output projection 128256x4096, one seeded matrix, "
+                        f"{copies} device copies rotated", "sizes": sizes, "rows": rows}
+
+
 def time_pipeline(copies, pipeline, kernel, split_k, X, reps=20, warmup=3, stream=None):
     """Seconds per uw_matmul call (pipeline, kernel, split_k), rotating copies."""
     import torch
@@ -946,6 +1022,7 @@ def main():
         out["attention"] = {"workload": "llama3.1-8b attention projections q/k/v/o, one step per layer, 6 seeded "
                                         "layers rotated",
                             **attention_bench([1, 4, 16])}
+        out["lm_head"] = lm_head_bench([1, 4, 16])
         out["layer_overlap"] = {"workload": "llama3.1-8b-mlp-layer through uw_mlp_layer, us per layer: decodes on the "
                                             "layer's stream vs on a second stream overlapping the matmuls",
                                 "rows": layer_overlap(layers, [1, 16], stream)}

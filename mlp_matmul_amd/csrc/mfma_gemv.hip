@@ -418,14 +418,18 @@ int env_int(const char* name, int dflt) {
 // the Llama MLP and attention shapes at batch 2..16 (UW_SKINNY_KW / _PD / _RB
 // override for tuning).  The K-split is the smallest that gives about one
 // wave per SIMD (a 14336-row matrix: 2; 4096 rows: 4; 1024 rows: 8), and at
-// least what keeps one wave's slice within kMaxSlice columns; one row block
-// per wave up to batch 16 (with the tiles staged through LDS a second block
-// saves little activation traffic and halves the workgroups), two on tall
-// matrices above (gate at batch 32: 29.6 against 30.8 us); two steps in
-// flight for long slices (>= 24 steps) at batch <= 8.
+// least what keeps one wave's slice within kMaxSlice columns.  One row
+// block per wave up to batch 16 (with the tiles staged through LDS a second
+// block saves little activation traffic and halves the workgroups), two on
+// tall matrices above (gate at batch 32: 29.6 against 30.8 us) and from
+// batch 5 on matrices of 32768 rows or more, where halving the workgroups
+// still leaves many per CU and each wave re-reads the activation tile for
+// fewer rows (the 128256-row output projection at batch 16: 168.5 against
+// 191.8 us).  Two steps in flight for long slices (>= 24 steps) at batch <= 8.
 Shape choose_shape(const MatArgs& a) {
     const int64_t steps = a.C / kKStep;
-    int rb = env_int("UW_SKINNY_RB", a.B > 16 && a.R >= 8192 ? 2 : 1);
+    const bool two_blocks = (a.B > 16 && a.R >= 8192) || (a.B > 4 && a.R >= 32768);
+    int rb = env_int("UW_SKINNY_RB", two_blocks ? 2 : 1);
     const int kw_env = env_int("UW_SKINNY_KW", 0);
     int kw = kw_env;
     if (kw <= 0) {

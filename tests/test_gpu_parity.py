@@ -124,6 +124,32 @@ def test_attention_projections_full_size(torch_cuda, name):
         assert_matmul_close(Y.cpu().numpy()[:, rows], w, x, rows=rows, what=f"{name} B={B}")
 
 
+def test_lm_head_full_size(torch_cuda):
+    """The largest matrix of the model, the output projection (128256 x 4096,
+    525M weights, the benchmark's lm_head workload): full and exponent decodes
+    bit-exact on every element, direct-palette matmul through the library's
+    kernel choice at batch 1, 4 and 16 on sampled rows against the fp64
+    oracle."""
+    import torch
+    print_case("lm head 128256x4096 full size")
+    w = workloads.lm_head_weight()
+    dm = uw.compress(w, emit_palette=True).to_device()
+    full = uw.decode_full(dm)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_bits(full), w), "full decode"
+    del full
+    exps = uw.decode_exponents(dm)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev_u8(exps), ((w >> 7) & 0xFF).astype(np.uint8)), "exponent decode"
+    del exps
+    rows = np.sort(np.random.default_rng(11).choice(w.shape[0], 256, replace=False))
+    for B in (1, 4, 16):
+        x = workloads.lm_head_activation(B)
+        Y = uw.matmul(dm, to_dev_bf16(x), pipeline=uw.UW_PIPE_DIRECT, kernel=uw.UW_KERNEL_AUTO, split_k=0,
+                      scratch=uw.alloc_scratch(uw.UW_PIPE_DIRECT, w.shape[0], w.shape[1], B, 0))
+        assert_matmul_close(Y.cpu().numpy()[:, rows], w, x, rows=rows, what=f"lm head B={B}")
+
+
 @pytest.mark.parametrize("wl,m", [(2, 0), (2, 2), (4, 1), (5, 2)])
 def test_decoders_full_size(torch_cuda, wl, m):
     print_case(f"decoders full size workload {wl} matrix {m}")

@@ -185,3 +185,31 @@ def attention_activation(layer: int, name: str, batch: int) -> np.ndarray:
     """bf16 bits [batch, cols] fed to one attention projection."""
     rng = np.random.default_rng([6, layer, ATTN_IDS[name], 1])
     return gaussian_activations(rng, batch, ATTN_SHAPES[name][1])
+
+
+# Llama-3.1-8B's output projection (the unembedding matrix, vocabulary x
+# hidden), the embedding-sized matmul of the model.
+LM_HEAD_SHAPE = (128256, 4096)
+
+
+def lm_head_weight(shape=None) -> np.ndarray:
+    """bf16 bits of the output projection, default_rng([7, 0, 0, 0]):
+    N(0, 0.02) with Binomial(N, 5e-4) outliers N(0, 0.5) at uniformly drawn
+    positions (the same distribution as the other weights, drawn without a
+    per-element mask so that a 525M-element matrix generates in seconds)."""
+    rows, cols = shape if shape is not None else LM_HEAD_SHAPE
+    rng = np.random.default_rng([7, 0, 0, 0])
+    w = rng.standard_normal((rows, cols), dtype=np.float32)
+    w *= np.float32(0.02)
+    n = int(rng.binomial(rows * cols, 5e-4))
+    pos = rng.integers(0, rows * cols, n)
+    w.reshape(-1)[pos] = rng.standard_normal(n, dtype=np.float32) * np.float32(0.5)
+    # round to nearest even as f32_to_bf16_bits does, in 32-bit arithmetic:
+    # the draws are finite, so the sum cannot carry out of 32 bits
+    u = w.view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def lm_head_activation(batch: int, cols: int = LM_HEAD_SHAPE[1]) -> np.ndarray:
+    """bf16 bits [batch, cols] N(0, 1) fed to the output projection."""
+    return gaussian_activations(np.random.default_rng([7, 0, 0, 1]), batch, cols)
