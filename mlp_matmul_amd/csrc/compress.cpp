@@ -530,23 +530,23 @@ int uw_blob_deserialize(const void* buf, uint64_t bytes, uw_blob** out) {
                 case UW_SEC_GLEN:
                     if (!need_mult(2)) return bad("uw_blob_deserialize: GLEN size");
                     b->glen.resize(n / 2);
-                    std::memcpy(b->glen.data(), p, n);
+                    if (n) std::memcpy(b->glen.data(), p, n);
                     break;
                 case UW_SEC_TILE_OFF:
                     if (!need_mult(4)) return bad("uw_blob_deserialize: TILE_OFF size");
                     b->tile_off.resize(n / 4);
-                    std::memcpy(b->tile_off.data(), p, n);
+                    if (n) std::memcpy(b->tile_off.data(), p, n);
                     break;
                 case UW_SEC_TILE_VBASE:
                     if (!need_mult(4)) return bad("uw_blob_deserialize: TILE_VBASE size");
                     b->tile_vbase.resize(n / 4);
-                    std::memcpy(b->tile_vbase.data(), p, n);
+                    if (n) std::memcpy(b->tile_vbase.data(), p, n);
                     break;
                 case UW_SEC_VEXP: b->vexp.assign(p, p + n); break;
                 case UW_SEC_BITMAP:
                     if (!need_mult(8)) return bad("uw_blob_deserialize: BITMAP size");
                     b->bitmap.resize(n / 8);
-                    std::memcpy(b->bitmap.data(), p, n);
+                    if (n) std::memcpy(b->bitmap.data(), p, n);
                     break;
                 case UW_SEC_NIB: b->nib.assign(p, p + n); break;
             }
@@ -556,12 +556,14 @@ int uw_blob_deserialize(const void* buf, uint64_t bytes, uw_blob** out) {
         delete b;
         return uw::fail(UW_ENOMEM, "uw_blob_deserialize: out of host memory");
     }
-    uw::canonical_codes(b->lengths, b->codes);
+    // the code lengths are checked (at most 15, Kraft sum 1) before the
+    // canonical codes and the decode tables are derived from them
     int rc = uw_validate(b);
     if (rc != UW_OK) {
         delete b;
         return rc;
     }
+    uw::canonical_codes(b->lengths, b->codes);
     uw::build_dlut(*b);
     uw::build_mlut(*b);
     *out = b;
