@@ -95,7 +95,6 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
     const uint32_t slots_a = buf_a + bw * 4;
     const uint32_t ptab_a = kMlutEntries * 4;
 
-    const uint32_t lim = bw - 2;
     const int fb_shift = 32 - (lmax > 0 ? lmax : 1);
     const bool vec_ok = a.stream_bytes >= 16;
     const int64_t N = a.G * 64;
@@ -179,13 +178,20 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
             if (lane >= d) incl += v;
         }
 
-        // q = 31 + bit position from buf[1]; nc4 = 4 x symbols decoded (256 = done)
-        uint32_t q = incl - gl + ((off0 & 3u) << 3) + 31;
+        // q = 31 + bit position from buf[1]; nc4 = 4 x symbols decoded (256 = done).
+        // A lane makes at most 64 lookups of at most 255 bits each (entries
+        // carry 8-bit lengths), so clamping its start once keeps every window
+        // read inside this wave's buffer and slots; for a consistent stream
+        // the clamp never binds.
+        // q carries the buffer's LDS address (x 8, a multiple of 32, so its
+        // low five bits are unchanged): the window's word address is then
+        // (q >> 3) & ~3 with no add.
+        uint32_t q = min(incl - gl + ((off0 & 3u) << 3) + 31, (bw + 64u) * 32u) + buf_a * 8u;
         uint32_t nc4 = (gvalid && !verb && lmax > 0) ? 0u : 256u;
         uint32_t oa = slots_a + lane * (kSlot * 4);
-        uint64_t acc = 0;
+        uint32_t cur = 0;                   // the slot word being filled, 8 nibbles
         while (nc4 < 256u) {
-            const uint32_t wa = buf_a + min(q >> 5, lim) * 4;
+            const uint32_t wa = (q >> 3) & ~3u;
             const uint32_t win = __builtin_amdgcn_alignbit(lds_ld(wa), lds_ld(wa + 4), ~q);
             uint32_t e = lds_ld((win >> 18) & 0x3FFCu);      // table entry win>>20
             if (e == 0) {                   // first codeword longer than 12 bits
@@ -193,13 +199,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
                 e = (d & 15u) | (4u << 8) | ((d >> 4) << 16);
             }
             q += e & 0xFFu;
-            acc |= uint64_t(e >> 16) << (nc4 & 31u);
-            lds_st(oa, uint32_t(acc));
-            lds_st(oa + 4, uint32_t(acc >> 32));
+            // append up to 4 nibbles at bit s of the word and store it; when
+            // they run past bit 31 (then s >= 16) the word is complete and
+            // its overflow, syms >> (32 - s), starts the next one
+            const uint32_t syms = e >> 16, s = nc4 & 31u;
+            cur |= syms << s;
+            lds_st(oa, cur);
             const uint32_t nn = nc4 + ((e >> 8) & 0xFFu);
-            const uint32_t c = (nn ^ nc4) & 32u;   // a word of 8 nibbles completed
-            acc >>= c;
-            oa += c >> 3;
+            const bool done = ((nn ^ nc4) & 32u) != 0;
+            const uint32_t spill = __builtin_amdgcn_alignbit(0u, syms, 32u - s);
+            cur = done ? spill : cur;
+            oa += done ? 4u : 0u;
             nc4 = nn;
         }
 
