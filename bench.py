@@ -889,7 +889,7 @@ def main():
     a = parse()
     if a.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {a.gpus}); the compressed matmul path is "
-              "per-GPU work and this build runs it on a single MI355X", file=sys.stderr)
+              "per-GPU work, measured here on a single MI355X", file=sys.stderr)
         sys.exit(2)
     import torch
     import mlp_matmul_amd as uw

@@ -52,7 +52,7 @@ extern "C" {
 #define UW_ENOMEM       -2   /* host allocation failed */
 #define UW_EFORMAT      -3   /* blob fails validation */
 #define UW_EHIP         -4   /* HIP runtime error */
-#define UW_EUNSUPPORTED -5   /* valid request this build does not handle */
+#define UW_EUNSUPPORTED -5   /* valid request the library does not handle */
 
 /* Thread-local text of the last error on this thread ("" if none). */
 const char* uw_last_error(void);

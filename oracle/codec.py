@@ -15,7 +15,7 @@ What the Unweight page fixes (Cloudflare, "Unweight: how we compressed an LLM
     palette indices (a quarter); the direct-palette form is that 4-bit form
     produced once at load time.
 
-Readings where the page is silent (each listed in the design doc):
+Readings taken where the page is silent:
   * a "64-element row" is 64 consecutive elements along a storage row
     (in-features), so C % 64 == 0 is required; it is called a *group*;
   * the palette is per matrix, ordered by (descending count, ascending
