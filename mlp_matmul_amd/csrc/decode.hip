@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kDecWaves = 8;
 constexpr int kMlutEntries = 4096;      // 12-bit index
+constexpr int kTailWords = 16;          // the last 64 single-symbol entries, bytes
 constexpr int kSlot = 9;                // LDS words per lane: 64 nibbles + one overflow word
 constexpr int kStageRounds = 4;         // 16-byte loads per lane issued before one wait
 
@@ -82,15 +83,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile metadata in scalar loads
     const int lmax = a.lmax;
     const uint32_t bw = uint32_t(a.buf_words);   // multiple of 4
-    // LDS: the multi-symbol table (at address 0) and the nibble-pair table
-    // shared by the workgroup, then per wave [stream buffer | 64 symbol slots]
+    // LDS: the multi-symbol table (at address 0), the nibble-pair table and
+    // the single-symbol table's tail shared by the workgroup, then per wave
+    // [stream buffer | 64 symbol slots]
     const uint32_t wave_words = bw + 64 * kSlot;
     uint32_t* mlut = lds;
     uint32_t* ptab = lds + kMlutEntries;
-    uint32_t* buf = ptab + 256 + wave * wave_words;
+    uint8_t* tail = reinterpret_cast<uint8_t*>(ptab + 256);
+    uint32_t* buf = ptab + 256 + kTailWords + wave * wave_words;
     // byte addresses; the empty asm keeps the wave's base one opaque scalar
     // so that each window read needs a single address instruction
-    uint32_t buf_a = uint32_t((kMlutEntries + 256 + wave * wave_words) * 4);
+    uint32_t buf_a = uint32_t((kMlutEntries + 256 + kTailWords + wave * wave_words) * 4);
     asm("" : "+s"(buf_a));
     const uint32_t slots_a = buf_a + bw * 4;
     const uint32_t ptab_a = kMlutEntries * 4;
@@ -107,6 +110,14 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
         uint32_t lo = pal_byte(a, tid & 15), hi = pal_byte(a, tid >> 4);
         ptab[tid] = MODE == MODE_FULL ? (lo << 7) | (hi << 23) : lo | (hi << 8);
     }
+    // A window whose first codeword is longer than the 12-bit index starts
+    // with one of the longest, numerically largest canonical codes, so its
+    // lmax-bit value lies in the top of the single-symbol table: at most 16
+    // codes of 13-15 bits cover at most 16 * 4 = 64 such values.  That tail
+    // is kept here, so the fallback is an LDS read, not a global load.
+    const uint32_t dlut_n = 1u << lmax;
+    const uint32_t tail_base = dlut_n > 64u ? dlut_n - 64u : 0u;
+    if (tid < 64) tail[tid] = tail_base + uint32_t(tid) < dlut_n ? a.dlut[tail_base + uint32_t(tid)] : uint8_t(0);
     __syncthreads();
 
     // waves take tiles independently (no workgroup barrier in the loop)
@@ -170,6 +181,16 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
         stage(0);
         for (uint32_t base = 256 * kStageRounds; base < need; base += 256 * kStageRounds) stage(base);
         wave_lds_sync();
+        // FULL: the sign/mantissa bytes of the lane's output elements go out
+        // now and arrive during the lookups
+        u32x2_t smv[8];
+        if (MODE == MODE_FULL) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int64_t e = e0 + 512 * k;
+                smv[k] = load_stream8(a.sm + (e < N ? e : 0));
+            }
+        }
 
         uint32_t incl = gl;
 #pragma unroll
@@ -195,7 +216,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
             const uint32_t win = __builtin_amdgcn_alignbit(lds_ld(wa), lds_ld(wa + 4), ~q);
             uint32_t e = lds_ld((win >> 18) & 0x3FFCu);      // table entry win>>20
             if (e == 0) {                   // first codeword longer than 12 bits
-                const uint32_t d = a.dlut[win >> fb_shift];
+                const uint32_t d = tail[((win >> fb_shift) - tail_base) & 63u];
                 e = (d & 15u) | (4u << 8) | ((d >> 4) << 16);
             }
             q += e & 0xFFu;
@@ -226,17 +247,6 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
             }
         } else {
             wave_lds_sync();     // slots are read across lanes
-            // sign/mantissa bytes of the lane's elements (loaded here rather
-            // than before the decode loop: keeps the kernel within 80 VGPRs,
-            // 6 waves per SIMD)
-            u32x2_t smv[8];
-            if (MODE == MODE_FULL) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int64_t e = e0 + 512 * k;
-                    smv[k] = load_stream8(a.sm + (e < N ? e : 0));
-                }
-            }
             // non-verbatim groups: 8 elements per lane, 512 per instruction
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -289,7 +299,7 @@ size_t decode_lds_bytes(int lmax, uint32_t max_tile_bytes, int* buf_words) {
     (void)lmax;
     const int bw = ((int(max_tile_bytes) + 3) / 4 + 3 + 3) & ~3;
     if (buf_words) *buf_words = bw;
-    return (size_t(kMlutEntries) + 256 + size_t(kDecWaves) * (bw + 64 * kSlot)) * 4;
+    return (size_t(kMlutEntries) + 256 + kTailWords + size_t(kDecWaves) * (bw + 64 * kSlot)) * 4;
 }
 
 hipError_t launch_decode(int mode, const DecodeArgs& a0, hipStream_t s) {

@@ -236,3 +236,35 @@ def test_plan_table_roundtrip(tmp_path):
     with pytest.raises(uw.UnweightError):
         uw.plan_set(1, 64, 1, 7, 0, 1)
     uw.plan_clear()
+
+
+@pytest.mark.parametrize("lengths", [
+    list(range(1, 15)) + [15, 15],                                  # the one 16-symbol shape reaching 15 bits
+    [2, 2, 2] + list(range(3, 14)) + [14, 14],
+    list(range(1, 13)) + [14, 14, 14, 14],
+    list(range(1, 11)) + [12, 12, 13, 13, 13, 13],
+])
+def test_long_codewords_fill_the_top_of_the_decode_table(lengths):
+    """The decoders keep only the last 64 entries of the single-symbol table
+    in LDS for windows whose first codeword is longer than the 12-bit
+    multi-symbol index.  That relies on canonical codes: the longest codes
+    are numerically the largest, so such windows are the top lmax-bit values,
+    at most 16 codes x 2^(15-13) = 64 of them.  Checked here on the tables
+    the host builds, for 16-symbol codes with 13-15-bit codewords."""
+    assert len(lengths) == 16 and sum(2.0 ** -l for l in lengths) == 1.0
+    # exponent 100+s repeated 2^(15 - len) times: dyadic counts, for which an
+    # optimal code has these lengths
+    counts = [2 ** (15 - l) for l in lengths]
+    exps = np.repeat(np.arange(100, 116, dtype=np.uint16), counts)
+    w = ((exps << 7) | (np.arange(exps.size, dtype=np.uint16) & 0x7F)).astype(np.uint16)
+    w = np.random.default_rng(5).permutation(w).reshape(-1, 256)
+    b = uw.compress(w)
+    L = b.info().lmax
+    assert L == max(lengths) and sorted(b.info().lengths[:16]) == sorted(lengths)
+    mlut = np.frombuffer(b.section("mlut"), np.uint32)
+    v = np.arange(1 << L)
+    long_first = mlut[v >> (L - 12)] == 0                        # first codeword over 12 bits
+    assert long_first.any()
+    lo = int(v[long_first].min())
+    assert lo >= (1 << L) - 64
+    assert long_first[lo:].all()                                 # one run up to the top
