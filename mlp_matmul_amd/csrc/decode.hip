@@ -23,7 +23,10 @@
 // accumulator whose words go to a per-lane LDS slot.  The output phase then
 // walks the tile in element order, 8 elements per lane and 512 per wave
 // instruction, so that exponent and bf16 stores (and the sign/mantissa
-// loads) are contiguous across the wave.  The stream buffer is sized by the
+// loads) are contiguous across the wave; it maps palette indices to
+// exponents through an LDS table of nibble pairs (full bf16) or with byte
+// permutes of the palette held in registers (exponent-only, where it
+// measured faster: the lookup loop already keeps LDS busy).  The stream buffer is sized by the
 // matrix's longest tile, which keeps LDS per wave small enough for several
 // workgroups per CU.
 #include "device_common.h"
@@ -105,10 +108,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
 
     for (int i = tid; i < kMlutEntries / 4; i += 64 * kDecWaves)
         reinterpret_cast<u32x4_t*>(mlut)[i] = reinterpret_cast<const u32x4_t*>(a.mlut)[i];
-    if (tid < 256) {
-        // nibble pair -> (FULL) two exponents in bf16 position, (EXP, PAL) two exponent bytes
+    if (MODE == MODE_FULL && tid < 256) {
+        // nibble pair -> two exponents in bf16 position
         uint32_t lo = pal_byte(a, tid & 15), hi = pal_byte(a, tid >> 4);
-        ptab[tid] = MODE == MODE_FULL ? (lo << 7) | (hi << 23) : lo | (hi << 8);
+        ptab[tid] = (lo << 7) | (hi << 23);
     }
     // A window whose first codeword is longer than the 12-bit index starts
     // with one of the longest, numerically largest canonical codes, so its
@@ -118,6 +121,18 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
     const uint32_t dlut_n = 1u << lmax;
     const uint32_t tail_base = dlut_n > 64u ? dlut_n - 64u : 0u;
     if (tid < 64) tail[tid] = tail_base + uint32_t(tid) < dlut_n ? a.dlut[tail_base + uint32_t(tid)] : uint8_t(0);
+    // EXP output: four palette indices (one per byte) -> their exponent
+    // bytes with v_perm on the 16 palette bytes held in four uniform words
+    // (selectors 0-7 pick a byte; 12 and 13 give 0x00 and 0xFF, the mask
+    // choosing entries 8-15)
+    const uint32_t P0 = __builtin_amdgcn_readfirstlane(a.pal[0]), P1 = __builtin_amdgcn_readfirstlane(a.pal[1]);
+    const uint32_t P2 = __builtin_amdgcn_readfirstlane(a.pal[2]), P3 = __builtin_amdgcn_readfirstlane(a.pal[3]);
+    auto pal4 = [&](uint32_t x) {
+        const uint32_t sel = x & 0x07070707u;
+        const uint32_t lo8 = __builtin_amdgcn_perm(P1, P0, sel), hi8 = __builtin_amdgcn_perm(P3, P2, sel);
+        const uint32_t m = __builtin_amdgcn_perm(0u, 0u, ((x >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+        return (hi8 & m) | (lo8 & ~m);
+    };
     __syncthreads();
 
     // waves take tiles independently (no workgroup barrier in the loop)
@@ -254,13 +269,16 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
                 const int64_t e = e0 + 512 * k;
                 if (e >= N || ((word >> gi) & 1ull)) continue;
                 const uint32_t nw32 = lds_ld(slots_a + gi * (kSlot * 4) + 4 * (lane & 7));
-                uint32_t pr[4];     // ptab entries of the 4 nibble pairs
-#pragma unroll
-                for (int i = 0; i < 4; ++i) pr[i] = lds_ld(ptab_a + ((nw32 >> (8 * i)) & 0xFFu) * 4);
                 if (MODE == MODE_EXP) {
+                    // palette lookups in registers: even and odd elements'
+                    // exponents, then interleaved into element order
+                    const uint32_t ev = pal4(nw32 & 0x0F0F0F0Fu), od = pal4((nw32 >> 4) & 0x0F0F0F0Fu);
                     *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(a.out) + e) =
-                        u32x2_t{pr[0] | (pr[1] << 16), pr[2] | (pr[3] << 16)};
+                        u32x2_t{__builtin_amdgcn_perm(od, ev, 0x05010400u), __builtin_amdgcn_perm(od, ev, 0x07030602u)};
                 } else {
+                    uint32_t pr[4];     // ptab entries of the 4 nibble pairs
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) pr[i] = lds_ld(ptab_a + ((nw32 >> (8 * i)) & 0xFFu) * 4);
                     const u32x2_t s8 = smv[k];
                     store16(static_cast<uint16_t*>(a.out) + e,
                             u32x4_t{join_pair<0>(s8[0], pr[0]), join_pair<1>(s8[0], pr[1]),
