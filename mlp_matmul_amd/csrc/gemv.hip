@@ -247,9 +247,21 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16
         issue_v(it0, sets[0]);
     }
     if (XLDS) {
+        // four 16-byte pieces per thread go out before one wait (a load,
+        // wait, store loop pays an L2 round trip per piece: seven of them
+        // for a 14336-column row); pieces past the end re-read the last one,
+        // so no load is conditional, and are not stored
         const int64_t n16 = int64_t(B) * C / 8;
-        for (int64_t i = tid; i < n16; i += 256)
-            reinterpret_cast<u32x4_t*>(xs)[i] = load16(a.X + i * 8);
+        for (int64_t i0 = tid; i0 < n16; i0 += 256 * 4) {
+            u32x4_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = load16(a.X + min(i0 + 256 * u, n16 - 1) * 8);
+            // a use of all four here keeps each load out of its store's branch
+            asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i0 + 256 * u < n16) reinterpret_cast<u32x4_t*>(xs)[i0 + 256 * u] = v[u];
+        }
     }
     __syncthreads();
     if (!live) return;
