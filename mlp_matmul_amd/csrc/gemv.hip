@@ -464,8 +464,11 @@ void launch_x(const MatArgs& a, hipStream_t s) {
     // measured on MI355X at batch 1: the bf16 kernel runs faster reading its
     // one activation row from L2 (20.8 against 21.5 us on 14336x4096), the
     // rebuilding kernels faster from LDS (16.7 against 18.8 us, palette)
+    // except on matrices of few rows, whose workgroups (about one per CU)
+    // cannot hide the staging (1024x4096: 4.8-4.9 against 5.2-5.6 us; at
+    // 4096x4096 LDS stays ahead, 7.3 against 7.4 us)
     static const int xg_env = env_int("UW_GEMV_XGLOBAL", -1);
-    const bool xglobal = xg_env >= 0 ? xg_env == 1 : (SRC == SRC_BF16 && a.B == 1);
+    const bool xglobal = xg_env >= 0 ? xg_env == 1 : (a.B == 1 && (SRC == SRC_BF16 || a.R < 4096));
     if (a.B * a.C * 2 <= kXLdsMax && !xglobal) launch_cfg<SRC, MB, NRW, true>(a, s);
     else launch_cfg<SRC, MB, NRW, false>(a, s);
 }
