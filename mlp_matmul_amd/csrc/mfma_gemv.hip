@@ -417,7 +417,9 @@ int env_int(const char* name, int dflt) {
 // K-split width, prefetch depth and row blocks per wavefront, as measured on
 // the Llama MLP and attention shapes at batch 2..16 (UW_SKINNY_KW / _PD / _RB
 // override for tuning).  The K-split is the smallest that gives about one
-// wave per SIMD (a 14336-row matrix: 2; 4096 rows: 4; 1024 rows: 8), and at
+// 16-row block per SIMD (a 14336-row matrix: 2; 4096 rows: 4; 1024 rows: 8;
+// blocks, not waves: with two blocks per wave, gate at batch 24 and 32 runs
+// 24.7 and 25.7 us at split 2 against 28.7 and 29.5 us at split 4), and at
 // least what keeps one wave's slice within kMaxSlice columns.  One row
 // block per wave up to batch 16 (with the tiles staged through LDS a second
 // block saves little activation traffic and halves the workgroups), two on
@@ -436,7 +438,7 @@ Shape choose_shape(const MatArgs& a) {
         const int64_t simds = 4 * int64_t(a.cus > 0 ? a.cus : 256);
         const int64_t waves_per_kw = (a.R + 16 * rb - 1) / (16 * rb) * ((a.B + 63) / 64);
         kw = 2;
-        while (kw < 8 && waves_per_kw * kw < simds) kw *= 2;
+        while (kw < 8 && waves_per_kw * rb * kw < simds) kw *= 2;
     }
     kw = kw <= 2 ? 2 : (kw <= 4 ? 4 : 8);
     while (kw < 8 && (steps + kw - 1) / kw * kKStep > kMaxSlice) kw *= 2;
