@@ -301,7 +301,8 @@ int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, voi
  * gate, up: same shape [rows, cols], both with a NIB section; X bf16 bits
  * [batch, cols]; h bf16 bits [batch, rows]; g_out, u_out fp32 [batch, rows]
  * or NULL (not written).  Device pointers, 16-byte aligned, caller-owned.
- * UW_EINVAL on NULL/misaligned pointers or mismatched shapes;
+ * UW_EINVAL on NULL/misaligned pointers, mismatched shapes, an inconsistent
+ * descriptor, or verbatim groups without their VEXP section;
  * UW_EUNSUPPORTED unless 1 <= batch <= 16, cols % 128 == 0, cols <= 32768
  * and the library splits K at most 4 ways for this shape on the current
  * device (about one wave per SIMD: at least ~4096 rows on MI355X), or, at

@@ -11,21 +11,25 @@ the fastest, and records it in the library's plan table (``uw_plan_set``) that
 
 Timing rotates over several distinct copies of the matrix (different layers)
 so that the 256 MiB Infinity Cache cannot serve the weights.  Each candidate's
-output is checked once against the full-decode pipeline (whose rebuilt weights
-are bit-exact) so that a broken candidate can never win.
+output is checked once, element by element, against the full-decode pipeline
+(whose rebuilt weights are bit-exact) with a per-output bound from
+sum_c |W[r,c] X[b,c]|, so that a broken candidate can never win.
 """
 from __future__ import annotations
 
 import ctypes as ct
 import json
 
-import numpy as np
 
 from . import (UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY, UW_PIPE_DIRECT, UW_PIPE_EXP, UW_PIPE_FULL, UW_PIPE_PAL,
-               check, lib, plan_set, scratch_bytes)
+               check, decode_full, lib, plan_set, scratch_bytes)
 
 PIPE_NAMES = {UW_PIPE_FULL: "full", UW_PIPE_EXP: "exp", UW_PIPE_PAL: "pal", UW_PIPE_DIRECT: "direct"}
 KERNEL_NAMES = {UW_KERNEL_GEMV: "gemv", UW_KERNEL_MFMA: "mfma", UW_KERNEL_SKINNY: "skinny"}
+# a candidate's outputs must stay within this many times sum_c |W[r,c] X[b,c]|
+# of the exact product (fp32 accumulation over up to 14336 terms stays well
+# inside it)
+TOL = 2e-3
 
 
 def skinny_ok(cols):
@@ -100,15 +104,22 @@ def tune_shape(copies, batch, X, reps=20, warmup=3, stream=None):
                stream)()
     stream.synchronize()
     ref = Y.clone()
-    scale = float(ref.abs().max()) + 1e-30
+    # per-output scale S[b, r] = sum_c |W[r, c] X[b, c]| from the decoded
+    # weights; a candidate and the reference each sit within 2e-3 * S of the
+    # exact product, so they may differ by at most twice that
+    with torch.cuda.stream(stream):
+        Wd = decode_full(copies[0], stream=stream.cuda_stream)
+        S = torch.matmul(X.float().abs(), Wd.float().abs().t().contiguous())
+    stream.synchronize()
+    del Wd
     table = []
     for cand in cands:
         with torch.cuda.stream(stream):
             Y.fill_(float("nan"))
             _Bound(copies[0], *cand, X, Y, scratch, stream)()
         stream.synchronize()
-        err = float((Y - ref).abs().max())
-        ok = bool(np.isfinite(err) and err <= 1e-2 * scale)
+        diff = (Y - ref).abs()
+        ok = bool(torch.isfinite(Y).all() and (diff <= 2 * TOL * S).all())
         t = time_candidate(copies, X, Y, scratch, cand, stream, reps, warmup) if ok else None
         table.append({"pipeline": PIPE_NAMES[cand[0]], "kernel": KERNEL_NAMES[cand[1]], "split_k": cand[2],
                       "us": None if t is None else round(t * 1e6, 3), "valid": ok})

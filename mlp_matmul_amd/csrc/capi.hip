@@ -110,13 +110,10 @@ int device_cus() {
     return cus;
 }
 
-// The kernel family UW_KERNEL_AUTO picks for a shape (measured on MI355X on
-// the Llama MLP shapes: the GEMV below batch 4, the skinny MFMA kernel up to
-// batch 16, the tiled MFMA kernel from batch 17, which is faster than the
-// skinny kernel at batch 32 and 64 on both shapes).
-// Measured on MI355X (Llama MLP shapes): the GEMV wins at batch 1 (below
-// batch 4 for bf16 weights), the skinny MFMA kernel from there through 32
-// (the autotuner's choice at batch 32 on both shapes), the tiled kernel above.
+// The kernel family UW_KERNEL_AUTO picks for a shape.  Measured on MI355X
+// (Llama MLP shapes): the GEMV wins at batch 1 (below batch 4 for bf16
+// weights), the skinny MFMA kernel from there through 32 (the autotuner's
+// choice at batch 32 on both shapes), the tiled kernel above.
 int auto_kernel(int src, const uwk::MatArgs& a) {
     const int64_t gemv_below = src == uwk::SRC_BF16 ? 4 : 2;
     return a.B < gemv_below ? UW_KERNEL_GEMV
@@ -449,9 +446,14 @@ int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, in
     if (gate->rows == 0 || batch == 0) return UW_OK;
     if (!X || !h || !aligned16(X) || !aligned16(h) || (g_out && !aligned16(g_out)) || (u_out && !aligned16(u_out)))
         return uw::fail(UW_EINVAL, std::string(who) + ": NULL or misaligned device pointer");
-    for (const uw_dmat* d : {gate, up})
+    for (const uw_dmat* d : {gate, up}) {
+        int rc = check_dmat(d, who);
+        if (rc) return rc;
         if (!d->nib || !d->sm || !d->bitmap || !d->tile_vbase || !aligned16(d->nib) || !aligned16(d->sm))
             return uw::fail(UW_EINVAL, std::string(who) + ": a matrix lacks its NIB/SM/BITMAP/TILE_VBASE sections");
+        if (d->verbatim_groups && !d->vexp)
+            return uw::fail(UW_EINVAL, std::string(who) + ": verbatim exponents missing");
+    }
     uwk::MatArgs g = compressed_args(gate, gate->nib, X, batch, g_out);
     uwk::MatArgs u = compressed_args(up, up->nib, X, batch, u_out);
     g.cus = u.cus = device_cus();

@@ -45,3 +45,17 @@ def assert_matmul_close(Y_gpu, w_bits, x_bits, rows=None, what=""):
 
 def print_case(msg):
     print(msg, flush=True)
+
+
+def bf16_order_key(b):
+    """bf16 bit patterns as integers ordered like their values (so that one
+    ulp apart means a difference of 1)."""
+    b = np.asarray(b).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+def check_silu_product(h_bits, g, u, what=""):
+    """h within one bf16 ulp of bf16(SiLU(g)*u) computed in fp64 on the same g, u."""
+    href = numerics.f64_to_bf16_bits(numerics.silu_mul(g, u))
+    d = np.abs(bf16_order_key(h_bits) - bf16_order_key(href)).max() if href.size else 0
+    assert d <= 1, f"{what}: h off by {d} bf16 ulps"

@@ -21,13 +21,44 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 
 
 def test_profiled_run_flags_parse(monkeypatch):
-    monkeypatch.setattr(sys, "argv", ["bench.py", "--steps", "20", "--warmup", "5", "--no-graph",
-                                      "--no-kernel-timer", "--copy-calibration"])
-    a = bench.parse()
-    assert (a.steps, a.warmup, a.no_graph, a.no_kernel_timer, a.copy_calibration) == (20, 5, True, True, True)
-    monkeypatch.setattr(sys, "argv", ["bench.py"])
-    a = bench.parse()
+    a = bench.parse(["--steps", "20", "--warmup", "5", "--no-kernel-timer", "--copy-calibration", "--no-sweep",
+                     "--no-cpu-baseline", "--no-compare"])
+    assert (a.steps, a.warmup, a.no_kernel_timer, a.copy_calibration, a.no_sweep) == (20, 5, True, True, True)
+    a = bench.parse([])
     assert a.gpus == 1 and a.steps > 0 and a.warmup > 0 and not a.no_kernel_timer
+    assert a.layers == 32 and a.batch == 1 and a.min_warmup_ms >= 50
+
+
+def test_headline_line_stays_compact():
+    """The stdout line the benchmark prints, with every field at a realistic
+    width, stays under 2 KB (the sweep detail goes to a file)."""
+    line = {
+        "metric": bench.METRIC, "value": 6666.6, "unit": "GB/s", "n_gpus": 1, "steps": 20, "warmup": 5,
+        "warmup_steps_run": 120, "ms_per_step": 1.6912, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3.1-8b-mlp-stack", "layers": 32, "batch": 1, "gate_up": [14336, 4096],
+                   "down": [4096, 14336], "pipeline": "auto",
+                   "plan": {"14336x4096": "direct/gemv", "4096x14336": "direct/gemv"}, "gate_up_fused": True,
+                   "weights": "N(0,0.02)+U[0.01%,0.2%] N(0,0.5) outliers per layer, seeded"},
+        "compressed_GBps": 5100.1, "compressed_hbm_frac": 0.6375, "bf16_ms_per_step": 1.9812,
+        "speedup_vs_bf16": 1.1715, "sizes_GB": {"bf16": 11.27, "huffman": 7.78, "palette": 8.65},
+        "verbatim_group_frac": 0.03093, "decode_bitexact": "96/96",
+        "roofline": {"bound": "hbm", "achieved": 6200.1, "peak": 8000.0, "unit": "GB/s", "frac": 0.775,
+                     "traffic": 181783460.0, "kernel": "fused gate/up + SiLU (direct palette)", "launches": 640,
+                     "avg_launch_us": 28.951, "bytes_per_launch": 179530408,
+                     "profile_avg_us": 30.039,
+                     "all_matmuls_frac": 0.7391, "per_kind_avg_us": {"gate_up": 28.95, "down": 16.71}},
+        "sweep": {"cols": "batch,ms,bf16_ms,x_bf16",
+                  "rows": [[b, 1.6912, 1.9812, 1.1715] for b in (1, 2, 4, 8, 16, 32, 64, 128, 256)]},
+        "cpu_baseline": {"value": 0.6512, "unit": "GB/s", "cores": 16, "kind": "oracle",
+                         "sample": "stack layer 0, 1/16 of gate/up/down rows, B=1: 4-bit rebuild + fp64 matmul + "
+                                   "SiLU, 33 reps/6.1 s; codec 1 thread, BLAS 16",
+                         "stages_GBps": {f"c{i}": [0.0123, 0.0321, 0.0321, 0.0321, 0.123, 1.23] for i in range(1, 6)},
+                         "stage_order": ",".join(bench.CPU_STAGES), "seconds": 31.2},
+        "detail": "gpurun_out/bench_detail.json",
+    }
+    import json
+    assert len(json.dumps(line, separators=(",", ":"), ensure_ascii=False).encode()) < 2000
 
 
 @pytest.mark.parametrize("name", sorted(f[:-3] for f in os.listdir(os.path.join(ROOT, "profiles"))

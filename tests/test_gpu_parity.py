@@ -659,6 +659,14 @@ def test_gate_up_fused_rejects(torch_cuda):
     with pytest.raises(uw.UnweightError) as ei:
         uw.mlp_gate_up(dn, du, to_dev_bf16(_x(1, 1, 512)))
     assert ei.value.code == uw.UW_EINVAL
+    # every exponent pattern: most groups verbatim, uploaded without VEXP
+    spread = workloads.random_bf16_bits(9, 64 * 512).reshape(64, 512)
+    blob = uw.compress(spread)
+    assert blob.info().verbatim_groups > 0
+    dv = blob.to_device(("sm", "nib", "bitmap", "tile_vbase"))
+    with pytest.raises(uw.UnweightError) as ei:
+        uw.mlp_gate_up(dv, dv, to_dev_bf16(_x(1, 1, 512)))
+    assert ei.value.code == uw.UW_EINVAL and "verbatim" in str(ei.value)
 
 
 # --------------------------------------------------------------- full sizes

@@ -47,15 +47,18 @@ STACK_P_HI = 2e-3
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
 
-    NaNs stay NaN (quiet bit forced), infinities stay infinite.
+    NaNs stay NaN (quiet bit forced), infinities stay infinite.  The rounding
+    add is done in 32-bit arithmetic: for every non-NaN pattern the sum stays
+    below 2^32 (the largest finite magnitude 0x7F7FFFFF plus 0x8000, with the
+    sign bit at most 0xFF807FFF), and NaNs are replaced afterwards.
     """
     a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = a.view(np.uint32)
+    with np.errstate(over="ignore"):
+        r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
-        r[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+        r[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return r
 
 
