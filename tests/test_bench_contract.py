@@ -78,5 +78,6 @@ def test_committed_profiles_match_the_kernel_sources(name):
 
 
 def test_headline_traffic_comes_from_the_current_profile():
-    t = bench.traffic_from_profiles("gemv_gateup_pal_llama_mlp_b1")
-    assert t is not None and 1.7e8 < t < 2.0e8     # ~180 MB read per fused gate/up launch
+    traffic, avg_us = bench.profile_figures("gemv_gateup_pal_llama_mlp_stack_b1")
+    assert traffic is not None and 1.7e8 < traffic < 2.0e8     # ~182 MB read per fused gate/up launch
+    assert avg_us is not None and 20 < avg_us < 40
