@@ -258,6 +258,26 @@ int uw_gemm_recon_pal(const uw_dmat* d, const uint8_t* nib,
                       int kernel, int split_k, void* scratch, uint64_t scratch_bytes,
                       void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * uw_gemm_recon_pal with the tiled MFMA kernel's split-K partial sums kept in
+ * a library-owned device array of UW_STATIC_SCRATCH_BYTES per GPU (reserved
+ * on each device the library runs on until the process ends) instead of
+ * caller scratch.  Same arguments, kernels and results as uw_gemm_recon_pal
+ * with that scratch: bit-identical output for the same kernel and split_k.
+ * split_k 0 takes the library's split lowered to what the array holds; an
+ * explicit split_k > 1 with split_k * batch * rows * 4 above
+ * UW_STATIC_SCRATCH_BYTES is UW_EINVAL.  Allocates nothing: no hipMalloc,
+ * hipFree or allocating library call.  Every call on a GPU shares that GPU's
+ * array, so calls that overlap on one GPU (on different streams, or from
+ * several threads without ordering) race on it; calls ordered on one stream
+ * are safe.  The array keeps the last call's partial sums (every launch writes
+ * the partials it reads). */
+#define UW_STATIC_SCRATCH_BYTES (64ull << 20)
+int uw_gemm_recon_pal_static(const uw_dmat* d, const uint8_t* nib,
+                             const uint16_t* X, int64_t batch, float* Y,
+                             int kernel, int split_k, void* stream);
+
 /* ------------------------------------------------------------- pipelines */
 enum {
     UW_PIPE_AUTO = 0,     /* consult the plan table (uw_plan_*) */

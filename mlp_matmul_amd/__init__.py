@@ -19,7 +19,8 @@ from ._capi import (  # noqa: F401
     SECTION_NAMES, UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY, UW_NUM_SECTIONS,
     UW_PIPE_AUTO, UW_PIPE_BF16, UW_PIPE_DIRECT, UW_PIPE_EXP, UW_PIPE_FULL, UW_PIPE_PAL,
     UW_SEC_BITMAP, UW_SEC_DLUT, UW_SEC_GLEN, UW_SEC_MLUT, UW_SEC_NIB, UW_SEC_SM, UW_SEC_STREAM,
-    UW_SEC_TILE_OFF, UW_SEC_TILE_VBASE, UW_SEC_VEXP, UW_EUNSUPPORTED, UW_EINVAL, UnweightError, check, lib,
+    UW_SEC_TILE_OFF, UW_SEC_TILE_VBASE, UW_SEC_VEXP, UW_EUNSUPPORTED, UW_EINVAL, UW_STATIC_SCRATCH_BYTES,
+    UnweightError, check, lib,
     uw_dmat, uw_info,
     uw_opts,
 )
@@ -217,6 +218,17 @@ def gemm_recon_pal(dm: DeviceMatrix, nib, X, Y=None, kernel=UW_KERNEL_AUTO, spli
     nibp = _ptr(nib) if nib is not None else ct.c_void_p(dm.dmat.nib)
     check(lib().uw_gemm_recon_pal(ct.byref(dm.dmat), nibp, _ptr(X), batch, _ptr(Y), kernel, split_k, sp, sb,
                                   _stream(stream)), "uw_gemm_recon_pal")
+    return Y
+
+
+def gemm_recon_pal_static(dm: DeviceMatrix, nib, X, Y=None, kernel=UW_KERNEL_AUTO, split_k=0, stream=None):
+    """uw_gemm_recon_pal_static: the palette-source matmul with its split-K
+    partials in the library's static device array (no caller scratch)."""
+    batch = X.shape[0]
+    Y = _y(Y, batch, dm.rows)
+    nibp = _ptr(nib) if nib is not None else ct.c_void_p(dm.dmat.nib)
+    check(lib().uw_gemm_recon_pal_static(ct.byref(dm.dmat), nibp, _ptr(X), batch, _ptr(Y), kernel, split_k,
+                                         _stream(stream)), "uw_gemm_recon_pal_static")
     return Y
 
 

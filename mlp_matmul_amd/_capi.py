@@ -21,6 +21,7 @@ SECTION_NAMES = ("sm", "stream", "glen", "tile_off", "tile_vbase", "vexp", "bitm
 
 UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY = 0, 1, 2, 3
 UW_PIPE_AUTO, UW_PIPE_FULL, UW_PIPE_EXP, UW_PIPE_PAL, UW_PIPE_DIRECT, UW_PIPE_BF16 = range(6)
+UW_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class uw_opts(ct.Structure):
@@ -76,6 +77,7 @@ SIGNATURES = {
     "uw_gemm_bf16": (_INT, [_P, _I64, _I64, _P, _I64, _P, _INT, _INT, _P, _U64, _P]),
     "uw_gemm_recon_exp": (_INT, [ct.POINTER(uw_dmat), _P, _P, _I64, _P, _INT, _INT, _P, _U64, _P]),
     "uw_gemm_recon_pal": (_INT, [ct.POINTER(uw_dmat), _P, _P, _I64, _P, _INT, _INT, _P, _U64, _P]),
+    "uw_gemm_recon_pal_static": (_INT, [ct.POINTER(uw_dmat), _P, _P, _I64, _P, _INT, _INT, _P]),
     "uw_scratch_bytes": (_I64, [_INT, _I64, _I64, _I64, _INT]),
     "uw_matmul": (_INT, [ct.POINTER(uw_dmat), _INT, _INT, _INT, _P, _I64, _P, _P, _U64, _P]),
     "uw_silu_mul_bf16": (_INT, [_P, _P, _I64, _P, _P]),

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <atomic>
 #include <map>
+#include <mutex>
 #include <cstdlib>
 #include <cstring>
 #include <string>
@@ -293,6 +294,35 @@ int layer_events(LayerEvents** out) {
     return UW_OK;
 }
 
+// ------------------------------------------------ allocation-free variant
+// uw_gemm_recon_pal_static keeps the tiled kernel's split-K partial sums in
+// this file-scope device array instead of caller scratch.  In host code the
+// name `scratch` is only a stand-in for the array: its device address, one
+// copy per GPU, comes from hipGetSymbolAddress and is what every launch gets.
+static __device__ __align__(256) uint8_t scratch[UW_STATIC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_static_mu;
+void* g_static_ptr[64];        // per device ordinal: the address of `scratch` there
+
+int static_scratch(void** out, const char* who) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, who);
+    if (dev < 0 || dev >= 64) return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": device ordinal above 63");
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, who);
+        if (!p) return uw::fail(UW_EHIP, std::string(who) + ": no device address for the static scratch");
+        g_static_ptr[dev] = p;
+    }
+    *out = g_static_ptr[dev];
+    return UW_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_SECTIONS]) {
@@ -560,6 +590,26 @@ int uw_mlp_layer(const uw_dmat* gate, const uw_dmat* up, const uw_dmat* down, in
         if (m == 1 && (rc = uw_silu_mul_bf16(g, u, batch * F, h, stream))) return rc;
     }
     return UW_OK;
+}
+
+int uw_gemm_recon_pal_static(const uw_dmat* d, const uint8_t* nib, const uint16_t* X, int64_t batch, float* Y,
+                             int kernel, int split_k, void* stream) {
+    uw::clear_error();
+    const char* who = "uw_gemm_recon_pal_static";
+    int rc = check_dmat(d, who);
+    if (rc) return rc;
+    if (d->groups && d->verbatim_groups && !d->vexp)
+        return uw::fail(UW_EINVAL, std::string(who) + ": verbatim exponents missing");
+    if (batch < 0 || split_k < 0 || split_k > 64) return uw::fail(UW_EINVAL, std::string(who) + ": bad batch or split_k");
+    const uint64_t need = uint64_t(split_k > 1 ? split_k : 0) * uint64_t(batch) * uint64_t(d->rows) * 4;
+    if (need > UW_STATIC_SCRATCH_BYTES)
+        return uw::fail(UW_EINVAL, std::string(who) + ": split_k * batch * rows * 4 = " + std::to_string(need) +
+                                       " bytes of partial sums exceed the static scratch of " +
+                                       std::to_string(uint64_t(UW_STATIC_SCRATCH_BYTES)) + " bytes");
+    void* p = nullptr;
+    if ((rc = static_scratch(&p, who))) return rc;
+    return run_matmul(uwk::SRC_PAL, compressed_args(d, nib, X, batch, Y), kernel, split_k, p, UW_STATIC_SCRATCH_BYTES,
+                      stream, who);
 }
 
 int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, void* stream) {
