@@ -27,10 +27,12 @@ Readings taken where the page is silent:
     length 1; codes are canonical, assigned in (length, symbol) order, and
     written MSB-first;
   * the stream is cut into tiles of 64 groups that start on a byte boundary;
-    each group's coded bit length is stored (u16) so that 64 lanes can find
-    their start bits by a prefix sum; tile byte offsets and verbatim counts
-    before each tile are u32 tables; a u64 bitmap per tile flags verbatim
-    groups, whose 64 raw exponent bytes go to a separate array;
+    each coded group's bits are followed by zero bits up to a multiple of 4
+    bits, and that padded length, in 4-bit units, is stored in one byte per
+    group (at most 64 * 15 / 4 = 240) so that 64 lanes can find their start
+    bits by a prefix sum; tile byte offsets and verbatim counts before each
+    tile are u32 tables; a u64 bitmap per tile flags verbatim groups, whose
+    64 raw exponent bytes go to a separate array;
   * the sign/mantissa byte is (sign << 7) | mantissa;
   * the 4-bit form puts element i in byte i // 2, low nibble for even i, and
     holds 0 for every element of a verbatim group.
@@ -45,6 +47,7 @@ import numpy as np
 GROUP = 64          # elements per verbatim decision ("64-element row")
 TILE = 64           # groups per independently addressable stream tile
 PALETTE_MAX = 16    # palette size: 4-bit indices
+GLEN_UNIT = 4       # bits: coded groups are padded to, and measured in, this unit
 
 
 # ------------------------------------------------------------------ field split
@@ -165,7 +168,7 @@ class Compressed:
     codes: np.ndarray            # int64[16]
     sm: np.ndarray               # uint8[N]   sign/mantissa plane
     stream: np.ndarray           # uint8[S]   Huffman stream, tiles byte aligned
-    glen: np.ndarray             # uint16[G]  coded bits of each group (0 if verbatim)
+    glen: np.ndarray             # uint8[G]   padded coded bits of each group / 4 (0 if verbatim)
     tile_off: np.ndarray         # uint32[T+1] byte offset of each tile's stream
     tile_vbase: np.ndarray       # uint32[T+1] verbatim groups before each tile
     vexp: np.ndarray             # uint8[64 V] raw exponents of verbatim groups
@@ -241,17 +244,20 @@ def encode(bits) -> Compressed:
     # per-element code length; verbatim groups contribute nothing
     L = lengths[sym].reshape(-1, GROUP) if G else np.zeros((0, GROUP), np.int64)
     L = np.where(vflag[:, None], 0, L)
-    glen = L.sum(axis=1)
+    gbits = L.sum(axis=1)                                   # code bits of each group
+    gpad = -(-gbits // GLEN_UNIT) * GLEN_UNIT               # padded to a 4-bit boundary
     # tiles start on byte boundaries
-    tile_bits = np.add.reduceat(glen, np.arange(0, G, TILE)) if G else np.zeros(0, np.int64)
+    tile_bits = np.add.reduceat(gpad, np.arange(0, G, TILE)) if G else np.zeros(0, np.int64)
     tile_bytes = (tile_bits + 7) // 8
     tile_off = np.concatenate([[0], np.cumsum(tile_bytes)]).astype(np.int64)
-    # start bit of every element: tile start + bits before it inside the tile
+    # start bit of every element: its tile's first bit + the padded lengths of
+    # the groups before it in the tile + the code bits before it in its group
     Lf = L.ravel()
     tile_of_elem = np.arange(N) // (GROUP * TILE)
-    within = np.cumsum(Lf) - Lf
-    tile_first = np.concatenate([[0], np.cumsum(tile_bits)])[:-1] if T else np.zeros(0, np.int64)
-    start = tile_off[tile_of_elem] * 8 + (within - tile_first[tile_of_elem])
+    g_excl = np.cumsum(gpad) - gpad
+    g_in_tile = g_excl - g_excl[(np.arange(G) // TILE) * TILE] if G else np.zeros(0, np.int64)
+    in_group = (np.cumsum(L, axis=1) - L).ravel()
+    start = tile_off[tile_of_elem] * 8 + np.repeat(g_in_tile, GROUP) + in_group
     total_bits = int(tile_off[-1]) * 8
     bitv = np.zeros(total_bits, dtype=np.uint8)
     cf = codes[sym] if N else np.zeros(0, np.int64)
@@ -271,7 +277,7 @@ def encode(bits) -> Compressed:
     return Compressed(
         R=R, C=C, palette=palette, lengths=lengths, codes=codes,
         sm=sm.astype(np.uint8), stream=stream.astype(np.uint8),
-        glen=glen.astype(np.uint16), tile_off=tile_off.astype(np.uint32),
+        glen=(gpad // GLEN_UNIT).astype(np.uint8), tile_off=tile_off.astype(np.uint32),
         tile_vbase=tile_vbase.astype(np.uint32), vexp=vexp.astype(np.uint8),
         bitmap=bitmap, nib=nib, hist=hist, freq=freq, vflag=vflag)
 
@@ -289,10 +295,13 @@ def encode_stream_bitstring(comp: Compressed, e: np.ndarray) -> list:
         for g in range(t * TILE, min((t + 1) * TILE, comp.G)):
             if comp.vflag[g]:
                 continue
+            gs = []
             for i in range(g * GROUP, (g + 1) * GROUP):
                 k = sym_of[int(e[i])]
                 L = int(comp.lengths[k])
-                s.append(format(int(comp.codes[k]), f"0{L}b"))
+                gs.append(format(int(comp.codes[k]), f"0{L}b"))
+            gbits = "".join(gs)
+            s.append(gbits + "0" * (-len(gbits) % GLEN_UNIT))
         bits = "".join(s)
         bits += "0" * (-len(bits) % 8)
         tiles.append(bits)
@@ -362,6 +371,7 @@ def decode_sequential(comp: Compressed, mode: str = "full"):
                         raise ValueError("invalid code in stream")
                 syms[base + i] = s
                 exps[base + i] = comp.palette[s]
+            pos += -pos % GLEN_UNIT          # the group's zero padding (tiles start byte aligned)
     return _assemble(comp, exps, syms, mode)
 
 
@@ -381,9 +391,9 @@ def decode_lut(lengths, codes):
 
 def group_start_bits(comp: Compressed) -> np.ndarray:
     """First stream bit of every group: its tile's byte offset times 8 plus the
-    coded lengths of the groups before it in the same tile."""
+    padded lengths of the groups before it in the same tile."""
     G = comp.G
-    gl = comp.glen.astype(np.int64)
+    gl = comp.glen.astype(np.int64) * GLEN_UNIT
     tile_of = np.arange(G) // TILE
     incl = np.cumsum(gl)
     tile_first = np.concatenate([[0], incl])[np.arange(0, G, TILE)] if G else np.zeros(0, np.int64)

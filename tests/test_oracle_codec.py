@@ -216,11 +216,20 @@ def test_histogram_matches_closed_form(which):
 def test_size_accounting_closed_form(small):
     w, c = small
     N, G, T, V = c.N, c.G, c.T, c.V
-    # stream bytes from the code side: sum over tiles of ceil(bits/8)
-    tile_bits = [int(c.glen[t * 64:(t + 1) * 64].astype(np.int64).sum()) for t in range(T)]
-    assert sum(tile_bits) == int((c.freq * c.lengths).sum())
+    # stream bytes from the code side: each coded group's code bits (its
+    # exponents' code lengths summed) rounded up to a multiple of 4, per tile
+    # rounded up to whole bytes
+    e = ((w.ravel() >> 7) & 0xFF).reshape(-1, 64)
+    sym_of = {int(E): s for s, E in enumerate(c.palette)}
+    vf = codec.group_flags(c)
+    gbits = np.array([0 if vf[g] else sum(int(c.lengths[sym_of[int(x)]]) for x in e[g]) for g in range(G)])
+    assert int(gbits.sum()) == int((c.freq * c.lengths).sum())
+    gpad = (gbits + 3) // 4 * 4
+    assert np.array_equal(c.glen.astype(np.int64) * 4, gpad)
+    tile_bits = [int(gpad[t * 64:(t + 1) * 64].sum()) for t in range(T)]
     stream_bytes = sum((b + 7) // 8 for b in tile_bits)
-    expect = (codec.HEADER_BYTES + N + stream_bytes + 2 * G + 64 * V + 8 * T + 2 * 4 * (T + 1))
+    # GLEN is one byte per group
+    expect = (codec.HEADER_BYTES + N + stream_bytes + G + 64 * V + 8 * T + 2 * 4 * (T + 1))
     assert codec.huffman_form_bytes(c) == expect
     assert codec.palette_form_bytes(c) == codec.HEADER_BYTES + N + N // 2 + 64 * V + 8 * T + 4 * (T + 1)
 
@@ -252,3 +261,27 @@ def test_compression_ratio_near_page_figure(small):
     w, c = small
     saved = 1 - codec.huffman_form_bytes(c) / (2 * w.size)
     assert 0.25 < saved < 0.36
+
+
+def test_group_of_longest_codes_fills_the_length_byte():
+    """Frequencies 32 * Fibonacci force a code 15 deep; a group made only of
+    the two 15-bit codewords is 64 * 15 = 960 bits, already a multiple of 4,
+    the largest group length: 240 in the one-byte GLEN.  It round-trips."""
+    fib = [1, 1]
+    while len(fib) < 16:
+        fib.append(fib[-1] + fib[-2])
+    counts = [32 * f for f in fib]                   # symbol k gets exponent 100 + k
+    exps = np.repeat(np.arange(100, 116), counts)
+    # the two rarest classes (32 each) first: one group of longest codes
+    order = np.concatenate([np.nonzero(exps < 102)[0], np.nonzero(exps >= 102)[0]])
+    exps = exps[order]
+    pad = (-exps.size) % 64
+    exps = np.concatenate([exps, np.full(pad, 115)])
+    w = ((exps.astype(np.uint16) << 7) | (np.arange(exps.size) % 128).astype(np.uint16)).reshape(1, -1)
+    c = codec.encode(w)
+    assert int(c.lengths.max()) == 15
+    rare = [s for s, E in enumerate(c.palette) if E in (100, 101)]
+    assert all(int(c.lengths[s]) == 15 for s in rare)
+    assert int(c.glen[0]) == 240 and int(c.glen.max()) == 240
+    assert np.array_equal(codec.decode_parallel(c, "full"), w)
+    assert np.array_equal(codec.decode_sequential(c, "full"), w)

@@ -27,7 +27,7 @@ def examples(golden_dir):
     return _load(golden_dir)
 
 
-NAMES = ["three_symbols", "verbatim_group", "single_exponent"]
+NAMES = ["three_symbols", "verbatim_group", "single_exponent", "group_padding"]
 
 
 def _matrix(ex):
