@@ -70,9 +70,13 @@ int uw_abi_struct_sizes(uint64_t* info, uint64_t* dmat, uint64_t* opts);
  * verbatim groups.
  *   SM         uint8[N]    sign/mantissa byte, (sign << 7) | mantissa
  *   STREAM     uint8[S]    Huffman codes of the palette index of every element
- *                          of every non-verbatim group, MSB-first; tile t
- *                          starts at byte TILE_OFF[t]
- *   GLEN       uint16[G]   coded bits of each group (0 for verbatim groups)
+ *                          of every non-verbatim group, MSB-first, each
+ *                          group followed by zero bits up to a multiple of 4
+ *                          bits; tile t starts at byte TILE_OFF[t]
+ *   GLEN       uint8[G]    padded bits of each group / 4 (0 for verbatim
+ *                          groups; at most 64*15/4 = 240): a group starts
+ *                          4 * (sum of GLEN before it in its tile) bits after
+ *                          its tile's first byte
  *   TILE_OFF   uint32[T+1] stream byte offset of each tile; [T] = S
  *   TILE_VBASE uint32[T+1] verbatim groups before each tile; [T] = V
  *   VEXP       uint8[64*V] raw exponent bytes of the verbatim groups, in order
@@ -144,12 +148,13 @@ int uw_blob_info(const uw_blob* blob, uw_info* info);
  * until uw_blob_free; NULL with size 0 for an empty or absent section). */
 int uw_blob_section(const uw_blob* blob, int sec, const void** ptr, uint64_t* bytes);
 
-/* Serialize to a byte image: a 256-byte header then each stored section at a
- * 256-byte aligned offset.  With buf == NULL only *need is set.  UW_EINVAL if
- * cap < *need. */
+/* Serialize to a byte image: a 256-byte header (magic "UWF2", format version
+ * 2) then each stored section at a 256-byte aligned offset.  With buf == NULL
+ * only *need is set.  UW_EINVAL if cap < *need. */
 int uw_blob_serialize(const uw_blob* blob, void* buf /*host*/, uint64_t cap, uint64_t* need);
 
-/* Parse a serialized image into a new blob and validate it (UW_EFORMAT). */
+/* Parse a serialized image into a new blob and validate it (UW_EFORMAT,
+ * also for version-1 images, whose group lengths were 16-bit). */
 int uw_blob_deserialize(const void* buf /*host*/, uint64_t bytes, uw_blob** out);
 
 /* Build the NIB section of a blob that lacks it (host transcode). */
@@ -179,7 +184,7 @@ typedef struct {
     uint8_t palette[16];
     const uint8_t* sm;
     const uint8_t* stream;
-    const uint16_t* glen;
+    const uint8_t* glen;
     const uint32_t* tile_off;
     const uint32_t* tile_vbase;
     const uint8_t* vexp;

@@ -31,7 +31,7 @@ KERNELS = {"auto": UW_KERNEL_AUTO, "gemv": UW_KERNEL_GEMV, "mfma": UW_KERNEL_MFM
 # sections each use reads on the device
 DECODE_SECTIONS = ("sm", "stream", "glen", "tile_off", "tile_vbase", "vexp", "bitmap", "dlut", "mlut")
 DIRECT_SECTIONS = ("sm", "nib", "vexp", "bitmap", "tile_vbase")
-SECTION_DTYPES = {"sm": np.uint8, "stream": np.uint8, "glen": np.uint16, "tile_off": np.uint32,
+SECTION_DTYPES = {"sm": np.uint8, "stream": np.uint8, "glen": np.uint8, "tile_off": np.uint32,
                   "tile_vbase": np.uint32, "vexp": np.uint8, "bitmap": np.uint64, "nib": np.uint8,
                   "dlut": np.uint8, "mlut": np.uint32}
 

@@ -341,7 +341,7 @@ int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_S
     std::memcpy(d->palette, info->palette, 16);
     d->sm = static_cast<const uint8_t*>(dev[UW_SEC_SM]);
     d->stream = static_cast<const uint8_t*>(dev[UW_SEC_STREAM]);
-    d->glen = static_cast<const uint16_t*>(dev[UW_SEC_GLEN]);
+    d->glen = static_cast<const uint8_t*>(dev[UW_SEC_GLEN]);
     d->tile_off = static_cast<const uint32_t*>(dev[UW_SEC_TILE_OFF]);
     d->tile_vbase = static_cast<const uint32_t*>(dev[UW_SEC_TILE_VBASE]);
     d->vexp = static_cast<const uint8_t*>(dev[UW_SEC_VEXP]);

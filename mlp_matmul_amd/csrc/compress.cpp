@@ -170,7 +170,7 @@ void build_nibbles(uw_blob& b, const uint8_t* e, int threads) {
 
 extern "C" {
 
-int uw_version(void) { return (1 << 16) | 0; }
+int uw_version(void) { return (1 << 16) | 1; }
 
 int uw_compress(const uint16_t* w, int64_t rows, int64_t cols, const uw_opts* opts, uw_blob** out) {
     uw::clear_error();
@@ -269,7 +269,8 @@ int uw_compress(const uint16_t* w, int64_t rows, int64_t cols, const uw_opts* op
                     const uint8_t* eg = e.data() + g * kGroup;
                     uint32_t gl = 0;
                     for (int j = 0; j < kGroup; ++j) gl += b->lengths[idx_of[eg[j]]];
-                    b->glen[g] = uint16_t(gl);
+                    gl = (gl + 3u) & ~3u;                    // padded to a 4-bit boundary
+                    b->glen[g] = uint8_t(gl / 4u);           // <= 64 * 15 / 4 = 240
                     bits += gl;
                 }
                 tile_bits[t] = bits;
@@ -309,15 +310,25 @@ int uw_compress(const uint16_t* w, int64_t rows, int64_t cols, const uw_opts* op
                         ++vslot;
                         continue;
                     }
+                    uint32_t gbits = 0;
                     for (int j = 0; j < kGroup; ++j) {
                         int s = idx_of[eg[j]];
                         int L = b->lengths[s];
                         acc = (acc << L) | b->codes[s];
                         nacc += L;
+                        gbits += uint32_t(L);
                         while (nacc >= 8) {
                             o[pos++] = uint8_t(acc >> (nacc - 8));
                             nacc -= 8;
                         }
+                    }
+                    // zero bits up to the group's 4-bit boundary (groups start on one)
+                    const int padb = int((4u - (gbits & 3u)) & 3u);
+                    acc <<= padb;
+                    nacc += padb;
+                    while (nacc >= 8) {
+                        o[pos++] = uint8_t(acc >> (nacc - 8));
+                        nacc -= 8;
                     }
                 }
                 if (nacc > 0) o[pos++] = uint8_t(acc << (8 - nacc));
@@ -359,6 +370,7 @@ int uw_blob_add_palette(uw_blob* b) {
                     e[g * kGroup + j] = b->palette[ent >> 4];
                     bitpos += ent & 15;
                 }
+                bitpos = (bitpos + 3) & ~uint64_t(3);   // the group's zero padding
             }
         }
         uw::build_nibbles(*b, e.data(), 0);
@@ -388,7 +400,7 @@ int uw_blob_info(const uw_blob* b, uw_info* info) {
     uint64_t* sb = info->section_bytes;
     sb[UW_SEC_SM] = b->sm.size();
     sb[UW_SEC_STREAM] = b->stream.size();
-    sb[UW_SEC_GLEN] = b->glen.size() * 2;
+    sb[UW_SEC_GLEN] = b->glen.size();
     sb[UW_SEC_TILE_OFF] = b->tile_off.size() * 4;
     sb[UW_SEC_TILE_VBASE] = b->tile_vbase.size() * 4;
     sb[UW_SEC_VEXP] = b->vexp.size();
@@ -416,7 +428,7 @@ int uw_blob_section(const uw_blob* b, int sec, const void** ptr, uint64_t* bytes
     switch (sec) {
         case UW_SEC_SM: p = b->sm.data(); n = b->sm.size(); break;
         case UW_SEC_STREAM: p = b->stream.data(); n = b->stream.size(); break;
-        case UW_SEC_GLEN: p = b->glen.data(); n = b->glen.size() * 2; break;
+        case UW_SEC_GLEN: p = b->glen.data(); n = b->glen.size(); break;
         case UW_SEC_TILE_OFF: p = b->tile_off.data(); n = b->tile_off.size() * 4; break;
         case UW_SEC_TILE_VBASE: p = b->tile_vbase.data(); n = b->tile_vbase.size() * 4; break;
         case UW_SEC_VEXP: p = b->vexp.data(); n = b->vexp.size(); break;
@@ -435,7 +447,7 @@ int uw_blob_section(const uw_blob* b, int sec, const void** ptr, uint64_t* bytes
 
 // ----------------------------------------------------------------- serialize
 // Header (little-endian, 256 bytes):
-//   0 "UWF1"  4 u32 version(1)  8 i64 rows  16 i64 cols  24 i64 V
+//   0 "UWF2"  4 u32 version(2)  8 i64 rows  16 i64 cols  24 i64 V
 //   32 u32 P  36 u32 lmax  40 u8 palette[16]  56 u8 lengths[16]
 //   72 u64 bytes of sections SM..NIB [8]  136 u32 flags (bit 0: NIB stored)
 // Sections follow in enum order, each at a 256-byte aligned offset.
@@ -460,8 +472,8 @@ int uw_blob_serialize(const uw_blob* b, void* buf, uint64_t cap, uint64_t* need)
     if (cap < total) return uw::fail(UW_EINVAL, "uw_blob_serialize: buffer too small");
     uint8_t* o = static_cast<uint8_t*>(buf);
     std::memset(o, 0, size_t(total));
-    std::memcpy(o, "UWF1", 4);
-    uint32_t ver = 1, P = uint32_t(b->P), L = uint32_t(b->lmax), flags = b->has_nib ? 1u : 0u;
+    std::memcpy(o, "UWF2", 4);
+    uint32_t ver = 2, P = uint32_t(b->P), L = uint32_t(b->lmax), flags = b->has_nib ? 1u : 0u;
     std::memcpy(o + 4, &ver, 4);
     std::memcpy(o + 8, &b->rows, 8);
     std::memcpy(o + 16, &b->cols, 8);
@@ -486,8 +498,11 @@ int uw_blob_deserialize(const void* buf, uint64_t bytes, uw_blob** out) {
     if (!buf || !out) return uw::fail(UW_EINVAL, "uw_blob_deserialize: NULL argument");
     *out = nullptr;
     const uint8_t* in = static_cast<const uint8_t*>(buf);
-    if (bytes < uw::kHeaderBytes || std::memcmp(in, "UWF1", 4) != 0)
-        return uw::fail(UW_EFORMAT, "uw_blob_deserialize: bad magic");
+    if (bytes < uw::kHeaderBytes || std::memcmp(in, "UWF2", 4) != 0)
+        return uw::fail(UW_EFORMAT, std::memcmp(in, "UWF1", 4) == 0 && bytes >= 4
+                                        ? "uw_blob_deserialize: format version 1 (16-bit group lengths) is not read; "
+                                          "compress the weights again"
+                                        : "uw_blob_deserialize: bad magic");
     uint32_t ver, P, L, flags;
     uint64_t sizes[kStored];
     uw_blob* b = new (std::nothrow) uw_blob;
@@ -506,7 +521,7 @@ int uw_blob_deserialize(const void* buf, uint64_t bytes, uw_blob** out) {
         delete b;
         return uw::fail(UW_EFORMAT, m);
     };
-    if (ver != 1) return bad("uw_blob_deserialize: unknown version");
+    if (ver != 2) return bad("uw_blob_deserialize: unknown version");
     if (b->rows < 0 || b->cols < 0 || b->cols % kGroup) return bad("uw_blob_deserialize: bad shape");
     if (b->cols && b->rows > (int64_t(1) << 40) / b->cols) return bad("uw_blob_deserialize: bad shape");
     if (P > 16 || L > uint32_t(uw::kMaxCodeLen)) return bad("uw_blob_deserialize: bad palette/lmax");
@@ -528,8 +543,7 @@ int uw_blob_deserialize(const void* buf, uint64_t bytes, uw_blob** out) {
                 case UW_SEC_SM: b->sm.assign(p, p + n); break;
                 case UW_SEC_STREAM: b->stream.assign(p, p + n); break;
                 case UW_SEC_GLEN:
-                    if (!need_mult(2)) return bad("uw_blob_deserialize: GLEN size");
-                    b->glen.resize(n / 2);
+                    b->glen.resize(n);
                     if (n) std::memcpy(b->glen.data(), p, n);
                     break;
                 case UW_SEC_TILE_OFF:
@@ -618,7 +632,7 @@ int uw_validate(const uw_blob* b) {
         uint64_t bits = 0;
         for (int64_t g = g0; g < g1; ++g) {
             bool verb = (b->bitmap[t] >> (g - g0)) & 1;
-            uint32_t gl = b->glen[g];
+            const uint32_t gl = 4u * b->glen[g];     // padded bits
             if (verb) {
                 if (gl) return bad("verbatim group with coded bits");
                 continue;

@@ -141,8 +141,12 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
         const uint64_t word = a.bitmap[t];
         const int64_t g = t * 64 + lane;
         const bool gvalid = g < a.G;
-        const uint32_t gl0 = a.glen[gvalid ? g : 0];   // unconditional: no wait inside a branch
-        const uint32_t gl = gvalid ? gl0 : 0u;
+        // padded bits of the lane's group (the next group starts there); the
+        // load is unconditional and its use too (lanes past the last group
+        // read the tile's first byte and mask it), so the compiler cannot
+        // move the load, and the wait for it, into a branch
+        const uint32_t gl0 = (a.glen + t * 64)[gvalid ? uint32_t(lane) : 0u];
+        const uint32_t gl = (4u * gl0) & (0u - uint32_t(gvalid));
         const bool verb = (word >> lane) & 1ull;
         // output phase: lane handles elements 512k + 8*lane .. +7 of the tile
         const int64_t e0 = t * 4096 + 8 * lane;

@@ -13,7 +13,7 @@ enum WeightSource { SRC_BF16 = 0, SRC_EXP = 1, SRC_PAL = 2 };
 struct DecodeArgs {
     const uint8_t* sm;
     const uint8_t* stream;
-    const uint16_t* glen;
+    const uint8_t* glen;        // padded coded bits of each group / 4
     const uint32_t* tile_off;
     const uint32_t* tile_vbase;
     const uint8_t* vexp;

@@ -32,7 +32,7 @@ struct uw_blob {
     bool has_nib = false;
     std::vector<uint8_t> sm, stream, vexp, nib, dlut;
     std::vector<uint32_t> mlut;
-    std::vector<uint16_t> glen;
+    std::vector<uint8_t> glen;     // padded coded bits of each group / 4
     std::vector<uint32_t> tile_off, tile_vbase;
     std::vector<uint64_t> bitmap;
 };

@@ -165,7 +165,7 @@ def test_serialize_roundtrip_and_add_palette():
     b = uw.compress(w, emit_palette=False)
     assert b.section("nib").size == 0
     data = b.serialize()
-    assert data[:4] == b"UWF1" and len(data) % 256 == 0
+    assert data[:4] == b"UWF2" and len(data) % 256 == 0
     b2 = uw.Blob.deserialize(data)
     for name in SEC:
         assert np.array_equal(b.section(name), b2.section(name)), name
@@ -268,3 +268,15 @@ def test_long_codewords_fill_the_top_of_the_decode_table(lengths):
     lo = int(v[long_first].min())
     assert lo >= (1 << L) - 64
     assert long_first[lo:].all()                                 # one run up to the top
+
+
+def test_version_one_images_are_rejected():
+    """Format version 2 pads coded groups to 4 bits and stores one-byte group
+    lengths; an image of the 16-bit-length version 1 is refused, not misread."""
+    w, _ = workloads.small_matrix()
+    data = bytearray(uw.compress(w).serialize())
+    assert data[:4] == b"UWF2"
+    data[:4] = b"UWF1"
+    with pytest.raises(uw.UnweightError, match="version 1") as ei:
+        uw.Blob.deserialize(bytes(data))
+    assert ei.value.code == -3          # UW_EFORMAT
