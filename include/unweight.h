@@ -290,10 +290,20 @@ enum {
     UW_PIPE_EXP = 2,      /* exponent decode -> u8 scratch -> recon matmul */
     UW_PIPE_PAL = 3,      /* palette transcode -> nibble scratch -> recon matmul */
     UW_PIPE_DIRECT = 4,   /* recon matmul on the resident NIB section */
-    UW_PIPE_BF16 = 5      /* uncompressed weights (baseline; not for uw_matmul) */
+    UW_PIPE_BF16 = 5,     /* uncompressed weights (baseline; not for uw_matmul) */
+    UW_PIPE_HUFF = 6      /* Huffman decode inside a batch-1 matmul: the Huffman
+                             form (the decoder's sections) read once, no decoded
+                             plane; batch 1 and cols >= 4096 only (else
+                             UW_EUNSUPPORTED); kernel and split_k are ignored;
+                             scratch: 8 * ceil(rows*cols/4096) bytes of per-tile
+                             partial sums, added per row in tile order (the
+                             result is deterministic).  Goes past the page's four
+                             pipelines ("Four ways to use compressed weights"):
+                             its decode and matmul fused in one pass. */
 };
 
-/* Scratch bytes uw_matmul needs for (pipeline, shape, batch, split_k);
+/* Scratch bytes uw_matmul needs for (pipeline, shape, batch, split_k)
+ * (UW_PIPE_HUFF: the per-tile partial sums, whatever split_k);
  * split_k 0: for the split the library would choose with UW_KERNEL_AUTO on
  * the current device.  Returns the size (>= 0) or a negative error code. */
 int64_t uw_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch, int split_k);

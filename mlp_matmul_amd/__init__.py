@@ -17,7 +17,7 @@ import numpy as np
 
 from ._capi import (  # noqa: F401
     SECTION_NAMES, UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY, UW_NUM_SECTIONS,
-    UW_PIPE_AUTO, UW_PIPE_BF16, UW_PIPE_DIRECT, UW_PIPE_EXP, UW_PIPE_FULL, UW_PIPE_PAL,
+    UW_PIPE_AUTO, UW_PIPE_BF16, UW_PIPE_DIRECT, UW_PIPE_EXP, UW_PIPE_FULL, UW_PIPE_HUFF, UW_PIPE_PAL,
     UW_SEC_BITMAP, UW_SEC_DLUT, UW_SEC_GLEN, UW_SEC_MLUT, UW_SEC_NIB, UW_SEC_SM, UW_SEC_STREAM,
     UW_SEC_TILE_OFF, UW_SEC_TILE_VBASE, UW_SEC_VEXP, UW_EUNSUPPORTED, UW_EINVAL, UW_STATIC_SCRATCH_BYTES,
     UnweightError, check, lib,

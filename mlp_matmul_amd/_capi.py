@@ -20,7 +20,7 @@ UW_EUNSUPPORTED = -5
 SECTION_NAMES = ("sm", "stream", "glen", "tile_off", "tile_vbase", "vexp", "bitmap", "nib", "dlut", "mlut")
 
 UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY = 0, 1, 2, 3
-UW_PIPE_AUTO, UW_PIPE_FULL, UW_PIPE_EXP, UW_PIPE_PAL, UW_PIPE_DIRECT, UW_PIPE_BF16 = range(6)
+UW_PIPE_AUTO, UW_PIPE_FULL, UW_PIPE_EXP, UW_PIPE_PAL, UW_PIPE_DIRECT, UW_PIPE_BF16, UW_PIPE_HUFF = range(7)
 UW_STATIC_SCRATCH_BYTES = 64 << 20
 
 

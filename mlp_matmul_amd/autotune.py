@@ -21,11 +21,12 @@ import ctypes as ct
 import json
 
 
-from . import (UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY, UW_PIPE_DIRECT, UW_PIPE_EXP, UW_PIPE_FULL, UW_PIPE_PAL,
-               check, decode_full, lib, plan_set, scratch_bytes)
+from . import (UW_KERNEL_AUTO, UW_KERNEL_GEMV, UW_KERNEL_MFMA, UW_KERNEL_SKINNY, UW_PIPE_DIRECT, UW_PIPE_EXP, UW_PIPE_FULL,
+               UW_PIPE_HUFF, UW_PIPE_PAL, check, decode_full, lib, plan_set, scratch_bytes)
 
-PIPE_NAMES = {UW_PIPE_FULL: "full", UW_PIPE_EXP: "exp", UW_PIPE_PAL: "pal", UW_PIPE_DIRECT: "direct"}
-KERNEL_NAMES = {UW_KERNEL_GEMV: "gemv", UW_KERNEL_MFMA: "mfma", UW_KERNEL_SKINNY: "skinny"}
+PIPE_NAMES = {UW_PIPE_FULL: "full", UW_PIPE_EXP: "exp", UW_PIPE_PAL: "pal", UW_PIPE_DIRECT: "direct",
+              UW_PIPE_HUFF: "huff"}
+KERNEL_NAMES = {UW_KERNEL_AUTO: "decoder", UW_KERNEL_GEMV: "gemv", UW_KERNEL_MFMA: "mfma", UW_KERNEL_SKINNY: "skinny"}
 # a candidate's outputs must stay within this many times sum_c |W[r,c] X[b,c]|
 # of the exact product (fp32 accumulation over up to 14336 terms stays well
 # inside it)
@@ -41,6 +42,8 @@ def candidates(rows, cols, batch, has_palette=True):
     """(pipeline, kernel, split_k) triples worth timing for one shape/batch."""
     pipes = [UW_PIPE_FULL, UW_PIPE_EXP, UW_PIPE_PAL] + ([UW_PIPE_DIRECT] if has_palette else [])
     out = []
+    if batch == 1 and cols >= 4096:
+        out.append((UW_PIPE_HUFF, UW_KERNEL_AUTO, 1))      # decode inside the matmul (one kernel family)
     for p in pipes:
         if batch <= 16:
             out.append((p, UW_KERNEL_GEMV, 1))

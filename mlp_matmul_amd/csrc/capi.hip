@@ -197,6 +197,12 @@ uwk::MatArgs compressed_args(const uw_dmat* d, const void* w, const uint16_t* X,
     return a;
 }
 
+// per-tile partial sums of the Huffman-decode GEMV: two floats per tile
+uint64_t huff_partial_bytes(int64_t rows, int64_t cols) {
+    const uint64_t n = uint64_t(rows) * uint64_t(cols);
+    return 8 * ((n + 4095) / 4096);
+}
+
 uint64_t decoded_bytes(int pipeline, int64_t rows, int64_t cols) {
     const uint64_t n = uint64_t(rows) * uint64_t(cols);
     switch (pipeline) {
@@ -205,6 +211,27 @@ uint64_t decoded_bytes(int pipeline, int64_t rows, int64_t cols) {
         case UW_PIPE_PAL: return n / 2;
         default: return 0;
     }
+}
+
+// UW_PIPE_HUFF: the decoder's GEMV mode (batch 1, cols >= 4096).
+int huff_gemv(const uw_dmat* d, const uint16_t* X, int64_t batch, float* Y, void* scratch, uint64_t scratch_bytes,
+              void* stream) {
+    const char* who = "uw_matmul(UW_PIPE_HUFF)";
+    if (batch < 0) return uw::fail(UW_EINVAL, std::string(who) + ": negative batch");
+    if (d->rows == 0 || batch == 0) return UW_OK;
+    if (batch != 1 || d->cols < 4096 || d->cols >= (int64_t(1) << 31))
+        return uw::fail(UW_EUNSUPPORTED, std::string(who) + ": needs batch 1 and 4096 <= cols < 2^31");
+    int rc = check_decoder_inputs(d, who, true);
+    if (rc) return rc;
+    if (!X || !Y || !aligned16(X) || !aligned16(Y))
+        return uw::fail(UW_EINVAL, std::string(who) + ": NULL or misaligned X or Y");
+    if (!scratch || !aligned16(scratch) || scratch_bytes < huff_partial_bytes(d->rows, d->cols))
+        return uw::fail(UW_EINVAL, std::string(who) + ": scratch smaller than uw_scratch_bytes()");
+    uwk::DecodeArgs a = decode_args(d, scratch);
+    a.x = X;
+    a.C = d->cols;
+    hipError_t e = uwk::launch_decode_gemv(a, d->rows, Y, as_stream(stream));
+    return e == hipSuccess ? UW_OK : hip_fail(e, who);
 }
 
 }  // namespace
@@ -400,8 +427,9 @@ int uw_gemm_recon_pal(const uw_dmat* d, const uint8_t* nib, const uint16_t* X, i
 
 int64_t uw_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch, int split_k) {
     uw::clear_error();
-    if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_BF16 || rows < 0 || cols < 0 || batch < 0 || split_k < 0)
+    if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_HUFF || rows < 0 || cols < 0 || batch < 0 || split_k < 0)
         return uw::fail(UW_EINVAL, "uw_scratch_bytes: bad argument");
+    if (pipeline == UW_PIPE_HUFF) return int64_t(align256(huff_partial_bytes(rows, cols)));
     if (split_k == 0) {
         // what split_k 0 resolves to with the kernel UW_KERNEL_AUTO picks
         uwk::MatArgs a{};
@@ -433,8 +461,9 @@ int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k, const uin
         }
         uw::clear_error();
     }
+    if (pipeline == UW_PIPE_HUFF) return huff_gemv(d, X, batch, Y, scratch, scratch_bytes, stream);
     if (pipeline < UW_PIPE_FULL || pipeline > UW_PIPE_DIRECT)
-        return uw::fail(UW_EINVAL, "uw_matmul: pipeline must be UW_PIPE_AUTO or FULL/EXP/PAL/DIRECT");
+        return uw::fail(UW_EINVAL, "uw_matmul: pipeline must be UW_PIPE_AUTO or FULL/EXP/PAL/DIRECT/HUFF");
     if (pipeline == UW_PIPE_DIRECT && d->groups && !d->nib)
         return uw::fail(UW_EINVAL, "uw_matmul: direct palette needs the NIB section on the device");
     // split_k 0 shrinks to what the scratch holds: only the decoded plane is required

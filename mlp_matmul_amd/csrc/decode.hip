@@ -1,5 +1,5 @@
 // Tile-parallel Huffman decoder for gfx950: full bf16, exponent-only and
-// palette-transcode outputs.
+// palette-transcode outputs, and the decode inside a batch-1 matmul.
 //
 // Method: Cloudflare, "Unweight: how we compressed an LLM 22% without
 // sacrificing quality", section "Four ways to use compressed weights": the
@@ -29,6 +29,16 @@
 // measured faster: the lookup loop already keeps LDS busy).  The stream buffer is sized by the
 // matrix's longest tile, which keeps LDS per wave small enough for several
 // workgroups per CU.
+//
+// The fourth mode decodes inside a batch-1 matmul (Huffman stream straight
+// from HBM, no decoded plane written): the output phase's element walk
+// rebuilds each lane's 8 weights in registers, multiplies them with the
+// matching activations (v_dot2, fp32) and keeps two sums per lane, for the
+// first and the second row the tile touches (a tile is 4096 elements, so at
+// most two rows when rows have at least 4096 columns); two wave sums give
+// the tile's partials, which a second kernel adds up per row in tile order
+// (deterministic).  This goes past the page's four pipelines: decode and
+// matmul in one pass, reading the Huffman form (the smallest) once.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -108,7 +118,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
 
     for (int i = tid; i < kMlutEntries / 4; i += 64 * kDecWaves)
         reinterpret_cast<u32x4_t*>(mlut)[i] = reinterpret_cast<const u32x4_t*>(a.mlut)[i];
-    if (MODE == MODE_FULL && tid < 256) {
+    if ((MODE == MODE_FULL || MODE == MODE_GEMV) && tid < 256) {
         // nibble pair -> two exponents in bf16 position
         uint32_t lo = pal_byte(a, tid & 15), hi = pal_byte(a, tid >> 4);
         ptab[tid] = (lo << 7) | (hi << 23);
@@ -158,10 +168,10 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
         uint32_t ve0 = 0, ve1 = 0, vs0 = 0, vs1 = 0;
         if (MODE != MODE_PAL && word && t * 64 + vg0 < a.G) {
             ve0 = a.vexp[uint64_t(vbase) * 64 + lane];
-            if (MODE == MODE_FULL) vs0 = a.sm[(t * 64 + vg0) * 64 + lane];
+            if (MODE == MODE_FULL || MODE == MODE_GEMV) vs0 = a.sm[(t * 64 + vg0) * 64 + lane];
             if (w1 && t * 64 + vg1 < a.G) {
                 ve1 = a.vexp[uint64_t(vbase + 1) * 64 + lane];
-                if (MODE == MODE_FULL) vs1 = a.sm[(t * 64 + vg1) * 64 + lane];
+                if (MODE == MODE_FULL || MODE == MODE_GEMV) vs1 = a.sm[(t * 64 + vg1) * 64 + lane];
             }
         }
 
@@ -203,7 +213,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
         // FULL: the sign/mantissa bytes of the lane's output elements go out
         // now and arrive during the lookups
         u32x2_t smv[8];
-        if (MODE == MODE_FULL) {
+        if (MODE == MODE_FULL || MODE == MODE_GEMV) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int64_t e = e0 + 512 * k;
@@ -266,6 +276,15 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
             }
         } else {
             wave_lds_sync();     // slots are read across lanes
+            // GEMV: the tile's elements before `rsplit` lie in its first row
+            // (starting at column c_first), the rest in the next row
+            float acc0 = 0.f, acc1 = 0.f;
+            uint32_t rsplit = 0, c_first = 0;      // cols < 2^31; tile-relative positions < 4096
+            if (MODE == MODE_GEMV) {
+                const int64_t cf = (t * 4096) % a.C;
+                c_first = uint32_t(cf);
+                rsplit = uint32_t(a.C - cf < 4096 ? a.C - cf : 4096);
+            }
             // non-verbatim groups: 8 elements per lane, 512 per instruction
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -284,9 +303,22 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) pr[i] = lds_ld(ptab_a + ((nw32 >> (8 * i)) & 0xFFu) * 4);
                     const u32x2_t s8 = smv[k];
-                    store16(static_cast<uint16_t*>(a.out) + e,
-                            u32x4_t{join_pair<0>(s8[0], pr[0]), join_pair<1>(s8[0], pr[1]),
-                                    join_pair<0>(s8[1], pr[2]), join_pair<1>(s8[1], pr[3])});
+                    const u32x4_t w = u32x4_t{join_pair<0>(s8[0], pr[0]), join_pair<1>(s8[0], pr[1]),
+                                              join_pair<0>(s8[1], pr[2]), join_pair<1>(s8[1], pr[3])};
+                    if (MODE == MODE_GEMV) {
+                        // the lane's 8 weights lie in one row (rows are whole groups)
+                        const uint32_t et = 8u * uint32_t(lane) + 512u * k;      // e - t * 4096
+                        const bool second = et >= rsplit;
+                        const u32x4_t xv = load16(a.x + (second ? et - rsplit : c_first + et));
+                        float s = dot2_bf16(w[0], xv[0], 0.f);
+                        s = dot2_bf16(w[1], xv[1], s);
+                        s = dot2_bf16(w[2], xv[2], s);
+                        s = dot2_bf16(w[3], xv[3], s);
+                        if (second) acc1 += s;
+                        else acc0 += s;
+                    } else {
+                        store16(static_cast<uint16_t*>(a.out) + e, w);
+                    }
                 }
             }
             // verbatim groups: the whole wave writes one group, lane = element
@@ -304,13 +336,46 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
                     sv = vs1;
                 } else {
                     ev = a.vexp[uint64_t(vbase + r) * 64 + lane];
-                    if (MODE == MODE_FULL) sv = a.sm[e];
+                    if (MODE == MODE_FULL || MODE == MODE_GEMV) sv = a.sm[e];
                 }
-                if (MODE == MODE_EXP) static_cast<uint8_t*>(a.out)[e] = uint8_t(ev);
-                else static_cast<uint16_t*>(a.out)[e] = uint16_t(((sv & 0x80u) << 8) | (ev << 7) | (sv & 0x7Fu));
+                const uint32_t wb = ((sv & 0x80u) << 8) | (ev << 7) | (sv & 0x7Fu);
+                if (MODE == MODE_GEMV) {
+                    // bf16 x bf16 is exact in fp32
+                    const uint32_t et = gi * 64u + uint32_t(lane);           // e - t * 4096
+                    const bool second = et >= rsplit;
+                    const float xe = __uint_as_float(uint32_t(a.x[second ? et - rsplit : c_first + et]) << 16);
+                    const float p = __uint_as_float(wb << 16) * xe;
+                    if (second) acc1 += p;
+                    else acc0 += p;
+                } else if (MODE == MODE_EXP) {
+                    static_cast<uint8_t*>(a.out)[e] = uint8_t(ev);
+                } else {
+                    static_cast<uint16_t*>(a.out)[e] = uint16_t(wb);
+                }
+            }
+            if (MODE == MODE_GEMV) {
+                acc0 = wave_sum(acc0);
+                acc1 = wave_sum(acc1);
+                if (lane == 0) {
+                    float* part = static_cast<float*>(a.out);
+                    part[2 * t] = acc0;
+                    part[2 * t + 1] = acc1;
+                }
             }
         }
     }
+}
+
+// y[r] = sum of the partials of row r over the tiles it spans, in tile order
+// (tile t's partial 0 belongs to its first row, partial 1 to the next).
+__global__ __launch_bounds__(256) void gemv_rows_reduce(const float* __restrict__ part, int64_t R, int64_t C,
+                                                        float* __restrict__ y) {
+    const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (r >= R) return;
+    const int64_t t0 = (r * C) / 4096, t1 = ((r + 1) * C - 1) / 4096;
+    float s = 0.f;
+    for (int64_t t = t0; t <= t1; ++t) s += part[2 * t + ((t * 4096) / C == r ? 0 : 1)];
+    y[r] = s;
 }
 
 }  // namespace
@@ -339,8 +404,17 @@ hipError_t launch_decode(int mode, const DecodeArgs& a0, hipStream_t s) {
     switch (mode) {
         case MODE_FULL: decode_kernel<MODE_FULL><<<grid, block, lds, s>>>(a); break;
         case MODE_EXP: decode_kernel<MODE_EXP><<<grid, block, lds, s>>>(a); break;
+        case MODE_GEMV: launch_timed(decode_kernel<MODE_GEMV>, dim3(grid), block, lds, s, a); break;
         default: decode_kernel<MODE_PAL><<<grid, block, lds, s>>>(a); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_gemv(const DecodeArgs& a, int64_t rows, float* y, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    hipError_t e = launch_decode(MODE_GEMV, a, s);
+    if (e != hipSuccess) return e;
+    gemv_rows_reduce<<<unsigned((rows + 255) / 256), 256, 0, s>>>(static_cast<const float*>(a.out), rows, a.C, y);
     return hipGetLastError();
 }
 

@@ -7,7 +7,9 @@
 
 namespace uwk {
 
-enum DecodeMode { MODE_FULL = 0, MODE_EXP = 1, MODE_PAL = 2 };
+// MODE_GEMV: Huffman decode inside a batch-1 matmul (no decoded output;
+// per-tile partial sums of the rows the tile covers, cols >= 4096)
+enum DecodeMode { MODE_FULL = 0, MODE_EXP = 1, MODE_PAL = 2, MODE_GEMV = 3 };
 enum WeightSource { SRC_BF16 = 0, SRC_EXP = 1, SRC_PAL = 2 };
 
 struct DecodeArgs {
@@ -26,7 +28,9 @@ struct DecodeArgs {
     int32_t lmax;
     int32_t buf_words;   // LDS dwords per wave for one staged tile stream
     uint32_t pal[4];     // palette bytes, index s in byte s%4 of pal[s/4]
-    void* out;
+    void* out;           // FULL/EXP/PAL: decoded plane; GEMV: partial sums float[2T]
+    const uint16_t* x;   // GEMV: bf16 activation [C]
+    int64_t C;           // GEMV: columns of the matrix
 };
 
 // Weights of one matmul and where they come from.
@@ -47,6 +51,9 @@ struct MatArgs {
 };
 
 hipError_t launch_decode(int mode, const DecodeArgs& a, hipStream_t s);
+// Huffman decode inside a batch-1 matmul: a.out = partial sums float[2T],
+// a.x the activation, a.C >= 4096; then y[r] summed per row in tile order.
+hipError_t launch_decode_gemv(const DecodeArgs& a, int64_t rows, float* y, hipStream_t s);
 hipError_t launch_gemv(int src, const MatArgs& a, hipStream_t s);
 // Fused gate/up GEMV with the SiLU product (palette sources, batch 1..4).
 bool gemv_gateup_supported(const MatArgs& gate, const MatArgs& up);

@@ -14,8 +14,11 @@ import workloads
 def test_candidate_space():
     c = autotune.candidates(14336, 4096, 1)
     pipes = {p for p, _, _ in c}
-    assert pipes == {uw.UW_PIPE_FULL, uw.UW_PIPE_EXP, uw.UW_PIPE_PAL, uw.UW_PIPE_DIRECT}
+    assert pipes == {uw.UW_PIPE_FULL, uw.UW_PIPE_EXP, uw.UW_PIPE_PAL, uw.UW_PIPE_DIRECT, uw.UW_PIPE_HUFF}
     assert any(k == uw.UW_KERNEL_GEMV for _, k, _ in c)
+    # the Huffman decode inside the matmul: batch 1 and at least 4096 columns
+    assert uw.UW_PIPE_HUFF not in {p for p, _, _ in autotune.candidates(14336, 4096, 2)}
+    assert uw.UW_PIPE_HUFF not in {p for p, _, _ in autotune.candidates(512, 1024, 1)}
     # no GEMV beyond batch 16, split-K only offered to short matrices
     assert {k for _, k, _ in autotune.candidates(14336, 4096, 64)} == {uw.UW_KERNEL_MFMA, uw.UW_KERNEL_SKINNY}
     # the skinny kernel needs whole 128-column steps and at most 32768 columns
