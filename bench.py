@@ -53,8 +53,9 @@ def parse(argv=None):
     p.add_argument("--min-warmup-ms", type=float, default=200.0,
                    help="warm up for at least this long, whatever --warmup says (clocks ramp after host phases)")
     p.add_argument("--batch", type=int, default=1)
-    p.add_argument("--pipeline", default="auto", choices=["auto", "direct", "pal", "exp", "full"],
-                   help="auto: the autotuner's plan per shape at this batch")
+    p.add_argument("--pipeline", default="auto", choices=["auto", "direct", "pal", "exp", "full", "huff"],
+                   help="auto: the autotuner's plan per shape at this batch; huff: Huffman decode inside the "
+                        "matmul (batch 1)")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--gen-threads", type=int, default=0, help="host threads generating the stack (0: up to 16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -99,6 +100,17 @@ def gate_up_bytes(info_g, info_u, batch):
 
 def bf16_bytes(R, C, batch):
     return int(2 * R * C + 2 * batch * C + 4 * batch * R)
+
+
+def huffman_bytes(info, batch):
+    """Algorithmic bytes of the Huffman-decode matmul: the Huffman form's
+    sections (sign/mantissa, stream, group lengths, tile tables, verbatim
+    exponents, bitmap) + activations in + outputs."""
+    import mlp_matmul_amd as uw
+    sb = info.section_bytes
+    w = sum(int(sb[k]) for k in (uw.UW_SEC_SM, uw.UW_SEC_STREAM, uw.UW_SEC_GLEN, uw.UW_SEC_TILE_OFF,
+                                 uw.UW_SEC_TILE_VBASE, uw.UW_SEC_VEXP, uw.UW_SEC_BITMAP))
+    return int(w + 2 * batch * info.cols + 4 * batch * info.rows)
 
 
 # ------------------------------------------------------------------ the stack
@@ -190,7 +202,8 @@ class Step:
         import mlp_matmul_amd as uw
         self.layers, self.B = layers, batch
         pipe = {"direct": uw.UW_PIPE_DIRECT, "pal": uw.UW_PIPE_PAL, "exp": uw.UW_PIPE_EXP,
-                "full": uw.UW_PIPE_FULL, "auto": uw.UW_PIPE_AUTO, "bf16": uw.UW_PIPE_BF16}[pipeline]
+                "full": uw.UW_PIPE_FULL, "auto": uw.UW_PIPE_AUTO, "bf16": uw.UW_PIPE_BF16,
+                "huff": uw.UW_PIPE_HUFF}[pipeline]
         lay0 = layers[0]
         F, H = (lay0.info[0].rows, lay0.info[0].cols) if lay0.info[0] is not None else lay0.bf16[0].shape
         self.X = [torch.from_numpy(_act(workload, i, batch, H)).view(torch.bfloat16).cuda()
@@ -241,7 +254,8 @@ class Step:
             else:
                 self.calls.append([row[0], row[1], silu, row[2]])
                 self.kinds.append(["gate", "up", "down"])
-                self.bytes.append([palette_bytes(lay.info[m], batch) for m in range(3)])
+                nbytes = huffman_bytes if pipe == uw.UW_PIPE_HUFF else palette_bytes
+                self.bytes.append([nbytes(lay.info[m], batch) for m in range(3)])
 
     @staticmethod
     def _scratch_need(uw, pipe, F, H, batch):
@@ -922,7 +936,9 @@ def main():
         traffic, prof_us = profile_figures(tag)
         roof = {"bound": "hbm", "achieved": round(d["GBps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(d["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": KIND_NAMES[dom] + (" (direct palette)" if a.pipeline in ("auto", "direct") else ""),
+                "kernel": KIND_NAMES[dom] + (" (direct palette)" if dom == "gate_up" else
+                                             {"auto": " (autotuned plan)", "direct": " (direct palette)",
+                                              "huff": " (Huffman decode in the matmul)"}.get(a.pipeline, "")),
                 "launches": d["launches"], "avg_launch_us": round(d["avg_us"], 3),
                 "bytes_per_launch": int(round(d["bytes"])), "profile_avg_us": prof_us,
                 "all_matmuls_frac": round(all_gbps / HBM_PEAK_GBPS, 4),

@@ -358,8 +358,12 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
                 acc1 = wave_sum(acc1);
                 if (lane == 0) {
                     float* part = static_cast<float*>(a.out);
-                    part[2 * t] = acc0;
-                    part[2 * t + 1] = acc1;
+                    if (a.C == 4096) {
+                        part[t] = acc0;          // tile t is row t: the output itself
+                    } else {
+                        part[2 * t] = acc0;
+                        part[2 * t + 1] = acc1;
+                    }
                 }
             }
         }
@@ -367,14 +371,27 @@ __global__ __launch_bounds__(64 * kDecWaves, 6) void decode_kernel(DecodeArgs a)
 }
 
 // y[r] = sum of the partials of row r over the tiles it spans, in tile order
-// (tile t's partial 0 belongs to its first row, partial 1 to the next).
+// (tile t's partial 0 belongs to its first row, partial 1 to the next: a
+// tile starting inside row r holds r's elements in partial 0, the one it
+// starts in before r holds them in partial 1).
 __global__ __launch_bounds__(256) void gemv_rows_reduce(const float* __restrict__ part, int64_t R, int64_t C,
                                                         float* __restrict__ y) {
     const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
     if (r >= R) return;
-    const int64_t t0 = (r * C) / 4096, t1 = ((r + 1) * C - 1) / 4096;
+    const int64_t first = r * C, t0 = first >> 12, t1 = (first + C - 1) >> 12;
     float s = 0.f;
-    for (int64_t t = t0; t <= t1; ++t) s += part[2 * t + ((t * 4096) / C == r ? 0 : 1)];
+    // eight loads issued together per round (no load waits for the previous
+    // one), then added in tile order
+    for (int64_t tb = t0; tb <= t1; tb += 8) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t t = tb + i;
+            v[i] = t <= t1 ? part[2 * t + ((t << 12) >= first ? 0 : 1)] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += v[i];
+    }
     y[r] = s;
 }
 
@@ -410,10 +427,12 @@ hipError_t launch_decode(int mode, const DecodeArgs& a0, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_decode_gemv(const DecodeArgs& a, int64_t rows, float* y, hipStream_t s) {
+hipError_t launch_decode_gemv(const DecodeArgs& a0, int64_t rows, float* y, hipStream_t s) {
     if (rows == 0) return hipSuccess;
+    DecodeArgs a = a0;
+    if (a.C == 4096) a.out = y;                 // one row per tile: written directly
     hipError_t e = launch_decode(MODE_GEMV, a, s);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.C == 4096) return e;
     gemv_rows_reduce<<<unsigned((rows + 255) / 256), 256, 0, s>>>(static_cast<const float*>(a.out), rows, a.C, y);
     return hipGetLastError();
 }

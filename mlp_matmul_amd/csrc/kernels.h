@@ -30,7 +30,7 @@ struct DecodeArgs {
     uint32_t pal[4];     // palette bytes, index s in byte s%4 of pal[s/4]
     void* out;           // FULL/EXP/PAL: decoded plane; GEMV: partial sums float[2T]
     const uint16_t* x;   // GEMV: bf16 activation [C]
-    int64_t C;           // GEMV: columns of the matrix
+    int64_t C;           // GEMV: columns of the matrix; 4096: a tile is one row and out is y itself
 };
 
 // Weights of one matmul and where they come from.
