@@ -35,6 +35,11 @@
  *     returned, launch failures surface as UW_EHIP.
  *   - Host blobs (uw_blob) are owned by the library and freed with
  *     uw_blob_free.
+ *   - The pages define the operations, not an API.  Calls that cite a passage
+ *     implement it; the rest are this library's own design decisions, marked
+ *     "(API)": error text, versioning, blob access and serialization, the
+ *     validator, scratch sizing, the device-matrix descriptor, the SiLU
+ *     helper, the kernel timer and the plan-file format.
  */
 #ifndef UNWEIGHT_H
 #define UNWEIGHT_H
@@ -54,13 +59,13 @@ extern "C" {
 #define UW_EHIP         -4   /* HIP runtime error */
 #define UW_EUNSUPPORTED -5   /* valid request the library does not handle */
 
-/* Thread-local text of the last error on this thread ("" if none). */
+/* (API) Thread-local text of the last error on this thread ("" if none). */
 const char* uw_last_error(void);
 
-/* Library version, (major << 16) | minor. */
+/* (API) Library version, (major << 16) | minor. */
 int uw_version(void);
 
-/* sizeof(uw_info), sizeof(uw_dmat), sizeof(uw_opts) as compiled, so a binding
+/* (API) sizeof(uw_info), sizeof(uw_dmat), sizeof(uw_opts) as compiled, so a binding
  * can check its mirror of these structs (any pointer may be NULL). */
 int uw_abi_struct_sizes(uint64_t* info, uint64_t* dmat, uint64_t* opts);
 
@@ -141,28 +146,29 @@ typedef struct {
 int uw_compress(const uint16_t* w /*host*/, int64_t rows, int64_t cols,
                 const uw_opts* opts, uw_blob** out);
 
-/* Fill *info (host) from a blob. */
+/* (API) Fill *info (host) from a blob. */
 int uw_blob_info(const uw_blob* blob, uw_info* info);
 
-/* Borrow a host pointer to section `sec` and its byte size (pointer valid
+/* (API) Borrow a host pointer to section `sec` and its byte size (pointer valid
  * until uw_blob_free; NULL with size 0 for an empty or absent section). */
 int uw_blob_section(const uw_blob* blob, int sec, const void** ptr, uint64_t* bytes);
 
-/* Serialize to a byte image: a 256-byte header (magic "UWF2", format version
+/* (API) Serialize to a byte image: a 256-byte header (magic "UWF2", format version
  * 2) then each stored section at a 256-byte aligned offset.  With buf == NULL
  * only *need is set.  UW_EINVAL if cap < *need. */
 int uw_blob_serialize(const uw_blob* blob, void* buf /*host*/, uint64_t cap, uint64_t* need);
 
-/* Parse a serialized image into a new blob and validate it (UW_EFORMAT,
+/* (API) Parse a serialized image into a new blob and validate it (UW_EFORMAT,
  * also for version-1 images, whose group lengths were 16-bit). */
 int uw_blob_deserialize(const void* buf /*host*/, uint64_t bytes, uw_blob** out);
 
 /* Build the NIB section of a blob that lacks it (host transcode). */
 int uw_blob_add_palette(uw_blob* blob);
 
+/* (API) Free a blob (NULL is a no-op). */
 void uw_blob_free(uw_blob* blob);
 
-/* Structural checks before any launch: magic sizes, C % 64, palette size,
+/* (API) Structural checks before any launch: magic sizes, C % 64, palette size,
  * code lengths (Kraft equality, <= 15), monotone tile offsets, per-tile
  * sum of GLEN against the tile's bytes, verbatim groups coded with 0 bits,
  * bitmap popcounts against TILE_VBASE and VEXP, no bitmap bits past G.
@@ -194,7 +200,7 @@ typedef struct {
     const uint32_t* mlut;
 } uw_dmat;
 
-/* Fill a descriptor from blob info (host) and device section pointers
+/* (API) Fill a descriptor from blob info (host) and device section pointers
  * (dev[s] for section s, NULL where absent). */
 int uw_dmat_init(uw_dmat* d, const uw_info* info, const void* const dev[UW_NUM_SECTIONS]);
 
@@ -302,7 +308,7 @@ enum {
                              its decode and matmul fused in one pass. */
 };
 
-/* Scratch bytes uw_matmul needs for (pipeline, shape, batch, split_k)
+/* (API) Scratch bytes uw_matmul needs for (pipeline, shape, batch, split_k)
  * (UW_PIPE_HUFF: the per-tile partial sums, whatever split_k);
  * split_k 0: for the split the library would choose with UW_KERNEL_AUTO on
  * the current device.  Returns the size (>= 0) or a negative error code. */
@@ -318,9 +324,10 @@ int uw_matmul(const uw_dmat* d, int pipeline, int kernel, int split_k,
               const uint16_t* X, int64_t batch, float* Y,
               void* scratch, uint64_t scratch_bytes, void* stream);
 
-/* h[i] = bf16_rne(SiLU(g[i]) * u[i]), SiLU(z) = z / (1 + exp(-z)), in fp32;
- * g, u fp32 [n], h bf16 bits [n].  The step between the gate/up and down
- * projections of a SwiGLU MLP. */
+/* (API) h[i] = bf16_rne(SiLU(g[i]) * u[i]), SiLU(z) = z / (1 + exp(-z)), in
+ * fp32; g, u fp32 [n], h bf16 bits [n].  The step between the gate/up and
+ * down projections of a SwiGLU MLP (the MLP whose matrices "How to compress
+ * model weights effectively" compresses; the page gives no formula for it). */
 int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, void* stream);
 
 /* Fused gate/up projections of a SwiGLU MLP block on the direct-palette
@@ -345,7 +352,7 @@ int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, voi
 int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, int64_t batch,
                    uint16_t* h, float* g_out, float* u_out, void* stream);
 
-/* Scratch bytes of uw_mlp_layer for gate and up of shape [rows, cols] and
+/* (API) Scratch bytes of uw_mlp_layer for gate and up of shape [rows, cols] and
  * down of shape [cols, rows] (rows, cols multiples of 64): one decoded plane
  * per matrix, g and u (fp32), h (bf16), split-K partials.  Returns the size
  * or a negative error code. */
@@ -375,7 +382,7 @@ int uw_mlp_layer(const uw_dmat* gate, const uw_dmat* up, const uw_dmat* down, in
                  void* scratch, uint64_t scratch_bytes, void* stream, void* aux_stream);
 
 /* ----------------------------------------------------------- kernel timer */
-/* Per-launch durations of the matmul kernels (GEMV and MFMA), for measuring
+/* (API) Per-launch durations of the matmul kernels (GEMV and MFMA), for measuring
  * them on their own stream.  While enabled, each matmul kernel launch takes
  * the next of `capacity` HIP event pairs, which the launch records at the
  * kernel's own start and end (hipExtLaunchKernel); launches beyond capacity
@@ -388,14 +395,23 @@ int uw_kernel_timer_reset(void);
 int uw_kernel_timer_read(float* ms /*host*/, int max, int* count /*host*/);
 
 /* --------------------------------------------------------------- autotune */
-/* Plan table: (rows, cols, batch) -> (pipeline, kernel, split_k), filled by a
- * measuring autotuner ("Why no single pipeline wins").  Process-global,
- * thread-safe.  lookup returns UW_EINVAL when the key is absent. */
+/* Plan table: (device, rows, cols, batch) -> (pipeline, kernel, split_k),
+ * filled by a measuring autotuner ("Why no single pipeline wins": the best
+ * pipeline is picked per matrix and batch by measuring).  The device is the
+ * calling thread's current HIP device (set, lookup and count act on its
+ * entries; clear empties the table for every device).  Process-global,
+ * thread-safe.  pipeline: UW_PIPE_FULL..UW_PIPE_DIRECT or UW_PIPE_HUFF;
+ * split_k 1..64.  lookup returns UW_EINVAL when the key is absent. */
 int uw_plan_set(int64_t rows, int64_t cols, int64_t batch, int pipeline, int kernel, int split_k);
 int uw_plan_lookup(int64_t rows, int64_t cols, int64_t batch, int* pipeline, int* kernel, int* split_k);
 int uw_plan_clear(void);
 int uw_plan_count(void);
-/* Text file, one "rows cols batch pipeline kernel split_k" line per entry. */
+/* Text file: a first line "uwplan-v2 <device>", <device> being
+ * "<gcnArchName>/<compute units>cu" of the current device ("none" without
+ * one), then one "rows cols batch pipeline kernel split_k" line per entry of
+ * that device.  load rejects a file tuned on another device (UW_EUNSUPPORTED)
+ * and a malformed one (UW_EFORMAT), leaving the table unchanged; UW_EINVAL
+ * when the file cannot be opened or written. */
 int uw_plan_save(const char* path /*host*/);
 int uw_plan_load(const char* path /*host*/);
 

@@ -111,6 +111,34 @@ int device_cus() {
     return cus;
 }
 
+}  // namespace
+
+namespace uw {
+int current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    return dev;
+}
+
+std::string device_key(int ordinal) {
+    if (ordinal < 0) return "none";
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, ordinal) != hipSuccess) {
+        (void)hipGetLastError();
+        return "none";
+    }
+    std::string arch(prop.gcnArchName);
+    for (char& c : arch)
+        if (c == ' ' || c == '\t' || c == '\n') c = '_';
+    return arch + "/" + std::to_string(prop.multiProcessorCount) + "cu";
+}
+}  // namespace uw
+
+namespace {
+
 // The kernel family UW_KERNEL_AUTO picks for a shape.  Measured on MI355X
 // (Llama MLP shapes): the GEMV wins at batch 1 (below batch 4 for bf16
 // weights), the skinny MFMA kernel from there through 32 (the autotuner's

@@ -19,6 +19,12 @@ constexpr uint64_t kHeaderBytes = 256;
 int fail(int code, const std::string& msg);
 void clear_error();
 
+// The current HIP device: its ordinal (-1 when no device can be selected) and
+// an identity for tuned plans, "<gcnArchName>/<compute units>cu" ("none"
+// without a device).  Defined with the HIP entry points.
+int current_device();
+std::string device_key(int ordinal);
+
 }  // namespace uw
 
 struct uw_blob {

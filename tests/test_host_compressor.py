@@ -235,6 +235,39 @@ def test_plan_table_roundtrip(tmp_path):
     assert uw.plan_lookup(4096, 14336, 256) == (uw.UW_PIPE_PAL, uw.UW_KERNEL_MFMA, 4)
     with pytest.raises(uw.UnweightError):
         uw.plan_set(1, 64, 1, 7, 0, 1)
+    with pytest.raises(uw.UnweightError):
+        uw.plan_set(1, 64, 1, uw.UW_PIPE_BF16, 0, 1)
+    uw.plan_set(14336, 4096, 1, uw.UW_PIPE_HUFF, uw.UW_KERNEL_AUTO, 1)      # the autotuner may pick it
+    assert uw.plan_lookup(14336, 4096, 1) == (uw.UW_PIPE_HUFF, uw.UW_KERNEL_AUTO, 1)
+    uw.plan_clear()
+
+
+def test_plan_file_device_key(tmp_path):
+    """A plan file names the device it was tuned on; another device's plan,
+    a file without that line and a malformed entry are refused and leave the
+    table as it was."""
+    uw.plan_clear()
+    uw.plan_set(4096, 14336, 16, uw.UW_PIPE_DIRECT, uw.UW_KERNEL_SKINNY, 1)
+    p = tmp_path / "plan.txt"
+    uw.plan_save(p)
+    head, *entries = p.read_text().splitlines()
+    magic, device = head.split()
+    assert magic == "uwplan-v2" and device                # "none" here, "<arch>/<cus>cu" on a GPU
+    assert entries == [f"4096 14336 16 {uw.UW_PIPE_DIRECT} {uw.UW_KERNEL_SKINNY} 1"]
+    other = tmp_path / "other.txt"
+    other.write_text("uwplan-v2 gfx000:test/1cu\n1 64 1 4 0 1\n")
+    no_head = tmp_path / "nohead.txt"
+    no_head.write_text("1 64 1 4 0 1\n")
+    bad = tmp_path / "bad.txt"
+    bad.write_text(f"uwplan-v2 {device}\n1 64 1 4 0 1\n1 64 2 9 0 1\n")
+    for path, code in ((other, -5), (no_head, -3), (bad, -3)):
+        with pytest.raises(uw.UnweightError) as ei:
+            uw.plan_load(path)
+        assert ei.value.code == code, path.name
+        assert uw.plan_count() == 1
+    uw.plan_clear()
+    uw.plan_load(p)
+    assert uw.plan_lookup(4096, 14336, 16) == (uw.UW_PIPE_DIRECT, uw.UW_KERNEL_SKINNY, 1)
     uw.plan_clear()
 
 
