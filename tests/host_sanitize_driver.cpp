@@ -17,6 +17,14 @@
 
 #include "unweight.h"
 
+// The host sources take the device's identity for tuned plans from the HIP
+// half of the library, which this CPU-only build does not link: here there
+// is no device (what the library reports when none can be selected).
+namespace uw {
+int current_device() { return -1; }
+std::string device_key(int) { return "none"; }
+}  // namespace uw
+
 namespace {
 
 void need(bool ok, const std::string& what) {
@@ -212,6 +220,17 @@ int main() {
         std::fputs("not a plan\n\x01\x02 rows cols", f);
         std::fclose(f);
         (void)uw_plan_load(path);   // an error or an empty table; never a crash
+        f = std::fopen(path, "w");
+        need(f != nullptr, "rewrite temp file");
+        std::fputs("uwplan-v2 none\n1 64 1 4 0 1\n1 64 2 4 0", f);   // truncated last entry
+        std::fclose(f);
+        need(uw_plan_clear() == UW_OK, "plan clear");
+        need(uw_plan_load(path) == UW_EFORMAT && uw_plan_count() == 0, "truncated plan refused, table unchanged");
+        f = std::fopen(path, "w");
+        need(f != nullptr, "rewrite temp file");
+        std::fputs("uwplan-v2 gfx000/1cu\n1 64 1 4 0 1\n", f);
+        std::fclose(f);
+        need(uw_plan_load(path) == UW_EUNSUPPORTED && uw_plan_count() == 0, "other device's plan refused");
         std::remove(path);
         need(uw_plan_clear() == UW_OK, "plan clear at end");
     }
