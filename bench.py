@@ -638,16 +638,18 @@ def _cpu_baseline(batch, frac_rows, step_seconds):
 
 
 # --------------------------------------------------------------- profiles
-def kernel_source(kernel_tag):
-    """The source file of the kernel a profile tag names (gemv_*, skinny_*, mfma_*)."""
-    return {"gemv": "gemv.hip", "skinny": "mfma_gemv.hip", "mfma": "gemm_mfma.hip",
-            "huffman": "decode.hip"}[kernel_tag.split("_")[0]]
+def kernel_sources(kernel_tag):
+    """The source files of the kernels a profile tag names (gemv_*, skinny_*,
+    mfma_*, huffman_*); the skinny family has two kernels, one dispatching to
+    the other."""
+    return {"gemv": ["gemv.hip"], "skinny": ["mfma_gemv.hip", "skinny_dma.hip"], "mfma": ["gemm_mfma.hip"],
+            "huffman": ["decode.hip"]}[kernel_tag.split("_")[0]]
 
 
 def profile_source_hash(kernel_tag):
     import hashlib
     csrc = os.path.join(ROOT, "mlp_matmul_amd", "csrc")
-    src = open(os.path.join(csrc, kernel_source(kernel_tag)), "rb").read()
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in kernel_sources(kernel_tag))
     src += open(os.path.join(csrc, "device_common.h"), "rb").read()
     return hashlib.sha256(src).hexdigest()[:16]
 

@@ -68,6 +68,14 @@ bool mfma_gemv_supported(const MatArgs& a);
 // sources, batch 1..16).
 bool mfma_gemv_gateup_supported(const MatArgs& gate, const MatArgs& up);
 hipError_t launch_mfma_gemv_gateup(const MatArgs& gate, const MatArgs& up, uint16_t* h, hipStream_t s);
+// Skinny MFMA kernel with LDS-DMA operand streaming (palette sources, batch
+// 1..16), single matrices and the gate/up pair.
+bool skinny_dma_supported(const MatArgs& a);
+// The library's choice between this kernel and the register-staged one (the
+// same for a matrix alone and for the gate/up pair of its shape).
+bool skinny_dma_preferred(const MatArgs& a);
+hipError_t launch_skinny_dma(const MatArgs& a, hipStream_t s);
+hipError_t launch_skinny_dma_gateup(const MatArgs& gate, const MatArgs& up, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, uint16_t* h, hipStream_t s);
 
 // LDS bytes the decoder needs for a code of longest length lmax.

@@ -523,6 +523,10 @@ bool mfma_gemv_gateup_supported(const MatArgs& g, const MatArgs& u) {
 // so g and u equal what separate skinny launches give, bit for bit.
 hipError_t launch_mfma_gemv_gateup(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
     if (g.R == 0) return hipSuccess;
+    if (skinny_dma_preferred(g)) {
+        const hipError_t e = launch_skinny_dma_gateup(g, u, h, s);
+        if (e != hipErrorNotSupported) return e;
+    }
     if (!mfma_gemv_gateup_supported(g, u)) return hipErrorNotSupported;
     const Shape sh = choose_shape(g);
     const int kw = sh.kw;
@@ -540,6 +544,10 @@ bool mfma_gemv_supported(const MatArgs& a) {
 
 hipError_t launch_mfma_gemv(int src, const MatArgs& a, hipStream_t s) {
     if (a.R == 0 || a.B == 0) return hipSuccess;
+    if (src == SRC_PAL && skinny_dma_preferred(a)) {
+        const hipError_t e = launch_skinny_dma(a, s);
+        if (e != hipErrorNotSupported) return e;
+    }
     switch (src) {
         case SRC_BF16: return launch_src<SRC_BF16>(a, s);
         case SRC_EXP: return launch_src<SRC_EXP>(a, s);

@@ -69,10 +69,11 @@ def test_committed_profiles_match_the_kernel_sources(name):
     txt = open(os.path.join(ROOT, "profiles", name + ".md")).read()
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
     assert m, "profile without a source hash"
-    src_file = {"gemv": "gemv.hip", "skinny": "mfma_gemv.hip", "mfma": "gemm_mfma.hip",
-                "huffman": "decode.hip"}[name.split("_")[0]]
+    src_files = {"gemv": ["gemv.hip"], "skinny": ["mfma_gemv.hip", "skinny_dma.hip"], "mfma": ["gemm_mfma.hip"],
+                 "huffman": ["decode.hip"]}[name.split("_")[0]]
     csrc = os.path.join(ROOT, "mlp_matmul_amd", "csrc")
-    src = open(os.path.join(csrc, src_file), "rb").read() + open(os.path.join(csrc, "device_common.h"), "rb").read()
+    src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in src_files)
+    src += open(os.path.join(csrc, "device_common.h"), "rb").read()
     assert hashlib.sha256(src).hexdigest()[:16] == m.group(1)[:16]
     assert "rocprofv3" in txt
 

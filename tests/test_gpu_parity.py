@@ -280,6 +280,56 @@ def test_skinny_launch_shapes(torch_cuda, monkeypatch, kw, pd, rb):
             assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny {name} kw={kw} pd={pd} rb={rb} C={C}")
 
 
+@pytest.mark.parametrize("kw", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [2, 3, 4])
+@pytest.mark.parametrize("nrb", [1, 2])
+def test_skinny_dma_launch_shapes(torch_cuda, monkeypatch, kw, d, nrb):
+    """The skinny kernel that streams its operands through LDS by DMA
+    (palette source), forced on small matrices in every K-split, ring depth
+    and row-block count the launcher can pick (UW_SKINNY_DMA / UW_DMA_KW /
+    _D / _NRB): slices shorter than the ring and not a multiple of it, empty
+    slices (one step split eight ways), rows past R, each count of loaded
+    activation row quads, row segments that straddle tiles, verbatim groups."""
+    monkeypatch.setenv("UW_SKINNY_DMA", "1")
+    monkeypatch.setenv("UW_DMA_KW", str(kw))
+    monkeypatch.setenv("UW_DMA_D", str(d))
+    monkeypatch.setenv("UW_DMA_NRB", str(nrb))
+    for R, C, B in [(29, 2048 + 256, 3), (45, 1152, 5), (33, 4096 + 512, 16), (17, 9216, 9), (70, 128, 12),
+                    (1, 640, 1)]:
+        print_case(f"skinny dma kw={kw} d={d} nrb={nrb} R={R} C={C} B={B}")
+        w = workloads.gaussian_weights(np.random.default_rng(R + C + kw + d), R, C, 0.02, 0.004, 1.0)
+        x = _x(C + B + nrb, B, C)
+        Y = uw.gemm_recon_pal(uw.compress(w).to_device(), None, to_dev_bf16(x), kernel=uw.UW_KERNEL_SKINNY)
+        assert_matmul_close(Y.cpu().numpy(), w, x, what=f"skinny dma kw={kw} d={d} nrb={nrb} R={R} C={C} B={B}")
+
+
+def test_skinny_dma_one_hot_and_verbatim(torch_cuda, monkeypatch):
+    """The DMA skinny kernel rebuilds every weight exactly (one-hot columns,
+    including groups verbatim in many rows) and handles matrices whose groups
+    are mostly verbatim."""
+    monkeypatch.setenv("UW_SKINNY_DMA", "1")
+    print_case("skinny dma one-hot")
+    w, _ = workloads.small_matrix()
+    dm = uw.compress(w).to_device()
+    vflag = codec.encode(w).vflag.reshape(w.shape[0], -1)
+    hot = np.argsort(-vflag.sum(axis=0))[:8] * 64 + np.array([0, 5, 17, 63, 31, 40, 2, 62])
+    cols = np.concatenate([hot, np.arange(8) * 111 + 3])
+    Y = uw.gemm_recon_pal(dm, None, to_dev_bf16(_one_hot(cols, w.shape[1])), kernel=uw.UW_KERNEL_SKINNY)
+    expect = numerics.bf16_to_f64(w[:, cols].T).astype(np.float32)
+    assert np.array_equal(Y.cpu().numpy().view(np.uint32), expect.view(np.uint32))
+    print_case("skinny dma mostly verbatim")
+    rng = np.random.default_rng(12)
+    R, C = 96, 2048
+    wide = np.repeat(rng.random((R, C // 64)) < 0.85, 64, axis=1)
+    scale = np.where(wide, np.exp2(rng.integers(-12, 13, (R, C))), 1.0)
+    w = workloads.f32_to_bf16_bits((rng.standard_normal((R, C)) * 0.02 * scale).astype(np.float32))
+    x = _x(13, 11, C)
+    dm = uw.compress(w).to_device()
+    assert 0.8 * dm.info.groups < dm.info.verbatim_groups < dm.info.groups
+    Y = uw.gemm_recon_pal(dm, None, to_dev_bf16(x), kernel=uw.UW_KERNEL_SKINNY)
+    assert_matmul_close(Y.cpu().numpy(), w, x, what="skinny dma verbatim")
+
+
 def test_skinny_mostly_verbatim(torch_cuda):
     """About 85% of the groups hold exponents far outside the palette (stored
     verbatim), mixed with ordinary groups: the verbatim override on most lanes
@@ -607,21 +657,29 @@ def _gate_up_case(wg, wu, x, rows=None, what=""):
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8, 9, 16])
-def test_gate_up_fused_small(torch_cuda, B):
+@pytest.mark.parametrize("dma", [False, True])
+def test_gate_up_fused_small(torch_cuda, monkeypatch, B, dma):
     """Reduced-width gate/up pair (4096 x 512) at every batch the fused
     launch takes: the GEMV pair at 1-2, the skinny MFMA pair (each quad count
     of activation rows) at 3-16."""
-    print_case(f"fused gate/up small B={B}")
+    if dma and B <= 2:
+        pytest.skip("the GEMV pair")
+    if dma:
+        monkeypatch.setenv("UW_SKINNY_DMA", "1")           # the pair and the unfused calls alike
+    print_case(f"fused gate/up small B={B} dma={dma}")
     wg = workloads.layer_weight(3, 1, 0, shape=(4096, 512))
     wu = workloads.layer_weight(3, 1, 1, shape=(4096, 512))
     _gate_up_case(wg, wu, workloads.layer_activation(3, 1, 0, B, cols=512), what=f"B={B}")
 
 
-@pytest.mark.parametrize("R,C,B", [(1, 64, 1), (37, 1088, 2), (5, 8192, 2), (4100, 1152, 3), (4111, 2176, 16)])
+@pytest.mark.parametrize("R,C,B", [(1, 64, 1), (37, 1088, 2), (5, 8192, 2), (4100, 1152, 3), (4111, 2176, 16),
+                                   (12300, 1152, 13), (12290, 4096 + 128, 5)])
 def test_gate_up_fused_ragged(torch_cuda, R, C, B):
     """Rows not a multiple of a workgroup, columns not a multiple of a slab
     (GEMV pair) or of the four K-slices (skinny pair: 9 and 17 steps), one-row
-    and one-group matrices, outliers forcing verbatim groups."""
+    and one-group matrices, outliers forcing verbatim groups; matrices tall
+    enough for the DMA skinny pair, whose 9 and 33 steps leave a step after
+    the two-step ring and whose last row block is partial."""
     print_case(f"fused gate/up ragged R={R} C={C} B={B}")
     rng = np.random.default_rng(R * C + B)
     wg = workloads.gaussian_weights(rng, R, C, 0.02, 0.004, 1.0)
@@ -629,11 +687,12 @@ def test_gate_up_fused_ragged(torch_cuda, R, C, B):
     _gate_up_case(wg, wu, _x(R + C, B, C), what=f"R={R} C={C} B={B}")
 
 
-@pytest.mark.parametrize("B", [1, 4, 16])
+@pytest.mark.parametrize("B", [1, 4, 8, 12, 16])
 def test_gate_up_fused_full_size(torch_cuda, B):
     """Llama-3.1-8B gate and up in the benchmark's launches (the GEMV pair at
-    batch 1, the skinny MFMA pair at 4 and 16): bitwise equal to the unfused
-    calls, sampled rows against the oracle."""
+    batch 1, the register-staged skinny pair at 4, the DMA skinny pair at 8,
+    12 and 16): bitwise equal to the unfused calls, sampled rows against the
+    oracle."""
     print_case(f"fused gate/up full size B={B}")
     wg, wu = workloads.layer_weight(2, 0, 0), workloads.layer_weight(2, 0, 1)
     rows = np.sort(np.random.default_rng(5).choice(wg.shape[0], 384, replace=False))
