@@ -336,12 +336,14 @@ struct DShape {
 // K-split: the smallest (1, 2, 4, 8) that gives at least three waves per
 // compute unit and keeps each slice within kDMaxSlice columns; the K-split,
 // and so the order of every output's sums, depends on the matrix shape only,
-// which makes the gate/up pair bitwise equal to single launches.  Ring depth:
-// two steps for the pair (measured on MI355X, Llama gate/up at batch 6-16:
-// 36.6-38.9 us against 37.5-39.8 with three); for single matrices as many
-// steps as fit an even share of 150 KB of LDS among the waves a compute unit
-// holds, between 2 and 4, and at most what one workgroup's share allows
-// (UW_DMA_KW / UW_DMA_D override).
+// which makes the gate/up pair bitwise equal to single launches.  Ring depth,
+// as measured on MI355X on the Llama shapes: two steps for the pair (gate/up
+// at batch 6-16: 36.6-38.9 us against 37.5-39.8 with three); for single
+// matrices three steps up to batch 8 (the 14336x4096 gate at batch 5: 19.9
+// against 23.2 us with four) and four above (batch 16: 24.9 against 25.8);
+// never more than an even share of 150 KB of LDS among the waves a compute
+// unit holds, nor than one workgroup's share allows (UW_DMA_KW / UW_DMA_D
+// override).
 DShape dma_shape(const MatArgs& a, int rows_per_wg, int slot_bytes, bool dual) {
     const int64_t cus = a.cus > 0 ? a.cus : 256;
     const int64_t steps = a.C / kDStep;
@@ -354,12 +356,12 @@ DShape dma_shape(const MatArgs& a, int rows_per_wg, int slot_bytes, bool dual) {
     kw = kw <= 1 ? 1 : (kw <= 2 ? 2 : (kw <= 4 ? 4 : 8));
     while (kw < 8 && (steps + kw - 1) / kw * kDStep > kDMaxSlice) kw *= 2;
     int d = env_int("UW_DMA_D", 0);
-    if (d <= 0 && dual) {
-        d = 2;                    // measured on MI355X: the pair runs best with two steps in flight
-    } else if (d <= 0) {
+    if (d <= 0) {
         const int64_t waves_per_cu = (wgs * kw + cus - 1) / cus;
         const int64_t budget = 150 * 1024 / (waves_per_cu > 0 ? waves_per_cu : 1);
-        d = int(budget / slot_bytes);
+        const int fit = int(budget / slot_bytes);
+        const int want = dual ? 2 : (a.B <= 8 ? 3 : 4);
+        d = want < fit ? want : fit;
     }
     d = d < 2 ? 2 : (d > 4 ? 4 : d);
     return {kw, d};
@@ -413,18 +415,22 @@ hipError_t launch_nrb(const MatArgs& a, const MatArgs& up, uint16_t* h, hipStrea
 
 }  // namespace
 
-// Taken where measured faster than the register-staged skinny kernel on
-// MI355X: from batch 5 on matrices tall enough for one wave per 16-row block
-// and at least three waves per compute unit (K unsplit; the Llama gate/up
-// pair at batch 8: 36.6 against 40.3 us, batch 16: 38.9 against 46.8 us).
-// Shorter matrices (the 4096-row down projection: 25.4 against 22.0 us at
-// batch 16) keep the other kernel.  UW_SKINNY_DMA=0 / 1 forces it off / on.
+// Taken where the gate/up pair measured faster than on the register-staged
+// skinny kernel on MI355X: from batch 3 on matrices tall enough for one wave
+// per 16-row block and at least three waves per compute unit (K unsplit; the
+// Llama gate/up pair at batch 4: 36.0 against 37.8 us, batch 8: 36.8 against
+// 40.4, batch 16: 39.1 against 46.3).  A single matrix of such a shape takes
+// the same kernel, so that the pair stays bitwise equal to single launches
+// (the 14336x4096 gate alone: 19.6 against 19.3 us at batch 4, 20.3 against
+// 20.6 at 8, 24.9 against 23.4 at 16).  Shorter matrices (the 4096-row down
+// projection: 25.4 against 22.0 us at batch 16) keep the other kernel.
+// UW_SKINNY_DMA=0 / 1 forces it off / on.
 bool skinny_dma_preferred(const MatArgs& a) {
     const int mode = env_int("UW_SKINNY_DMA", -1);
     if (mode == 0 || !skinny_dma_supported(a)) return false;
     if (mode > 0) return true;
     const int64_t cus = a.cus > 0 ? a.cus : 256;
-    return a.B >= 5 && (a.R + 15) / 16 >= 3 * cus;
+    return a.B >= 3 && (a.R + 15) / 16 >= 3 * cus;
 }
 
 // Whole 128-column steps, batch 1..16, every K-slice (split 8 ways at most)

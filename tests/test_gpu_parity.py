@@ -673,7 +673,7 @@ def test_gate_up_fused_small(torch_cuda, monkeypatch, B, dma):
 
 
 @pytest.mark.parametrize("R,C,B", [(1, 64, 1), (37, 1088, 2), (5, 8192, 2), (4100, 1152, 3), (4111, 2176, 16),
-                                   (12300, 1152, 13), (12290, 4096 + 128, 5)])
+                                   (12300, 1152, 13), (12290, 4096 + 128, 5), (12289, 640, 3)])
 def test_gate_up_fused_ragged(torch_cuda, R, C, B):
     """Rows not a multiple of a workgroup, columns not a multiple of a slab
     (GEMV pair) or of the four K-slices (skinny pair: 9 and 17 steps), one-row
@@ -690,9 +690,9 @@ def test_gate_up_fused_ragged(torch_cuda, R, C, B):
 @pytest.mark.parametrize("B", [1, 4, 8, 12, 16])
 def test_gate_up_fused_full_size(torch_cuda, B):
     """Llama-3.1-8B gate and up in the benchmark's launches (the GEMV pair at
-    batch 1, the register-staged skinny pair at 4, the DMA skinny pair at 8,
-    12 and 16): bitwise equal to the unfused calls, sampled rows against the
-    oracle."""
+    batch 1, the DMA skinny pair at 4, 8, 12 and 16, one, two and four
+    activation row quads): bitwise equal to the unfused calls, sampled rows
+    against the oracle."""
     print_case(f"fused gate/up full size B={B}")
     wg, wu = workloads.layer_weight(2, 0, 0), workloads.layer_weight(2, 0, 1)
     rows = np.sort(np.random.default_rng(5).choice(wg.shape[0], 384, replace=False))
