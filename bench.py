@@ -220,7 +220,8 @@ class Step:
         st = ct.c_void_p(stream.cuda_stream)
         P = lambda t: ct.c_void_p(t.data_ptr())
         scr, nsc = P(self.scratch), ct.c_uint64(self.scratch.numel())
-        self.fused = fuse and batch <= 16 and self._plans_direct(uw, pipe, F, H, batch)
+        self.fused = fuse and batch <= 32 and self._plans_direct(uw, pipe, F, H, batch) and \
+            self._pair_supported(uw, layers[0], self.X[0], batch)
         self.calls = []          # per layer: the bound calls in launch order
         self.kinds = []          # per layer: what each timed (matmul) launch is
         self.bytes = []          # per layer: algorithmic bytes of each timed launch
@@ -276,9 +277,23 @@ class Step:
         return need
 
     @staticmethod
+    def _pair_supported(uw, lay, X, batch):
+        """Whether uw_mlp_gate_up takes this shape at this batch (batch 17-32
+        only on tall matrices)."""
+        if lay.mats[0] is None:
+            return False
+        try:
+            uw.mlp_gate_up(lay.mats[0], lay.mats[1], X)
+            return True
+        except uw.UnweightError as e:
+            if e.code != uw.UW_EUNSUPPORTED:
+                raise
+            return False
+
+    @staticmethod
     def _plans_direct(uw, pipe, F, H, batch):
         """Gate/up may be fused (uw_mlp_gate_up: the GEMV pair at batch 1-2,
-        the skinny MFMA pair at 3-16) when they would run on the direct-palette
+        a skinny MFMA pair at 3-32) when they would run on the direct-palette
         form with those kernels: asked for directly, or what the plan table
         holds for the gate shape at this batch (no entry: direct palette with
         the library's kernel choice)."""

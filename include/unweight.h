@@ -337,18 +337,26 @@ int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, voi
  *   g = X . gate^T,  u = X . up^T  (fp32 accumulation), h[b][r] =
  *   bf16_rne(SiLU(g) * u) with the same SiLU arithmetic as uw_silu_mul_bf16.
  * Batch 1-2 runs the GEMV pair: g and u equal uw_gemm_recon_pal with
- * UW_KERNEL_GEMV bit for bit.  Batch 3-16 runs the skinny MFMA pair: g and u
- * equal uw_gemm_recon_pal with UW_KERNEL_SKINNY bit for bit (same K-split).
- * h is bit-identical to uw_silu_mul_bf16 on those g, u.
+ * UW_KERNEL_GEMV bit for bit.  Batch 3-32 on matrices of at least 48 rows
+ * per compute unit (12288 on MI355X) runs the pair on the skinny kernel that
+ * streams its operands into LDS by DMA, which sums each output's K in one
+ * wave (K unsplit up to 4096 columns): g and u are the same products as
+ * uw_gemm_recon_pal with UW_KERNEL_SKINNY, summed in another order (equal
+ * within the matmul's fp32 rounding, not bit for bit).  Other shapes at
+ * batch 3-16 run the register-staged skinny pair: g and u equal
+ * uw_gemm_recon_pal with UW_KERNEL_SKINNY bit for bit (same K-split).  In
+ * every case h is bit-identical to uw_silu_mul_bf16 on the g, u the call
+ * computes.
  * gate, up: same shape [rows, cols], both with a NIB section; X bf16 bits
  * [batch, cols]; h bf16 bits [batch, rows]; g_out, u_out fp32 [batch, rows]
  * or NULL (not written).  Device pointers, 16-byte aligned, caller-owned.
  * UW_EINVAL on NULL/misaligned pointers, mismatched shapes, an inconsistent
  * descriptor, or verbatim groups without their VEXP section;
- * UW_EUNSUPPORTED unless 1 <= batch <= 16, cols % 128 == 0, cols <= 32768
- * and the library splits K at most 4 ways for this shape on the current
- * device (about one wave per SIMD: at least ~4096 rows on MI355X), or, at
- * batch 1-2, batch*cols*2 <= 32768 and cols <= 245760. */
+ * UW_EUNSUPPORTED unless cols % 128 == 0, cols <= 32768 and either
+ * 1 <= batch <= 32 on a matrix of at least 48 rows per compute unit, or
+ * 1 <= batch <= 16 and the library splits K at most 4 ways for this shape on
+ * the current device (about one wave per SIMD: at least ~4096 rows on
+ * MI355X), or, at batch 1-2, batch*cols*2 <= 32768 and cols <= 245760. */
 int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, int64_t batch,
                    uint16_t* h, float* g_out, float* u_out, void* stream);
 

@@ -545,7 +545,7 @@ int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, in
     uwk::MatArgs u = compressed_args(up, up->nib, X, batch, u_out);
     g.cus = u.cus = device_cus();
     const bool small = gate->rows * gate->cols < (int64_t(1) << 31) && batch * gate->cols < (int64_t(1) << 31);
-    // batch 1-2: the GEMV pair; 3-16: the skinny MFMA pair (measured on MI355X)
+    // batch 1-2: the GEMV pair; 3-32: a skinny MFMA pair (measured on MI355X)
     static const int gemv_max = [] {
         const char* e = getenv("UW_GATEUP_GEMV_MAX");
         return e && *e ? atoi(e) : 2;
@@ -558,7 +558,8 @@ int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, in
     else
         return uw::fail(UW_EUNSUPPORTED, std::string(who) +
                                              ": needs batch 1..16, cols % 128 == 0, cols <= 32768 and a K-split of at "
-                                             "most 4 for the shape (batch 1-2: or batch*cols*2 <= 32768)");
+                                             "most 4 for the shape (batch 1-2: or batch*cols*2 <= 32768; batch 17-32: "
+                                             "at least 48 rows per compute unit)");
     return e == hipSuccess ? UW_OK : hip_fail(e, who);
 }
 

@@ -69,11 +69,13 @@ bool mfma_gemv_supported(const MatArgs& a);
 bool mfma_gemv_gateup_supported(const MatArgs& gate, const MatArgs& up);
 hipError_t launch_mfma_gemv_gateup(const MatArgs& gate, const MatArgs& up, uint16_t* h, hipStream_t s);
 // Skinny MFMA kernel with LDS-DMA operand streaming (palette sources, batch
-// 1..16), single matrices and the gate/up pair.
+// 1..32), single matrices and the gate/up pair.
 bool skinny_dma_supported(const MatArgs& a);
-// The library's choice between this kernel and the register-staged one (the
-// same for a matrix alone and for the gate/up pair of its shape).
-bool skinny_dma_preferred(const MatArgs& a);
+// Whether the gate/up pair of this shape and batch takes this kernel (the
+// library's choice, or forced by UW_SKINNY_DMA).
+bool skinny_dma_pair_preferred(const MatArgs& a);
+// Whether single matrices are forced onto this kernel (UW_SKINNY_DMA=1).
+bool skinny_dma_forced();
 hipError_t launch_skinny_dma(const MatArgs& a, hipStream_t s);
 hipError_t launch_skinny_dma_gateup(const MatArgs& gate, const MatArgs& up, uint16_t* h, hipStream_t s);
 hipError_t launch_silu_mul(const float* g, const float* u, int64_t n, uint16_t* h, hipStream_t s);

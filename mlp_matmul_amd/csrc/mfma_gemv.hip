@@ -508,26 +508,35 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
 // Supported when the K-slices are whole 128-column steps and, split 8 ways at
 // most, each slice spans at most 4096 columns (so a lane's row segment
 // touches at most two tiles).
-// Gate/up pair (palette sources): batch <= 16 (above it the separate
-// launches take two row blocks per wave on tall matrices and measured faster
-// than the pair: Llama gate/up at batch 32, 61.8 against 67.9 us), and the
-// K-split the library takes for one of the matrices at most 4 (so a
-// workgroup holds at most 8 waves; small matrices that split 8 ways are left
-// to separate launches).
-bool mfma_gemv_gateup_supported(const MatArgs& g, const MatArgs& u) {
+// Gate/up pair (palette sources): the LDS-DMA kernel's pair where the
+// library prefers it (batch 3-32 on tall matrices); else this kernel's pair:
+// batch <= 16 (above it the separate launches take two row blocks per wave
+// on tall matrices and measured faster than this pair: Llama gate/up at
+// batch 32, 61.8 against 67.9 us), and the K-split the library takes for one
+// of the matrices at most 4 (so a workgroup holds at most 8 waves; small
+// matrices that split 8 ways are left to separate launches).
+namespace {
+bool staged_pair_supported(const MatArgs& g, const MatArgs& u) {
     return g.R == u.R && g.C == u.C && g.B == u.B && g.B >= 1 && g.B <= 16 && g.C > 0 && g.C % kKStep == 0 &&
            mfma_gemv_supported(g) && choose_shape(g).kw <= 4;
 }
+}  // namespace
 
-// The K-split of the pair is the library's choice for one of its matrices,
-// so g and u equal what separate skinny launches give, bit for bit.
+bool mfma_gemv_gateup_supported(const MatArgs& g, const MatArgs& u) {
+    if (g.R == u.R && g.C == u.C && g.B == u.B && skinny_dma_pair_preferred(g)) return true;   // the DMA pair
+    return staged_pair_supported(g, u);
+}
+
+// This kernel's pair splits K as the library does for one of its matrices,
+// so its g and u equal what separate launches of this kernel give, bit for
+// bit; the DMA pair likewise equals single launches of the DMA kernel.
 hipError_t launch_mfma_gemv_gateup(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
     if (g.R == 0) return hipSuccess;
-    if (skinny_dma_preferred(g)) {
+    if (skinny_dma_pair_preferred(g)) {
         const hipError_t e = launch_skinny_dma_gateup(g, u, h, s);
         if (e != hipErrorNotSupported) return e;
     }
-    if (!mfma_gemv_gateup_supported(g, u)) return hipErrorNotSupported;
+    if (!staged_pair_supported(g, u)) return hipErrorNotSupported;
     const Shape sh = choose_shape(g);
     const int kw = sh.kw;
     if (kw <= 2)
@@ -544,7 +553,7 @@ bool mfma_gemv_supported(const MatArgs& a) {
 
 hipError_t launch_mfma_gemv(int src, const MatArgs& a, hipStream_t s) {
     if (a.R == 0 || a.B == 0) return hipSuccess;
-    if (src == SRC_PAL && skinny_dma_preferred(a)) {
+    if (src == SRC_PAL && skinny_dma_forced() && skinny_dma_supported(a)) {
         const hipError_t e = launch_skinny_dma(a, s);
         if (e != hipErrorNotSupported) return e;
     }

@@ -1,4 +1,4 @@
-// Skinny matmul (batch 1..16) on palette-source weights with every streamed
+// Skinny matmul (batch 1..32) on palette-source weights with every streamed
 // operand moved by the LDS DMA path, and the gate/up pair of an MLP block
 // with the SiLU product in its epilogue.
 //
@@ -19,7 +19,9 @@
 // slots, one LDS array per slot so the compiler can tell the slots apart).
 // Per row block and step: the 4-bit indices (16 rows x 64 bytes, one load)
 // and the sign/mantissa bytes (16 x 128 bytes, two loads); once per step the
-// activation tile (4*XQ batch rows x 256 bytes, XQ loads).  The lane that
+// activation tile (4*XQ batch rows x 256 bytes, XQ loads; batch 17-32 takes
+// two 16-column batch tiles, so each rebuilt weight feeds eight MFMAs a step
+// instead of four).  The lane that
 // loads a 16-byte chunk is picked so that the chunk lands at an XOR-swizzled
 // slot of its row, which makes the read-back in the MFMA operand layout (16
 // lanes on 16 rows, one chunk column) hit distinct banks.  Verbatim
@@ -76,7 +78,8 @@ struct VRegs {
 template <int NRB, bool DUAL, int XQ, int KW, int D>
 __global__ __launch_bounds__(64 * KW) void skinny_dma_kernel(MatArgs a, MatArgs up, uint16_t* H) {
     static_assert(!DUAL || NRB == 2, "gate/up pair: one block of each matrix");
-    static_assert(D >= 2 && D <= 4 && XQ >= 1 && XQ <= 4, "ring depth, activation quads");
+    static_assert(D >= 2 && D <= 4 && ((XQ >= 1 && XQ <= 4) || XQ == 8), "ring depth, activation quads");
+    constexpr int NB = XQ > 4 ? 2 : 1;                   // 16-column batch tiles
     constexpr int kXOff = NRB * (kNibBytes + kSmBytes);
     constexpr int kSlot = kXOff + XQ * 1024;             // LDS bytes of one step of one wave
     constexpr int kPer = NRB * 5 + XQ;                   // vector-memory instructions a step
@@ -185,21 +188,26 @@ __global__ __launch_bounds__(64 * KW) void skinny_dma_kernel(MatArgs a, MatArgs 
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    f32x4_t acc[NRB];
+    f32x4_t acc[NRB][NB];
 #pragma unroll
-    for (int r = 0; r < NRB; ++r) acc[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < NRB; ++r)
+#pragma unroll
+        for (int n = 0; n < NB; ++n) acc[r][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int j, const VRegs<NRB>& v) {
         const uint8_t* const base = slot_base(j);
-        // every LDS read of the step first (B fragments: batch row rl, or a
-        // loaded row when fewer than 16 are; the lane's 8-column runs 32q +
-        // 8sub), then the table lookups of all row blocks, so the wave waits
+        // every LDS read of the step first (B fragments: batch row 16n + rl,
+        // or a loaded row when fewer are loaded; the lane's 8-column runs 32q
+        // + 8sub), then the table lookups of all row blocks, so the wave waits
         // on LDS twice a step
-        const uint32_t xb = rl & uint32_t(4 * XQ - 1);
-        u32x4_t xf[4], nb[NRB], sm[NRB][2];
+        u32x4_t xf[4][NB], nb[NRB], sm[NRB][2];
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-            xf[sub] = lds16(base + kXOff + (xb * 16u + ((4u * q + uint32_t(sub)) ^ (xb & 7u))) * 16u);
+        for (int n = 0; n < NB; ++n) {
+            const uint32_t xb = (16u * uint32_t(n) + rl) & uint32_t(4 * XQ - 1);
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub)
+                xf[sub][n] = lds16(base + kXOff + (xb * 16u + ((4u * q + uint32_t(sub)) ^ (xb & 7u))) * 16u);
+        }
 #pragma unroll
         for (int r = 0; r < NRB; ++r) {
             nb[r] = lds16(base + r * kNibBytes + (rl * 4u + (q ^ ((rl >> 1) & 3u))) * 16u);
@@ -242,7 +250,10 @@ __global__ __launch_bounds__(64 * KW) void skinny_dma_kernel(MatArgs a, MatArgs 
             for (int sub = 0; sub < 4; ++sub) {
                 const bf16x8_t A = __builtin_bit_cast(bf16x8_t, u32x4_t{w[4 * sub], w[4 * sub + 1], w[4 * sub + 2],
                                                                         w[4 * sub + 3]});
-                acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, xf[sub]), acc[r], 0, 0, 0);
+#pragma unroll
+                for (int n = 0; n < NB; ++n)
+                    acc[r][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, xf[sub][n]),
+                                                                        acc[r][n], 0, 0, 0);
             }
         }
         // every read of this slot has returned before it is refilled
@@ -279,48 +290,58 @@ __global__ __launch_bounds__(64 * KW) void skinny_dma_kernel(MatArgs a, MatArgs 
         wait_vm<0>();                                    // no DMA may land after the LDS is reused
     }
 
-    // D layout: lane l holds batch column l%16, rows 4*(l/16)..+3 of a block
-    const uint32_t b = lane & 15u;
-    f32x4_t res[NRB];
+    // D layout: lane l holds batch column l%16 of its tile, rows 4*(l/16)..+3
+    // of a block
+    f32x4_t res[NRB][NB];
     if (KW == 1) {
 #pragma unroll
-        for (int r = 0; r < NRB; ++r) res[r] = acc[r];
+        for (int r = 0; r < NRB; ++r)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) res[r][n] = acc[r][n];
     } else {
         // sum the K-slices in wave order, through the first ring slot
         __syncthreads();
-        f32x4_t* const part = reinterpret_cast<f32x4_t*>(ring0);   // [KW][NRB][64]
+        f32x4_t* const part = reinterpret_cast<f32x4_t*>(ring0);   // [KW][NRB][NB][64]
 #pragma unroll
-        for (int r = 0; r < NRB; ++r) part[(wave * NRB + r) * 64 + int(lane)] = acc[r];
+        for (int r = 0; r < NRB; ++r)
+#pragma unroll
+            for (int n = 0; n < NB; ++n) part[((wave * NRB + r) * NB + n) * 64 + int(lane)] = acc[r][n];
         __syncthreads();
         if (wave != 0) return;
 #pragma unroll
-        for (int r = 0; r < NRB; ++r) {
-            res[r] = part[r * 64 + int(lane)];
+        for (int r = 0; r < NRB; ++r)
 #pragma unroll
-            for (int w_ = 1; w_ < KW; ++w_) res[r] += part[(w_ * NRB + r) * 64 + int(lane)];
-        }
+            for (int n = 0; n < NB; ++n) {
+                res[r][n] = part[(r * NB + n) * 64 + int(lane)];
+#pragma unroll
+                for (int w_ = 1; w_ < KW; ++w_) res[r][n] += part[((w_ * NRB + r) * NB + n) * 64 + int(lane)];
+            }
     }
-    if (b >= B) return;
-    if (DUAL) {
-        const uint32_t rr = row0 + 4u * q;
-        const int64_t o = int64_t(b) * a.R + rr;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (rr + uint32_t(i) < R) {
-                if (a.Y) a.Y[o + i] = res[0][i];
-                if (up.Y) up.Y[o + i] = res[1][i];
-                H[o + i] = uint16_t(f32_to_bf16_rne(silu_mul1(res[0][i], res[1][i])));
+    for (int n = 0; n < NB; ++n) {
+        const uint32_t b = 16u * uint32_t(n) + (lane & 15u);
+        if (b >= B) continue;
+        if (DUAL) {
+            const uint32_t rr = row0 + 4u * q;
+            const int64_t o = int64_t(b) * a.R + rr;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (rr + uint32_t(i) < R) {
+                    if (a.Y) a.Y[o + i] = res[0][n][i];
+                    if (up.Y) up.Y[o + i] = res[1][n][i];
+                    H[o + i] = uint16_t(f32_to_bf16_rne(silu_mul1(res[0][n][i], res[1][n][i])));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < NRB; ++r) {
+                const uint32_t rr = block_row(r) + 4u * q;
+                float* const o = a.Y + int64_t(b) * a.R + rr;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (rr + uint32_t(i) < R) o[i] = res[r][n][i];
             }
         }
-        return;
-    }
-#pragma unroll
-    for (int r = 0; r < NRB; ++r) {
-        const uint32_t rr = block_row(r) + 4u * q;
-        float* const o = a.Y + int64_t(b) * a.R + rr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (rr + uint32_t(i) < R) o[i] = res[r][i];
     }
 }
 
@@ -334,9 +355,10 @@ struct DShape {
 };
 
 // K-split: the smallest (1, 2, 4, 8) that gives at least three waves per
-// compute unit and keeps each slice within kDMaxSlice columns; the K-split,
-// and so the order of every output's sums, depends on the matrix shape only,
-// which makes the gate/up pair bitwise equal to single launches.  Ring depth,
+// compute unit and keeps each slice within kDMaxSlice columns, counted in
+// 16-row blocks: the K-split, and so the order of every output's sums,
+// depends on the matrix shape only, so the gate/up pair is bitwise equal to
+// single launches of this kernel.  Ring depth,
 // as measured on MI355X on the Llama shapes: two steps for the pair (gate/up
 // at batch 6-16: 36.6-38.9 us against 37.5-39.8 with three); for single
 // matrices three steps up to batch 8 (the 14336x4096 gate at batch 5: 19.9
@@ -348,10 +370,11 @@ DShape dma_shape(const MatArgs& a, int rows_per_wg, int slot_bytes, bool dual) {
     const int64_t cus = a.cus > 0 ? a.cus : 256;
     const int64_t steps = a.C / kDStep;
     const int64_t wgs = (a.R + rows_per_wg - 1) / rows_per_wg;
+    const int64_t blocks = (a.R + 15) / 16;
     int kw = env_int("UW_DMA_KW", 0);
     if (kw <= 0) {
         kw = 1;
-        while (kw < 8 && wgs * kw < 3 * cus) kw *= 2;
+        while (kw < 8 && blocks * kw < 3 * cus) kw *= 2;
     }
     kw = kw <= 1 ? 1 : (kw <= 2 ? 2 : (kw <= 4 ? 4 : 8));
     while (kw < 8 && (steps + kw - 1) / kw * kDStep > kDMaxSlice) kw *= 2;
@@ -410,22 +433,23 @@ template <int NRB, bool DUAL>
 hipError_t launch_nrb(const MatArgs& a, const MatArgs& up, uint16_t* h, hipStream_t s) {
     if (a.B <= 4) return launch_xq<NRB, DUAL, 1>(a, up, h, s);
     if (a.B <= 8) return launch_xq<NRB, DUAL, 2>(a, up, h, s);
-    return launch_xq<NRB, DUAL, 4>(a, up, h, s);
+    if (a.B <= 16) return launch_xq<NRB, DUAL, 4>(a, up, h, s);
+    return launch_xq<NRB, DUAL, 8>(a, up, h, s);
 }
 
 }  // namespace
 
-// Taken where the gate/up pair measured faster than on the register-staged
-// skinny kernel on MI355X: from batch 3 on matrices tall enough for one wave
-// per 16-row block and at least three waves per compute unit (K unsplit; the
-// Llama gate/up pair at batch 4: 36.0 against 37.8 us, batch 8: 36.8 against
-// 40.4, batch 16: 39.1 against 46.3).  A single matrix of such a shape takes
-// the same kernel, so that the pair stays bitwise equal to single launches
-// (the 14336x4096 gate alone: 19.6 against 19.3 us at batch 4, 20.3 against
-// 20.6 at 8, 24.9 against 23.4 at 16).  Shorter matrices (the 4096-row down
-// projection: 25.4 against 22.0 us at batch 16) keep the other kernel.
-// UW_SKINNY_DMA=0 / 1 forces it off / on.
-bool skinny_dma_preferred(const MatArgs& a) {
+// The gate/up pair takes this kernel where it measured faster than the two
+// register-staged skinny launches (or that kernel's own pair) on MI355X:
+// batch 3-32 on matrices tall enough for one wave per 16-row block and at
+// least three waves per compute unit (K unsplit; the Llama gate/up pair at
+// batch 4: 36.0 against 37.8 us, batch 16: 39.1 against 46.3, batch 32: 46.6
+// against 54.3 for the separate launches and the SiLU product).  Single
+// matrices keep the register-staged kernel, which is faster for them (the
+// 14336x4096 gate at batch 16: 23.6 against 25.1 us, batch 32: 25.9 against
+// 29.3); UW_SKINNY_DMA=1 forces this kernel for both, UW_SKINNY_DMA=0 for
+// neither.
+bool skinny_dma_pair_preferred(const MatArgs& a) {
     const int mode = env_int("UW_SKINNY_DMA", -1);
     if (mode == 0 || !skinny_dma_supported(a)) return false;
     if (mode > 0) return true;
@@ -433,11 +457,13 @@ bool skinny_dma_preferred(const MatArgs& a) {
     return a.B >= 3 && (a.R + 15) / 16 >= 3 * cus;
 }
 
-// Whole 128-column steps, batch 1..16, every K-slice (split 8 ways at most)
+bool skinny_dma_forced() { return env_int("UW_SKINNY_DMA", -1) > 0; }
+
+// Whole 128-column steps, batch 1..32, every K-slice (split 8 ways at most)
 // within 4096 columns.
 bool skinny_dma_supported(const MatArgs& a) {
     const int64_t steps = a.C / kDStep;
-    return a.B >= 1 && a.B <= 16 && a.C > 0 && a.C % kDStep == 0 && (steps + 7) / 8 * kDStep <= kDMaxSlice &&
+    return a.B >= 1 && a.B <= 32 && a.C > 0 && a.C % kDStep == 0 && (steps + 7) / 8 * kDStep <= kDMaxSlice &&
            a.R > 0;
 }
 

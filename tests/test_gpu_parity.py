@@ -5,6 +5,8 @@ sum |w*x| per output (fp32 accumulation against the fp64 oracle); the
 one-hot activations pin the in-kernel reconstruction bit-exactly.
 Every input comes from the seeded generators in workloads.py.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -295,7 +297,7 @@ def test_skinny_dma_launch_shapes(torch_cuda, monkeypatch, kw, d, nrb):
     monkeypatch.setenv("UW_DMA_D", str(d))
     monkeypatch.setenv("UW_DMA_NRB", str(nrb))
     for R, C, B in [(29, 2048 + 256, 3), (45, 1152, 5), (33, 4096 + 512, 16), (17, 9216, 9), (70, 128, 12),
-                    (1, 640, 1)]:
+                    (1, 640, 1), (40, 1152, 27), (19, 2048 + 128, 32)]:
         print_case(f"skinny dma kw={kw} d={d} nrb={nrb} R={R} C={C} B={B}")
         w = workloads.gaussian_weights(np.random.default_rng(R + C + kw + d), R, C, 0.02, 0.004, 1.0)
         x = _x(C + B + nrb, B, C)
@@ -623,11 +625,23 @@ def _bf16_key(b):
     return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
 
 
+def _dma_pair(R, B):
+    """Whether the library runs the gate/up pair on the LDS-DMA skinny kernel
+    (batch 3-32, at least three 16-row blocks per compute unit; or forced)."""
+    import torch
+    forced = os.environ.get("UW_SKINNY_DMA")
+    if forced in ("0", "1"):
+        return forced == "1" and B >= 3
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return B >= 3 and (R + 15) // 16 >= 3 * cus
+
+
 def _gate_up_case(wg, wu, x, rows=None, what=""):
     """The fused launch against the unfused three calls with the same kernel
-    family (the GEMV at batch 1-2, the skinny MFMA kernel at 3-16; bit for
-    bit) and against the fp64 oracle (g, u within tolerance; h within one
-    bf16 ulp of bf16(SiLU(g)*u) on the GPU's g, u)."""
+    (the GEMV at batch 1-2, the register-staged or the DMA skinny kernel at
+    3-32, whichever the pair takes; bit for bit) and against the fp64 oracle
+    (g, u within tolerance; h within one bf16 ulp of bf16(SiLU(g)*u) on the
+    GPU's g, u)."""
     import torch
     dg, du = uw.compress(wg).to_device(), uw.compress(wu).to_device()
     X = to_dev_bf16(x)
@@ -637,8 +651,17 @@ def _gate_up_case(wg, wu, x, rows=None, what=""):
     h = uw.mlp_gate_up(dg, du, X, g=g, u=u)
     h_only = uw.mlp_gate_up(dg, du, X)                       # no g/u outputs
     kernel = uw.UW_KERNEL_GEMV if B <= 2 else uw.UW_KERNEL_SKINNY
-    g2 = uw.gemm_recon_pal(dg, None, X, kernel=kernel)
-    u2 = uw.gemm_recon_pal(du, None, X, kernel=kernel)
+    saved = os.environ.get("UW_SKINNY_DMA")
+    if _dma_pair(R, B):
+        os.environ["UW_SKINNY_DMA"] = "1"                    # single launches on the pair's kernel
+    try:
+        g2 = uw.gemm_recon_pal(dg, None, X, kernel=kernel)
+        u2 = uw.gemm_recon_pal(du, None, X, kernel=kernel)
+    finally:
+        if saved is None:
+            os.environ.pop("UW_SKINNY_DMA", None)
+        else:
+            os.environ["UW_SKINNY_DMA"] = saved
     h2 = uw.silu_mul_bf16(g2, u2)
     gn, un = g.cpu().numpy(), u.cpu().numpy()
     assert np.array_equal(gn.view(np.uint32), g2.cpu().numpy().view(np.uint32)), what + " g"
@@ -673,13 +696,15 @@ def test_gate_up_fused_small(torch_cuda, monkeypatch, B, dma):
 
 
 @pytest.mark.parametrize("R,C,B", [(1, 64, 1), (37, 1088, 2), (5, 8192, 2), (4100, 1152, 3), (4111, 2176, 16),
-                                   (12300, 1152, 13), (12290, 4096 + 128, 5), (12289, 640, 3)])
+                                   (12300, 1152, 13), (12290, 4096 + 128, 5), (12289, 640, 3), (12301, 1152, 29),
+                                   (12320, 2176, 17)])
 def test_gate_up_fused_ragged(torch_cuda, R, C, B):
     """Rows not a multiple of a workgroup, columns not a multiple of a slab
     (GEMV pair) or of the four K-slices (skinny pair: 9 and 17 steps), one-row
     and one-group matrices, outliers forcing verbatim groups; matrices tall
     enough for the DMA skinny pair, whose 9 and 33 steps leave a step after
-    the two-step ring and whose last row block is partial."""
+    the two-step ring and whose last row block is partial, at batch 3-32
+    (one and two batch tiles)."""
     print_case(f"fused gate/up ragged R={R} C={C} B={B}")
     rng = np.random.default_rng(R * C + B)
     wg = workloads.gaussian_weights(rng, R, C, 0.02, 0.004, 1.0)
@@ -687,12 +712,12 @@ def test_gate_up_fused_ragged(torch_cuda, R, C, B):
     _gate_up_case(wg, wu, _x(R + C, B, C), what=f"R={R} C={C} B={B}")
 
 
-@pytest.mark.parametrize("B", [1, 4, 8, 12, 16])
+@pytest.mark.parametrize("B", [1, 4, 8, 12, 16, 24, 32])
 def test_gate_up_fused_full_size(torch_cuda, B):
     """Llama-3.1-8B gate and up in the benchmark's launches (the GEMV pair at
-    batch 1, the DMA skinny pair at 4, 8, 12 and 16, one, two and four
-    activation row quads): bitwise equal to the unfused calls, sampled rows
-    against the oracle."""
+    batch 1, the DMA skinny pair at 4 to 32: one, two, four and eight
+    activation row quads, one and two batch tiles): bitwise equal to the
+    unfused calls on the same kernel, sampled rows against the oracle."""
     print_case(f"fused gate/up full size B={B}")
     wg, wu = workloads.layer_weight(2, 0, 0), workloads.layer_weight(2, 0, 1)
     rows = np.sort(np.random.default_rng(5).choice(wg.shape[0], 384, replace=False))
@@ -709,7 +734,12 @@ def test_gate_up_fused_rejects(torch_cuda):
     assert ei.value.code == uw.UW_EUNSUPPORTED
     big_g = uw.compress(workloads.layer_weight(3, 1, 0, shape=(4096, 512))).to_device()
     with pytest.raises(uw.UnweightError) as ei:
-        uw.mlp_gate_up(big_g, big_g, to_dev_bf16(_x(1, 17, 512)))  # batch above 16
+        uw.mlp_gate_up(big_g, big_g, to_dev_bf16(_x(1, 17, 512)))  # batch above 16, not tall enough for 17-32
+    assert ei.value.code == uw.UW_EUNSUPPORTED
+    tall = uw.compress(workloads.layer_weight(3, 1, 0, shape=(12288, 256))).to_device()
+    uw.mlp_gate_up(tall, tall, to_dev_bf16(_x(1, 32, 256)))
+    with pytest.raises(uw.UnweightError) as ei:
+        uw.mlp_gate_up(tall, tall, to_dev_bf16(_x(1, 33, 256)))   # batch above 32
     assert ei.value.code == uw.UW_EUNSUPPORTED
     with pytest.raises(uw.UnweightError) as ei:
         uw.mlp_gate_up(dg, do, to_dev_bf16(_x(1, 1, 512)))
