@@ -774,13 +774,50 @@ def workloads_act(workload, m, batch, cols):
     return workloads.layer_activation(workload, 0, m, batch, cols=cols).view(np.int16)
 
 
+def timed_rotation(calls, steps, warmup, stream, min_warm_s=0.1):
+    """us per step of calls[i % len(calls)]() (each a list of launches, or one
+    launch): warmed up for at least `warmup` steps and min_warm_s seconds
+    (after a host phase the clocks ramp for longer than a few steps), then
+    `steps` steps between two events on `stream`."""
+    import torch
+    import mlp_matmul_amd as uw
+    n = len(calls)
+
+    def one(i):
+        c = calls[i % n]
+        for f in (c if isinstance(c, list) else [c]):
+            uw.check(f(), "timed launch")
+    t0, i = time.perf_counter(), 0
+    while i < warmup or time.perf_counter() - t0 < min_warm_s:
+        one(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        one(i)
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def interleaved_pair(a_calls, b_calls, steps, warmup, stream):
+    """(us of a, us of b): each timed twice, interleaved, the faster run of each."""
+    ta = timed_rotation(a_calls, steps, warmup, stream)
+    tb = timed_rotation(b_calls, steps, warmup, stream)
+    return (min(ta, timed_rotation(a_calls, steps, warmup, stream)),
+            min(tb, timed_rotation(b_calls, steps, warmup, stream)))
+
+
 def attention_bench(batches, n_layers=6, steps=30, warmup=4):
     """A second workload on the codec: Llama-3.1-8B attention projections
     (q, o 4096x4096; k, v 1024x4096) of 6 seeded layers.  One step runs the
     four projections of one layer, steps rotate over the layers (495 MB of
     bf16, more than the 256 MiB Infinity Cache).  Direct palette with the
     library's kernel and split choice against the hand-written bf16 kernels
-    (the fastest per shape) and torch.matmul; us per step."""
+    (the fastest per shape); us per step, each side warmed up for at least
+    0.1 s and timed twice, interleaved, keeping the faster run."""
     import ctypes as ct
     import functools
     import torch
@@ -813,20 +850,7 @@ def attention_bench(batches, n_layers=6, steps=30, warmup=4):
                                    choice[n][1], choice[n][2], P(scr), ct.c_uint64(scr.numel()), st) for n in names]
                 for bl in bf]
 
-        def run(calls):
-            for i in range(warmup):
-                for f in calls[i % n_layers]:
-                    uw.check(f(), "attention")
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(steps):
-                for f in calls[i % n_layers]:
-                    uw.check(f(), "attention")
-            e1.record(stream)
-            e1.synchronize()
-            return e0.elapsed_time(e1) / steps * 1e3
-
-        t_d, t_b = run(direct), run(hand)
+        t_d, t_b = interleaved_pair(direct, hand, steps, warmup, stream)
         rows.append({"batch": b, "direct_us": round(t_d, 2), "bf16_us": round(t_b, 2),
                      "speedup_vs_bf16": round(t_b / t_d, 3), "bf16_kernels": {n: choice[n][0] for n in names}})
         log(f"attention q/k/v/o step B={b}: {rows[-1]}")
@@ -839,7 +863,8 @@ def lm_head_bench(batches, copies=2, steps=20, warmup=3):
     """The embedding-sized matmul of the model: the output projection
     (128256 x 4096, 1.05 GB of bf16), one seeded matrix uploaded `copies`
     times and rotated.  Direct palette with the library's kernel choice
-    against the fastest hand-written bf16 kernel."""
+    against the fastest hand-written bf16 kernel, each timed twice,
+    interleaved, after a minimum warm-up (timed_rotation)."""
     import ctypes as ct
     import functools
     import torch
@@ -868,18 +893,7 @@ def lm_head_bench(batches, copies=2, steps=20, warmup=3):
         hand = [functools.partial(L.uw_gemm_bf16, P(W), R, C, P(X), b, P(Y), k, sk, P(scr),
                                   ct.c_uint64(scr.numel()), st) for W in bf]
 
-        def run(calls):
-            for i in range(warmup):
-                uw.check(calls[i % copies](), "lm head")
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(steps):
-                uw.check(calls[i % copies](), "lm head")
-            e1.record(stream)
-            e1.synchronize()
-            return e0.elapsed_time(e1) / steps * 1e3
-
-        t_d, t_b = run(direct), run(hand)
+        t_d, t_b = interleaved_pair(direct, hand, steps, warmup, stream)
         rows.append({"batch": b, "direct_us": round(t_d, 2), "bf16_us": round(t_b, 2), "bf16_kernel": kname,
                      "speedup_vs_bf16": round(t_b / t_d, 3),
                      "compressed_hbm_frac": round(inf.palette_form_bytes / t_d / 1e3 / HBM_PEAK_GBPS, 4)})
