@@ -25,10 +25,15 @@
 // matching activation runs as B fragments: the K order inside an MFMA is a
 // free permutation as long as A and B agree.  All loads of step s+1 (the
 // activation tile, the weight planes, the verbatim exponents) are issued
-// before step s is computed, with no load behind a branch.  The verbatim
-// bitmap words and bases of every tile the workgroup's rows touch are staged
-// in LDS once, so a step's verbatim flag and slot cost LDS reads, not a
-// dependent global load.  Split-K (blockIdx -> K slice) adds workgroups for
+// before step s is computed, with no load behind a branch.  When each lane's
+// row segment of the K-slice spans at most two tiles (slices of at most 4096
+// columns: every split the Llama shapes take at large batch), the verbatim
+// bitmap words and bases of those tiles are loaded into registers once, so a
+// step's verbatim flag and slot are register arithmetic (1.5-5 % faster than
+// the LDS tables at batch 64-256 on MI355X); otherwise the words and bases of
+// every tile the workgroup's rows touch are staged in LDS once, so a step's
+// verbatim flag and slot cost LDS reads, not a dependent global load.
+// Split-K (blockIdx -> K slice) adds workgroups for
 // short matrices; partial tiles go to a scratch array that a second kernel
 // sums in a fixed order (deterministic).  Workgroups are numbered so that the
 // batch tiles of one row band run back to back on one XCD and share its L2.
@@ -72,7 +77,7 @@ struct Step {
 // blocks, or four with four batch blocks and PD = 1, fit two waves per SIMD;
 // deeper prefetch or four row blocks with eight batch blocks take the
 // register file of one wave per SIMD.
-template <int SRC, int NB, int PD, int RBW, int WPG>
+template <int SRC, int NB, int PD, int RBW, int WPG, bool REGTAB = false>
 __global__ __launch_bounds__(64 * WPG, (RBW == 2 || (NB <= 4 && PD == 1)) ? 2 : 1)
 void mfma_kernel(MatArgs a, int tiles_n, int split) {
     constexpr int kRBW = RBW;
@@ -113,7 +118,7 @@ void mfma_kernel(MatArgs a, int tiles_n, int split) {
     const uint32_t t_base = (band0 * C) >> 12;
     uint64_t* tword = reinterpret_cast<uint64_t*>(tabs);
     uint32_t nt = 0;
-    if (SRC == SRC_PAL) {
+    if (SRC == SRC_PAL && !REGTAB) {
         const uint32_t last_row = min(band0 + kMT, R) - 1u;
         nt = ((last_row * C + C - 1u) >> 12) - t_base + 1u;
     }
@@ -151,17 +156,44 @@ void mfma_kernel(MatArgs a, int tiles_n, int split) {
             }
         }
     };
+    // REGTAB: a lane's row segment of the K-slice spans at most two tiles,
+    // whose bitmap words and bases stay in registers (no LDS read per step;
+    // a workgroup without steps reads its rows' first tile)
+    uint32_t rt0[kRBW], rvb0[kRBW], rvb1[kRBW];
+    uint64_t rw0[kRBW], rw1[kRBW];
+    if (SRC == SRC_PAL && REGTAB) {
+        const uint32_t sa = s_lo < s_hi ? s_lo : 0u, sb = s_lo < s_hi ? s_hi : 1u;
+#pragma unroll
+        for (int rb = 0; rb < kRBW; ++rb) {
+            const uint32_t p0 = rowc[rb] * C + sa * kKS, p1 = rowc[rb] * C + sb * kKS - 1u;
+            rt0[rb] = p0 >> 12;
+            rw0[rb] = a.bitmap[rt0[rb]];
+            rvb0[rb] = a.tile_vbase[rt0[rb]];
+            rw1[rb] = a.bitmap[p1 >> 12];
+            rvb1[rb] = a.tile_vbase[p1 >> 12];
+        }
+    }
     auto issue_v = [&](uint32_t s, Step<SRC, NB, RBW, WPG>& st) {
         if (SRC != SRC_PAL) return;
         const uint32_t k0 = s * kKS;
 #pragma unroll
         for (int rb = 0; rb < kRBW; ++rb) {
             const uint32_t pos = rowc[rb] * C + k0 + 16u * q;
-            const uint32_t g = pos >> 6, tl = (g >> 6) - t_base, bit = g & 63u;
-            const uint64_t word = tword[tl];
+            const uint32_t g = pos >> 6, bit = g & 63u;
+            uint64_t word;
+            uint32_t vbase;
+            if (REGTAB) {
+                const bool second = (pos >> 12) != rt0[rb];
+                word = second ? rw1[rb] : rw0[rb];
+                vbase = second ? rvb1[rb] : rvb0[rb];
+            } else {
+                const uint32_t tl = (g >> 6) - t_base;
+                word = tword[tl];
+                vbase = tbase[tl];
+            }
             AStep<SRC>& f = st.r[rb];
             f.verb = uint32_t(word >> bit) & 1u;
-            const uint32_t slot = verbatim_slot(word, bit, tbase[tl]);
+            const uint32_t slot = verbatim_slot(word, bit, vbase);
             // lanes outside verbatim groups all read one shared line
             f.vx = load16(vb_ptr + (f.verb ? slot * 64u + (pos & 63u) : 0u));
         }
@@ -328,12 +360,20 @@ size_t table_bytes(const MatArgs& a) {
     return size_t(nt) * 12;
 }
 
+int env_int(const char* name, int dflt);
+
 template <int SRC, int NB, int PD, int RBW, int WPG>
 hipError_t launch_cfg(const MatArgs& a, hipStream_t s) {
     constexpr int NT = NB * 16, kMT = WPG * 16 * RBW;
-    const size_t lds = SRC == SRC_PAL ? table_bytes(a) : 0;
     const int tiles_m = int((a.R + kMT - 1) / kMT), tiles_n = int((a.B + NT - 1) / NT);
     const int64_t grid = int64_t(tiles_m) * tiles_n * a.split_k;
+    const int64_t slice = (a.C / kKS + a.split_k - 1) / a.split_k * kKS;
+    if (SRC == SRC_PAL && slice <= 4096 && env_int("UW_MFMA_REGTAB", 1)) {   // UW_MFMA_REGTAB=0: LDS tables
+        launch_timed(mfma_kernel<SRC, NB, PD, RBW, WPG, true>, dim3(unsigned(grid)), dim3(64 * WPG), 0, s, a,
+                     tiles_n, int(a.split_k));
+        return hipGetLastError();
+    }
+    const size_t lds = SRC == SRC_PAL ? table_bytes(a) : 0;
     launch_timed(mfma_kernel<SRC, NB, PD, RBW, WPG>, dim3(unsigned(grid)), dim3(64 * WPG), lds, s, a, tiles_n,
                  int(a.split_k));
     return hipGetLastError();

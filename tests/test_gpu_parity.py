@@ -226,6 +226,37 @@ def test_mfma_small_workload(torch_cuda, B):
         assert_matmul_close(Y.cpu().numpy(), w, x, what=f"mfma {name} B={B}")
 
 
+@pytest.mark.parametrize("R,C,B,split", [(300, 8192, 70, 1), (300, 8192, 70, 2), (129, 4096 + 1024, 40, 1),
+                                         (257, 12288, 130, 4), (64, 2048, 17, 1), (96, 2048, 33, 2)])
+def test_mfma_verbatim_tables_in_registers_and_lds(torch_cuda, monkeypatch, R, C, B, split):
+    """The tiled kernel's two ways to find verbatim groups: bitmap words kept
+    in registers (K-slices of at most 4096 columns) and the band's tables
+    staged in LDS (forced with UW_MFMA_REGTAB=0, and the only way for longer
+    slices): bit-identical to each other and within tolerance of the oracle,
+    on row segments that straddle tiles and a matrix whose groups are mostly
+    verbatim."""
+    print_case(f"mfma verbatim tables R={R} C={C} B={B} split={split}")
+    rng = np.random.default_rng(R + C + B + split)
+    if R == 96:
+        wide = np.repeat(rng.random((R, C // 64)) < 0.85, 64, axis=1)
+        scale = np.where(wide, np.exp2(rng.integers(-12, 13, (R, C))), 1.0)
+        w = workloads.f32_to_bf16_bits((rng.standard_normal((R, C)) * 0.02 * scale).astype(np.float32))
+    else:
+        w = workloads.gaussian_weights(rng, R, C, 0.02, 0.004, 1.0)
+    x = _x(C + B, B, C)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    import torch
+    scr = torch.empty(split * 4 * B * R + 256, dtype=torch.uint8, device="cuda")
+    outs = []
+    for regtab in ("1", "0"):
+        monkeypatch.setenv("UW_MFMA_REGTAB", regtab)
+        outs.append(uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_MFMA, split_k=split,
+                                      scratch=scr).cpu().numpy())
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert_matmul_close(outs[0], w, x, what=f"mfma R={R} C={C} B={B} split={split}")
+
+
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 31, 33, 48, 64, 65, 100])
 def test_skinny_small_workload(torch_cuda, B):
     print_case(f"skinny small workload B={B}")
