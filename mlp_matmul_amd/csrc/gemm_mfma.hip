@@ -11,19 +11,26 @@
 //
 // Mapping to CDNA4 (the page's Hopper producer/consumer TMA + WGMMA design is
 // not used).  Y^T = W . X^T is a tall-skinny product (rows up to 14336, batch
-// up to a few hundred), so the tiling is set by two budgets:
+// up to a few hundred), so the tiling is set by three budgets:
 //   * LDS bandwidth: the activation (B) fragments come from LDS, and each one
-//     feeds one v_mfma_f32_16x16x32_bf16 per 16-row block a wave owns; with
-//     four row blocks per wave the B reads stay at ~64 B/clk per CU at the
-//     full MFMA rate (half the LDS bandwidth);
+//     feeds one v_mfma_f32_16x16x32_bf16 per 16-row block a wave owns (1 KB
+//     per fragment: one row block per wave needs twice the LDS bandwidth of
+//     the full MFMA rate, two row blocks exactly the LDS bandwidth);
+//   * waves: a band of rows is one workgroup per batch tile, and the waves
+//     of one workgroup meet at a barrier every step, so a compute unit needs
+//     two waves per SIMD to overlap one wave's loads and rebuild with
+//     another's MFMAs; at batch 64-256 the Llama shapes have about one
+//     128-row band per compute unit, which one row block per wave (8 waves
+//     to a 128-row band) fills where two row blocks (4 waves) did not;
 //   * registers: the weights (A) are rebuilt straight into A-operand
 //     registers from the compressed planes (no LDS round trip, no
 //     redundancy: every wave owns distinct rows), double-buffered.
-// A workgroup is 4 waves x 64 rows = 256 rows by NB*16 batch columns; a step
-// covers 64 columns of K.  Lane l holds 16 consecutive weights of row l%16 of
-// each of its row blocks (columns 16*(l/16)..+16 of the step) and the
-// matching activation runs as B fragments: the K order inside an MFMA is a
-// free permutation as long as A and B agree.  All loads of step s+1 (the
+// A workgroup is WPG (4 or 8) waves x RBW (1 or 2) 16-row blocks by NB*16
+// batch columns; a step covers 64 columns of K.  Lane l holds 16
+// consecutive weights of row l%16 of each of its row blocks (columns
+// 16*(l/16)..+16 of the step) and the matching activation runs as B
+// fragments: the K order inside an MFMA is a free permutation as long as A
+// and B agree.  All loads of step s+1 (the
 // activation tile, the weight planes, the verbatim exponents) are issued
 // before step s is computed, with no load behind a branch.  When each lane's
 // row segment of the K-slice spans at most two tiles (slices of at most 4096
@@ -69,16 +76,13 @@ struct Step {
 };
 
 // WPG waves per workgroup, each with RBW 16-row blocks (WPG*16*RBW rows per
-// workgroup).  Two row blocks per wave keep two waves per SIMD, so one
-// wave's rebuild overlaps another's MFMAs; with four waves per workgroup
-// those are waves of two independent workgroups, whose barriers and LDS
-// waits do not line up.  PD steps of loads are kept in flight ahead of the
-// step being computed (PD + 1 register sets).  Register budget: two row
-// blocks, or four with four batch blocks and PD = 1, fit two waves per SIMD;
-// deeper prefetch or four row blocks with eight batch blocks take the
-// register file of one wave per SIMD.
+// workgroup).  PD steps of loads are kept in flight ahead of the step being
+// computed (PD + 1 register sets).  Register budget: one or two row blocks,
+// or four with four batch blocks and PD = 1, fit two waves per SIMD; deeper
+// prefetch or four row blocks with eight batch blocks take the register file
+// of one wave per SIMD.
 template <int SRC, int NB, int PD, int RBW, int WPG, bool REGTAB = false>
-__global__ __launch_bounds__(64 * WPG, (RBW == 2 || (NB <= 4 && PD == 1)) ? 2 : 1)
+__global__ __launch_bounds__(64 * WPG, (RBW <= 2 || (NB <= 4 && PD == 1)) ? 2 : 1)
 void mfma_kernel(MatArgs a, int tiles_n, int split) {
     constexpr int kRBW = RBW;
     constexpr int kMT = WPG * 16 * RBW;                // rows per workgroup
@@ -384,25 +388,43 @@ int env_int(const char* name, int dflt) {
     return e && *e ? atoi(e) : dflt;
 }
 
-// Batch blocks per workgroup (4 up to batch 64, else 8), row blocks per
-// wave (2), waves per workgroup (8 above batch 128 for matrices under 8192
-// rows, else 4) and prefetch depth (3 for the 4-block tiles of the
-// rebuilding sources, else 1), as measured on the Llama MLP shapes at batch
-// 32-256; UW_MFMA_NB / _RBW / _WPG / _PD override for tuning.  Combinations
-// that do not fit the register file are never instantiated.
+// Batch blocks per workgroup (4 up to batch 64, else 8); row blocks per
+// wave (1, or 2 above batch 128 on matrices under 8192 rows); waves per
+// workgroup (8 above batch 128, and above batch 64 on matrices under 8192
+// rows, else 4); prefetch depth (2 for one row block and 4 waves, 3 for the
+// 4-block batch tiles of the rebuilding sources with two row blocks, else
+// 1).  Measured on the Llama MLP shapes at batch 64-256 on MI355X: one row
+// block per wave gives a band twice the waves, so a compute unit runs two
+// waves per SIMD where two row blocks left it one; the gate shape
+// (14336 x 4096, palette source) at batch 64 / 128 / 256 took 31.4 / 44.9 /
+// 64.6 us against 35.5 / 47.1 / 73.0 us with two row blocks per wave, and the
+// bf16 source gained alike.  UW_MFMA_NB / _RBW / _WPG / _PD override for
+// tuning.  Combinations that do not fit the register file are never
+// instantiated.
 struct Tiling {
     int nb, rbw, wpg;
 };
 Tiling tiling_of(const MatArgs& a) {
-    return {env_int("UW_MFMA_NB", a.B <= 64 ? 4 : 8), env_int("UW_MFMA_RBW", 2),
-            env_int("UW_MFMA_WPG", a.B > 128 && a.R < 8192 ? 8 : 4)};
+    const bool tall = a.R >= 8192;
+    const int nb = a.B <= 64 ? 4 : 8;
+    const int rbw = a.B > 128 && !tall ? 2 : 1;
+    const int wpg = a.B > 128 || (a.B > 64 && !tall) ? 8 : 4;
+    return {env_int("UW_MFMA_NB", nb), env_int("UW_MFMA_RBW", rbw), env_int("UW_MFMA_WPG", wpg)};
 }
 
 template <int SRC>
 hipError_t launch_src(const MatArgs& a, hipStream_t s) {
     const Tiling tl = tiling_of(a);
     const int nb = tl.nb, rbw = tl.rbw, wpg = tl.wpg;
-    const int pd = env_int("UW_MFMA_PD", nb <= 4 && SRC != SRC_BF16 ? 3 : 1);
+    const int pd = env_int("UW_MFMA_PD", rbw <= 1 ? (wpg <= 4 ? 2 : 1) : nb <= 4 && SRC != SRC_BF16 ? 3 : 1);
+    if (rbw <= 1) {
+        if (wpg <= 4) {
+            if (nb <= 4) return pd <= 1 ? launch_cfg<SRC, 4, 1, 1, 4>(a, s) : launch_cfg<SRC, 4, 2, 1, 4>(a, s);
+            return pd <= 1 ? launch_cfg<SRC, 8, 1, 1, 4>(a, s) : launch_cfg<SRC, 8, 2, 1, 4>(a, s);
+        }
+        if (nb <= 4) return pd <= 1 ? launch_cfg<SRC, 4, 1, 1, 8>(a, s) : launch_cfg<SRC, 4, 2, 1, 8>(a, s);
+        return pd <= 1 ? launch_cfg<SRC, 8, 1, 1, 8>(a, s) : launch_cfg<SRC, 8, 2, 1, 8>(a, s);
+    }
     if (rbw <= 2) {
         if (wpg <= 4) {
             if (nb <= 4) {
@@ -439,7 +461,7 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
 int mfma_default_split(const MatArgs& a, int cus) {
     if (a.R <= 0 || a.B <= 0 || a.C <= 0) return 1;
     const Tiling tl = tiling_of(a);
-    const int64_t mt = 16 * int64_t(tl.rbw <= 2 ? 2 : 4) * (tl.wpg <= 4 ? 4 : 8);
+    const int64_t mt = 16 * int64_t(tl.rbw <= 1 ? 1 : tl.rbw <= 2 ? 2 : 4) * (tl.wpg <= 4 ? 4 : 8);
     const int64_t nt = 16 * int64_t(tl.nb <= 4 ? 4 : 8);
     const int64_t tiles = ((a.R + mt - 1) / mt) * ((a.B + nt - 1) / nt);
     const int64_t steps = a.C / kKS;

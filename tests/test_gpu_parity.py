@@ -257,6 +257,47 @@ def test_mfma_verbatim_tables_in_registers_and_lds(torch_cuda, monkeypatch, R, C
     assert_matmul_close(outs[0], w, x, what=f"mfma R={R} C={C} B={B} split={split}")
 
 
+# every (row blocks per wave, waves per workgroup, batch blocks, prefetch
+# depth) the tiled kernel is instantiated with (tuning overrides UW_MFMA_RBW /
+# _WPG / _NB / _PD)
+_MFMA_TILINGS = [(1, 4, 4, 1), (1, 4, 4, 2), (1, 4, 8, 1), (1, 4, 8, 2), (1, 8, 4, 1), (1, 8, 4, 2),
+                 (1, 8, 8, 1), (1, 8, 8, 2), (2, 4, 4, 1), (2, 4, 4, 3), (2, 4, 8, 2), (2, 8, 4, 2),
+                 (2, 8, 8, 1), (4, 4, 4, 3), (4, 4, 8, 1)]
+
+
+@pytest.mark.parametrize("rbw,wpg,nb,pd", _MFMA_TILINGS)
+def test_mfma_tilings(torch_cuda, monkeypatch, rbw, wpg, nb, pd):
+    """Each tiling of the tiled kernel gives the same bits as the default one
+    for the same split (the tiling moves rows and batch columns between
+    waves and workgroups, never the order of a sum), on bands past R, batch
+    tiles past B and K-slices whose row segments straddle tiles; the palette
+    source is also checked against the oracle."""
+    print_case(f"mfma tiling rbw={rbw} wpg={wpg} nb={nb} pd={pd}")
+    import torch
+    R, C, B, split = 300, 4096 + 1024, 70, 2
+    w = workloads.gaussian_weights(np.random.default_rng(R + C + B), R, C, 0.02, 0.004, 1.0)
+    x = _x(C + B + 1, B, C)
+    dm = uw.compress(w).to_device()
+    X = to_dev_bf16(x)
+    W = to_dev_bf16(w)
+    exps = uw.decode_exponents(dm)
+    scr = torch.empty(split * 4 * B * R + 256, dtype=torch.uint8, device="cuda")
+
+    def run():
+        return [f(X).cpu().numpy().view(np.uint32) for f in (
+            lambda X: uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_MFMA, split_k=split, scratch=scr),
+            lambda X: uw.gemm_bf16(W, X, kernel=uw.UW_KERNEL_MFMA, split_k=split, scratch=scr),
+            lambda X: uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_MFMA, split_k=split, scratch=scr))]
+
+    ref = run()
+    for k, v in (("UW_MFMA_RBW", rbw), ("UW_MFMA_WPG", wpg), ("UW_MFMA_NB", nb), ("UW_MFMA_PD", pd)):
+        monkeypatch.setenv(k, str(v))
+    got = run()
+    for name, a, b in zip(("direct", "bf16", "exp"), got, ref):
+        assert np.array_equal(a, b), name
+    assert_matmul_close(got[0].view(np.float32), w, x, what=f"mfma tiling {rbw}/{wpg}/{nb}/{pd}")
+
+
 @pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 7, 8, 9, 16, 17, 31, 33, 48, 64, 65, 100])
 def test_skinny_small_workload(torch_cuda, B):
     print_case(f"skinny small workload B={B}")
