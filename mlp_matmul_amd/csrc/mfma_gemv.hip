@@ -297,13 +297,10 @@ __global__ __launch_bounds__(64 * KW * (DUAL ? 2 : 1)) void mfma_gemv_kernel(Mat
                         const uint32_t nbyte = (wl[r][0][2 * h + (p >> 2)] >> (8 * (p & 3))) & 0xFFu;
                         e7[p] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lutm) + (nbyte << 2));
                     }
-                    if (__builtin_amdgcn_ballot_w64(st.verb[r] != 0)) {   // rare: raw exponents for verbatim lanes
+                    if (st.verb[r]) {   // a verbatim lane: raw exponents, under its own exec mask
 #pragma unroll
-                        for (int p = 0; p < 8; ++p) {
-                            const uint32_t er =
-                                (p & 1) ? exp_pair<1>(st.vx[r][h][p >> 1]) : exp_pair<0>(st.vx[r][h][p >> 1]);
-                            e7[p] = st.verb[r] ? er : e7[p];
-                        }
+                        for (int p = 0; p < 8; ++p)
+                            e7[p] = (p & 1) ? exp_pair<1>(st.vx[r][h][p >> 1]) : exp_pair<0>(st.vx[r][h][p >> 1]);
                     }
                     join8(sml[r][h], e7, w + 8 * h);
                 }

@@ -229,18 +229,19 @@ __global__ __launch_bounds__(64 * KW) void skinny_dma_kernel(MatArgs a, MatArgs 
                 e7[r][p] = *reinterpret_cast<const uint32_t*>(lutm + (nbyte << 2));
             }
         }
-        uint32_t any_verb = 0;
+        // a lane's 32 weights of a row block lie in one group: a verbatim
+        // lane takes all of them from its raw exponents, under its own exec
+        // mask (two instructions a pair, and none when no lane of the wave
+        // is verbatim in that block)
 #pragma unroll
-        for (int r = 0; r < NRB; ++r) any_verb |= v.verb[r];
-        if (__builtin_amdgcn_ballot_w64(any_verb != 0)) {    // rare: raw exponents for verbatim lanes
-#pragma unroll
-            for (int r = 0; r < NRB; ++r)
+        for (int r = 0; r < NRB; ++r) {
+            if (v.verb[r]) {
 #pragma unroll
                 for (int p = 0; p < 16; ++p) {
                     const uint32_t d = v.vx[r][p >> 3][(p & 7) >> 1];
-                    const uint32_t er = (p & 1) ? exp_pair<1>(d) : exp_pair<0>(d);
-                    e7[r][p] = v.verb[r] ? er : e7[r][p];
+                    e7[r][p] = (p & 1) ? exp_pair<1>(d) : exp_pair<0>(d);
                 }
+            }
         }
 #pragma unroll
         for (int r = 0; r < NRB; ++r) {
