@@ -69,7 +69,8 @@ def parse(argv=None):
     p.add_argument("--extras", action="store_true",
                    help="also the one-layer pipelines, per-row-sigma matrices, shard shapes, attention and output "
                         "projection (into the detail file)")
-    p.add_argument("--detail", default=os.path.join(ROOT, "gpurun_out", "bench_detail.json"))
+    p.add_argument("--detail", default=os.path.join(ROOT, "bench_out", "bench_detail.json"),
+                   help="JSON file for the sweep, per-launch rows and the other legs (the printed line stays compact)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also launch a plain device copy of known size (for counter calibration)")
     return p.parse_args(argv)

@@ -55,7 +55,7 @@ def test_headline_line_stays_compact():
                                    "SiLU, 33 reps/6.1 s; codec 1 thread, BLAS 16",
                          "stages_GBps": {f"c{i}": [0.0123, 0.0321, 0.0321, 0.0321, 0.123, 1.23] for i in range(1, 6)},
                          "stage_order": ",".join(bench.CPU_STAGES), "seconds": 31.2},
-        "detail": "gpurun_out/bench_detail.json",
+        "detail": "bench_out/bench_detail.json",
     }
     import json
     assert len(json.dumps(line, separators=(",", ":"), ensure_ascii=False).encode()) < 2000
