@@ -35,6 +35,7 @@
 //   exponent source: v_perm spreads two exponent bytes into place.
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -68,7 +69,7 @@ struct Chunk {
 // the up matrix (up), over the same staged activations; the second group's
 // epilogue writes h[b][r] = bf16(SiLU(g) * u), and g and u themselves when
 // a.Y / up.Y are not null.
-template <int SRC, int MB, int NRW, bool EXACT, bool XLDS, bool DUAL, int DEPTH>
+template <int SRC, int MB, int NRW, bool EXACT, bool XLDS, bool DUAL, int DEPTH, int XPC = 0>
 __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16_t* H) {
     __shared__ uint32_t lut[DUAL ? 512 : 256];                   // nibble pair -> exponents in place
     extern __shared__ uint32_t lds[];
@@ -227,13 +228,31 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16
     auto next = [&](Item it) { return it.s + 1 == iters ? Item{it.g + 1, 0} : Item{it.g, it.s + 1}; };
     Chunk<SRC, MB> sets[DEPTH + 1][NRW];
     const Item it0{0, 0};
-    // item 0's weight loads go out first; the verbatim tables of every tile
-    // the wave's rows touch (one per lane) follow, then item 0's verbatim
-    // loads, then the activations are staged.  (Issuing item 1 here as well,
-    // ahead of the staging, measured slower.)
-    if (live) {
-        issue_x(it0, sets[0]);
-        issue_w(it0, sets[0]);
+    // XPC > 0 (XLDS): the activation rows, at most XPC pieces of 16 bytes a
+    // thread, and the verbatim tables of every tile the wave's rows touch
+    // (one per lane) are loaded before item 0's weight loads; the waits
+    // before the pieces are stored and before item 0's verbatim addresses
+    // then cover only them, so the staging runs beside the start of the
+    // weight stream.  (Without staging: weights, tables, verbatim.)  Every
+    // thread loads all XPC pieces (past the end: the last one again, not
+    // stored), so no load sits behind a branch.  (Issuing item 1 here as
+    // well, ahead of the staging, measured slower.)
+    constexpr int kXP = XLDS ? XPC : 0;
+    const int64_t n16 = int64_t(B) * C / 8;
+    u32x4_t xv[kXP > 0 ? kXP : 1];
+    auto stage_load = [&]() {
+#pragma unroll
+        for (int u = 0; u < kXP; ++u) xv[u] = load16(a.X + min(int64_t(tid) + 256 * u, n16 - 1) * 8);
+    };
+    auto stage_store = [&]() {
+        // a use of every piece keeps each load out of its store's branch
+#pragma unroll
+        for (int u = 0; u < kXP; ++u) asm volatile("" ::"v"(xv[u]));
+#pragma unroll
+        for (int u = 0; u < kXP; ++u)
+            if (int64_t(tid) + 256 * u < n16) reinterpret_cast<u32x4_t*>(xs)[tid + 256 * u] = xv[u];
+    };
+    auto load_tables = [&]() {
         if (SRC == SRC_PAL) {
             const int64_t t_end = max(((rl0 + wrows) * C + 4095) >> 12, t_first + 1);
             const int64_t tl = min(t_first + lane, t_end - 1);
@@ -244,14 +263,30 @@ __global__ __launch_bounds__(256) void gemv_kernel(MatArgs a, MatArgs up, uint16
                 my_vbase1 = up.tile_vbase[tl];
             }
         }
+    };
+    if (live && kXP > 0) {
+        // staging, tables, then the weights: the waits of the stores and of
+        // the verbatim addresses cover the loads issued before the weights
+        stage_load();
+        load_tables();
+        issue_x(it0, sets[0]);
+        issue_w(it0, sets[0]);
+        stage_store();
         issue_v(it0, sets[0]);
+    } else if (live) {
+        issue_x(it0, sets[0]);
+        issue_w(it0, sets[0]);
+        load_tables();
+        issue_v(it0, sets[0]);
+    } else if (kXP > 0) {
+        stage_load();
+        stage_store();
     }
-    if (XLDS) {
+    if (XLDS && kXP == 0) {
         // four 16-byte pieces per thread go out before one wait (a load,
         // wait, store loop pays an L2 round trip per piece: seven of them
         // for a 14336-column row); pieces past the end re-read the last one,
         // so no load is conditional, and are not stored
-        const int64_t n16 = int64_t(B) * C / 8;
         for (int64_t i0 = tid; i0 < n16; i0 += 256 * 4) {
             u32x4_t v[4];
 #pragma unroll
@@ -424,6 +459,13 @@ int env_int(const char* name, int dflt) {
     return e ? atoi(e) : dflt;
 }
 
+// 16-byte activation pieces a thread of a 256-thread workgroup stages: 2, 4
+// or 8 (at most kXLdsMax bytes)
+int stage_pieces(const MatArgs& a) {
+    const int64_t np = (a.B * a.C / 8 + 255) / 256;
+    return np <= 2 ? 2 : (np <= 4 ? 4 : 8);
+}
+
 template <int SRC, int MB, int NRW, bool XLDS>
 void launch_cfg(const MatArgs& a0, hipStream_t s) {
     // row groups per wave: long-lived waves amortise the per-wave start (tables,
@@ -447,10 +489,27 @@ void launch_cfg(const MatArgs& a0, hipStream_t s) {
     uint16_t* const no_h = nullptr;
     if (depth >= 2 && MB <= 2) {
         constexpr int D = MB <= 2 ? 2 : 1;
-        if (a.C % kSlab == 0)
-            launch_timed(gemv_kernel<SRC, MB, NRW, true, XLDS, false, D>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
-        else
-            launch_timed(gemv_kernel<SRC, MB, NRW, false, XLDS, false, D>, dim3(grid), dim3(256), lds, s, a, MatArgs{}, no_h);
+        const int xp = XLDS ? stage_pieces(a) : 0;
+        auto go = [&](auto E, auto P) {
+            launch_timed(gemv_kernel<SRC, MB, NRW, decltype(E)::value, XLDS, false, D, decltype(P)::value>, dim3(grid),
+                         dim3(256), lds, s, a, MatArgs{}, no_h);
+        };
+        using T = std::true_type;
+        using F = std::false_type;
+        using P0 = std::integral_constant<int, 0>;
+        using P2 = std::integral_constant<int, 2>;
+        using P4 = std::integral_constant<int, 4>;
+        using P8 = std::integral_constant<int, 8>;
+        const bool ex = a.C % kSlab == 0;
+        if (!XLDS) {
+            if (ex) go(T{}, P0{}); else go(F{}, P0{});
+        } else if (xp <= 2) {
+            if (ex) go(T{}, P2{}); else go(F{}, P2{});
+        } else if (xp <= 4) {
+            if (ex) go(T{}, P4{}); else go(F{}, P4{});
+        } else {
+            if (ex) go(T{}, P8{}); else go(F{}, P8{});
+        }
         return;
     }
     if (a.C % kSlab == 0)
@@ -508,10 +567,24 @@ void launch_gateup_mb(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream
     static const int depth_env = env_int("UW_GEMV_DEPTH", 0);
     if ((depth_env == 0 || depth_env >= 2) && MB <= 2) {
         constexpr int D = MB <= 2 ? 2 : 1;
-        if (a.C % kSlab == 0)
-            launch_timed(gemv_kernel<SRC_PAL, MB, 1, true, true, true, D>, dim3(grid), dim3(256), lds, s, a, u, h);
-        else
-            launch_timed(gemv_kernel<SRC_PAL, MB, 1, false, true, true, D>, dim3(grid), dim3(256), lds, s, a, u, h);
+        const int xp = stage_pieces(a);
+        auto go = [&](auto E, auto P) {
+            launch_timed(gemv_kernel<SRC_PAL, MB, 1, decltype(E)::value, true, true, D, decltype(P)::value>, dim3(grid),
+                         dim3(256), lds, s, a, u, h);
+        };
+        using T = std::true_type;
+        using F = std::false_type;
+        using P2 = std::integral_constant<int, 2>;
+        using P4 = std::integral_constant<int, 4>;
+        using P8 = std::integral_constant<int, 8>;
+        const bool ex = a.C % kSlab == 0;
+        if (xp <= 2) {
+            if (ex) go(T{}, P2{}); else go(F{}, P2{});
+        } else if (xp <= 4) {
+            if (ex) go(T{}, P4{}); else go(F{}, P4{});
+        } else {
+            if (ex) go(T{}, P8{}); else go(F{}, P8{});
+        }
         return;
     }
     if (a.C % kSlab == 0)
