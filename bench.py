@@ -658,7 +658,7 @@ def kernel_sources(kernel_tag):
     """The source files of the kernels a profile tag names (gemv_*, skinny_*,
     mfma_*, huffman_*); the skinny family has two kernels, one dispatching to
     the other."""
-    return {"gemv": ["gemv.hip"], "skinny": ["mfma_gemv.hip", "skinny_dma.hip"], "mfma": ["gemm_mfma.hip"],
+    return {"gemv": ["gemv.hip"], "skinny": ["mfma_gemv.hip", "skinny_dma.hip"], "mfma": ["gemm_mfma.hip", "gemm_lds.hip"],
             "huffman": ["decode.hip"]}[kernel_tag.split("_")[0]]
 
 

@@ -21,7 +21,7 @@ LIB = os.path.join(HERE, "libunweight.so")
 
 ARCH = "gfx950"
 HOST_SOURCES = ["compress.cpp", "host_misc.cpp"]
-HIP_SOURCES = ["capi.hip", "decode.hip", "gemv.hip", "gemm_mfma.hip", "silu.hip", "timer.hip", "mfma_gemv.hip", "skinny_dma.hip"]
+HIP_SOURCES = ["capi.hip", "decode.hip", "gemv.hip", "gemm_mfma.hip", "gemm_lds.hip", "silu.hip", "timer.hip", "mfma_gemv.hip", "skinny_dma.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 # packed-fp32 instructions stay off: hipcc would otherwise form them from plain float code

@@ -151,9 +151,9 @@ int auto_kernel(int src, const uwk::MatArgs& a) {
 
 // split_k 0: the library's choice, K-slices for the tiled MFMA kernel that
 // fill the chip (1 for the other kernels).
-int resolve_split(const uwk::MatArgs& a, int kernel, int split_k) {
+int resolve_split(int src, const uwk::MatArgs& a, int kernel, int split_k) {
     if (split_k != 0) return split_k;
-    return kernel == UW_KERNEL_MFMA ? uwk::mfma_default_split(a, device_cus()) : 1;
+    return kernel == UW_KERNEL_MFMA ? uwk::mfma_default_split(src, a, device_cus()) : 1;
 }
 
 // Common checks and dispatch of one matmul.
@@ -182,7 +182,7 @@ int run_matmul(int src, const uwk::MatArgs& a0, int kernel, int split_k, void* s
     if (split_k < 0 || split_k > 64) return uw::fail(UW_EINVAL, std::string(who) + ": split_k must be 0..64");
     if (split_k == 0) {
         // the library's choice, as large as the scratch the caller gave allows
-        split_k = resolve_split(a, kernel, 0);
+        split_k = resolve_split(src, a, kernel, 0);
         while (split_k > 1 && (!scratch || !aligned16(scratch) ||
                                scratch_bytes < uint64_t(split_k) * uint64_t(a.B) * uint64_t(a.R) * 4))
             split_k >>= 1;
@@ -459,12 +459,16 @@ int64_t uw_scratch_bytes(int pipeline, int64_t rows, int64_t cols, int64_t batch
         return uw::fail(UW_EINVAL, "uw_scratch_bytes: bad argument");
     if (pipeline == UW_PIPE_HUFF) return int64_t(align256(huff_partial_bytes(rows, cols)));
     if (split_k == 0) {
-        // what split_k 0 resolves to with the kernel UW_KERNEL_AUTO picks
+        // the largest split_k 0 resolves to, over the weight sources, with
+        // the kernel UW_KERNEL_AUTO picks
         uwk::MatArgs a{};
         a.R = rows;
         a.C = cols;
         a.B = batch;
-        split_k = cols % uw::kGroup ? 1 : resolve_split(a, auto_kernel(uwk::SRC_PAL, a), 0);
+        split_k = 1;
+        if (cols % uw::kGroup == 0)
+            for (int src : {uwk::SRC_BF16, uwk::SRC_EXP, uwk::SRC_PAL})
+                split_k = std::max(split_k, resolve_split(src, a, auto_kernel(src, a), 0));
     }
     uint64_t n = align256(decoded_bytes(pipeline, rows, cols));
     if (split_k > 1) n += align256(uint64_t(split_k) * uint64_t(batch) * uint64_t(rows) * 4);

@@ -1,6 +1,7 @@
 // bf16 MFMA matmul on gfx950 for larger batches, over uncompressed weights
-// or with on-chip weight reconstruction (any batch works; it is the kernel
-// family the launcher picks above the skinny kernel's range).
+// or with on-chip weight reconstruction (any batch works; the launcher picks
+// it above the skinny kernel's range through batch 64, and the LDS-tile
+// kernel of gemm_lds.hip above that).
 //
 // Method: Cloudflare, "Unweight: how we compressed an LLM 22% without
 // sacrificing quality", "How the reconstructive matmul works": compressed
@@ -458,8 +459,9 @@ hipError_t launch_src(const MatArgs& a, hipStream_t s) {
 // power of two (at most 8, each slice at least 4 steps) for which tiles x
 // slices reaches three quarters of the CUs (measured on the Llama MLP
 // shapes at batch 32-256, this is the split the autotuner picks).
-int mfma_default_split(const MatArgs& a, int cus) {
+int mfma_default_split(int src, const MatArgs& a, int cus) {
     if (a.R <= 0 || a.B <= 0 || a.C <= 0) return 1;
+    if (lds_gemm_preferred(src, a)) return lds_gemm_default_split(src, a, cus);
     const Tiling tl = tiling_of(a);
     const int64_t mt = 16 * int64_t(tl.rbw <= 1 ? 1 : tl.rbw <= 2 ? 2 : 4) * (tl.wpg <= 4 ? 4 : 8);
     const int64_t nt = 16 * int64_t(tl.nb <= 4 ? 4 : 8);
@@ -485,7 +487,8 @@ hipError_t launch_mfma(int src, const MatArgs& a, hipStream_t s) {
     }
     if (!mfma_supported(a)) return hipErrorNotSupported;
     hipError_t e;
-    switch (src) {
+    if (lds_gemm_preferred(src, a)) e = launch_lds_gemm(src, a, s);
+    else switch (src) {
         case SRC_BF16: e = launch_src<SRC_BF16>(a, s); break;
         case SRC_EXP: e = launch_src<SRC_EXP>(a, s); break;
         default: e = launch_src<SRC_PAL>(a, s); break;

@@ -60,8 +60,14 @@ bool gemv_gateup_supported(const MatArgs& gate, const MatArgs& up);
 hipError_t launch_gemv_gateup(const MatArgs& gate, const MatArgs& up, uint16_t* h, hipStream_t s);
 hipError_t launch_mfma(int src, const MatArgs& a, hipStream_t s);
 bool mfma_supported(const MatArgs& a);
-// Split-K that fills the chip for the tiled MFMA kernel on `cus` compute units.
-int mfma_default_split(const MatArgs& a, int cus);
+// Split-K that fills the chip for the tiled MFMA family on `cus` compute units.
+int mfma_default_split(int src, const MatArgs& a, int cus);
+// The tiled MFMA kernel that rebuilds each weight once per workgroup into a
+// shared LDS tile (batch 64 and up by default; partial sums as launch_mfma).
+bool lds_gemm_supported(int src, const MatArgs& a);
+bool lds_gemm_preferred(int src, const MatArgs& a);
+int lds_gemm_default_split(int src, const MatArgs& a, int cus);
+hipError_t launch_lds_gemm(int src, const MatArgs& a, hipStream_t s);
 hipError_t launch_mfma_gemv(int src, const MatArgs& a, hipStream_t s);
 bool mfma_gemv_supported(const MatArgs& a);
 // Fused gate/up on the skinny MFMA kernel with the SiLU product (palette

@@ -89,9 +89,11 @@ def test_decoders_check_descriptors_before_launch():
 
 
 def test_scratch_for_library_split_choice():
-    """split_k 0 sizes scratch for the split the library would pick: none for
-    the GEMV batches, eight K-slices for a 4096x14336 matrix at batch 256
-    (the CU count falls back to 256 without a device)."""
+    """split_k 0 sizes scratch for the largest split the library would pick
+    over the weight sources: none for the GEMV batches; at batch 256 a
+    4096x14336 matrix has 32 tiles of 128 rows x 256 columns (eight
+    K-slices) and a 14336x4096 one 224 of 128 x 128 (none), the CU count
+    falling back to 256 without a device."""
     L = uw.lib()
     P = _capi.UW_PIPE_DIRECT
     assert L.uw_scratch_bytes(P, 4096, 14336, 1, 0) == 0

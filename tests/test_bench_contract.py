@@ -69,7 +69,7 @@ def test_committed_profiles_match_the_kernel_sources(name):
     txt = open(os.path.join(ROOT, "profiles", name + ".md")).read()
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", txt)
     assert m, "profile without a source hash"
-    src_files = {"gemv": ["gemv.hip"], "skinny": ["mfma_gemv.hip", "skinny_dma.hip"], "mfma": ["gemm_mfma.hip"],
+    src_files = {"gemv": ["gemv.hip"], "skinny": ["mfma_gemv.hip", "skinny_dma.hip"], "mfma": ["gemm_mfma.hip", "gemm_lds.hip"],
                  "huffman": ["decode.hip"]}[name.split("_")[0]]
     csrc = os.path.join(ROOT, "mlp_matmul_amd", "csrc")
     src = b"".join(open(os.path.join(csrc, f), "rb").read() for f in src_files)

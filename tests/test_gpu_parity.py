@@ -249,6 +249,7 @@ def test_mfma_verbatim_tables_in_registers_and_lds(torch_cuda, monkeypatch, R, C
     import torch
     scr = torch.empty(split * 4 * B * R + 256, dtype=torch.uint8, device="cuda")
     outs = []
+    monkeypatch.setenv("UW_MFMA_LDS", "0")       # the register-rebuilding tiled kernel
     for regtab in ("1", "0"):
         monkeypatch.setenv("UW_MFMA_REGTAB", regtab)
         outs.append(uw.gemm_recon_pal(dm, None, X, kernel=uw.UW_KERNEL_MFMA, split_k=split,
@@ -289,6 +290,7 @@ def test_mfma_tilings(torch_cuda, monkeypatch, rbw, wpg, nb, pd):
             lambda X: uw.gemm_bf16(W, X, kernel=uw.UW_KERNEL_MFMA, split_k=split, scratch=scr),
             lambda X: uw.gemm_recon_exp(dm, exps, X, kernel=uw.UW_KERNEL_MFMA, split_k=split, scratch=scr))]
 
+    monkeypatch.setenv("UW_MFMA_LDS", "0")       # the register-rebuilding tiled kernel
     ref = run()
     for k, v in (("UW_MFMA_RBW", rbw), ("UW_MFMA_WPG", wpg), ("UW_MFMA_NB", nb), ("UW_MFMA_PD", pd)):
         monkeypatch.setenv(k, str(v))
