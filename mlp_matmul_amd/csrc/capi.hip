@@ -559,11 +559,13 @@ int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, in
         e = uwk::launch_gemv_gateup(g, u, h, as_stream(stream));
     else if (small && uwk::mfma_gemv_gateup_supported(g, u))
         e = uwk::launch_mfma_gemv_gateup(g, u, h, as_stream(stream));
+    else if (uwk::lds_gateup_supported(g, u))
+        e = uwk::launch_lds_gateup(g, u, h, as_stream(stream));
     else
         return uw::fail(UW_EUNSUPPORTED, std::string(who) +
                                              ": needs batch 1..16, cols % 128 == 0, cols <= 32768 and a K-split of at "
                                              "most 4 for the shape (batch 1-2: or batch*cols*2 <= 32768; batch 17-32: "
-                                             "at least 48 rows per compute unit)");
+                                             "at least 48 rows per compute unit), or batch above 128");
     return e == hipSuccess ? UW_OK : hip_fail(e, who);
 }
 

@@ -66,32 +66,42 @@ struct LItem {
     uint32_t verb;    // PAL
 };
 
-template <int MT, int NT, int NW>
+template <int MT, int NT, int NW, int NMAT>
 struct LStage {
-    LItem w[MT / (16 * NW)];
+    LItem w[NMAT][MT / (16 * NW)];
     u32x4_t x[NT / (8 * NW)];
 };
 
 // MT rows x NT batch columns per workgroup of NW waves, laid out WGM x (NW /
-// WGM) over the tile; P steps of loads in flight.
-template <int SRC, int MT, int NT, int NW, int WGM, int P>
+// WGM) over the tile; P steps of loads in flight.  DUAL: the gate/up pair of
+// an MLP block (`a` gate, `up` up, same shape, palette sources, no K split):
+// each step rebuilds the band's rows of both matrices, both use the one
+// activation tile, and the epilogue writes H = bf16(SiLU(g) * u) (and g, u
+// into a.Y, up.Y when those are not NULL).
+template <int SRC, int MT, int NT, int NW, int WGM, int P, bool DUAL = false>
 __global__ __launch_bounds__(64 * NW, 1)
-void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
+void lds_gemm_kernel(MatArgs a, MatArgs up, uint16_t* H, int tiles_n, int split, int order) {
+    static_assert(!DUAL || SRC == SRC_PAL, "the gate/up pair takes palette sources");
+    constexpr int NMAT = DUAL ? 2 : 1;
     constexpr int WGN = NW / WGM;
     constexpr int NS = P;                              // register sets of loads
     constexpr int FM = MT / 16 / WGM, FN = NT / 16 / WGN;
     constexpr int IPT = MT / (16 * NW), XP = NT / (8 * NW);
     static_assert(IPT >= 1 && XP >= 1 && FM >= 1 && FN >= 1, "tile too small for the waves");
     constexpr int WBUF = MT * kLS, XBUF = NT * kLS;     // bf16 elements per buffer
-    __shared__ __align__(16) uint16_t wl[2 * WBUF];
+    __shared__ __align__(16) uint16_t wl[NMAT][2 * WBUF];
     __shared__ __align__(16) uint16_t xl[2 * XBUF];
-    __shared__ uint32_t lut[256];
-    __shared__ uint64_t tword[SRC == SRC_PAL ? kLMaxTiles : 1];
-    __shared__ uint32_t tbase[SRC == SRC_PAL ? kLMaxTiles : 1];
+    __shared__ uint32_t lut[NMAT][256];
+    __shared__ uint64_t tword[NMAT][SRC == SRC_PAL ? kLMaxTiles : 1];
+    __shared__ uint32_t tbase[NMAT][SRC == SRC_PAL ? kLMaxTiles : 1];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    if (SRC == SRC_PAL && tid < 256) lut[tid] = (lpalb(a, tid & 15) << 7) | (lpalb(a, tid >> 4) << 23);
+    auto mat = [&](int m) -> const MatArgs& { return (DUAL && m) ? up : a; };
+    if (SRC == SRC_PAL && tid < 256) {
+        lut[0][tid] = (lpalb(a, tid & 15) << 7) | (lpalb(a, tid >> 4) << 23);
+        if (DUAL) lut[NMAT - 1][tid] = (lpalb(up, tid & 15) << 7) | (lpalb(up, tid >> 4) << 23);
+    }
 
     // workgroup id -> (row band m, K slice s, batch tile n), each XCD (id %
     // 8) taking a contiguous run of logical tiles; n fastest, then m, then s
@@ -144,13 +154,10 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
         nt = ((last_row * C + C - 1u) >> 12) - t_base + 1u;
     }
 
-    const uint8_t* vb_ptr = a.vexp ? a.vexp : a.sm;
-    const uint16_t* wb = static_cast<const uint16_t*>(a.w);
-    const uint8_t* w8 = static_cast<const uint8_t*>(a.w);
 
     // issue_w: activation pieces and weight planes of step s (no dependency);
     // issue_v: the verbatim exponents (needs the LDS tables)
-    auto issue_w = [&](uint32_t s, LStage<MT, NT, NW>& st) {
+    auto issue_w = [&](uint32_t s, LStage<MT, NT, NW, NMAT>& st) {
         const uint32_t k0 = s * kLS;
 #pragma unroll
         for (int j = 0; j < XP; ++j) {
@@ -161,46 +168,55 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
             st.x[j] = load16(a.X + b * C + k0 + 32u * (f & 1u) + 8u * lc);
         }
 #pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
         for (int it = 0; it < IPT; ++it) {
             const uint32_t pos = rowc[it] * C + k0 + koff;
-            LItem& f = st.w[it];
+            LItem& f = st.w[m][it];
+            const uint16_t* wb = static_cast<const uint16_t*>(mat(m).w);
+            const uint8_t* w8 = static_cast<const uint8_t*>(mat(m).w);
             if (SRC == SRC_BF16) {
                 f.d0 = load16(wb + pos);
                 f.d1 = load16(wb + pos + 8);
             } else if (SRC == SRC_EXP) {
                 f.d0 = load16(w8 + pos);
-                f.sm = load16(a.sm + pos);
+                f.sm = load16(mat(m).sm + pos);
             } else {
                 f.nib = *reinterpret_cast<const u32x2_t*>(w8 + pos / 2);
-                f.sm = load16(a.sm + pos);
+                f.sm = load16(mat(m).sm + pos);
             }
         }
     };
-    auto issue_v = [&](uint32_t s, LStage<MT, NT, NW>& st) {
+    auto issue_v = [&](uint32_t s, LStage<MT, NT, NW, NMAT>& st) {
         if (SRC != SRC_PAL) return;
         const uint32_t k0 = s * kLS;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int it = 0; it < IPT; ++it) {
             const uint32_t pos = rowc[it] * C + k0 + koff;
             const uint32_t g = pos >> 6, bit = g & 63u;
             const uint32_t tl = (g >> 6) - t_base;
-            const uint64_t word = tword[tl];
-            LItem& f = st.w[it];
+            const uint64_t word = tword[m][tl];
+            LItem& f = st.w[m][it];
             f.verb = uint32_t(word >> bit) & 1u;
-            const uint32_t slot = verbatim_slot(word, bit, tbase[tl]);
+            const uint32_t slot = verbatim_slot(word, bit, tbase[m][tl]);
+            const uint8_t* vb_ptr = mat(m).vexp ? mat(m).vexp : mat(m).sm;
             // lanes outside verbatim groups all read one shared line
             f.vx = load16(vb_ptr + (f.verb ? slot * 64u + (pos & 63u) : 0u));
         }
     };
     // commit: rebuild the step's weights into W buffer `buf` and store its
     // activation pieces into X buffer `buf`
-    auto commit = [&](const LStage<MT, NT, NW>& st, uint32_t buf) {
+    auto commit = [&](const LStage<MT, NT, NW, NMAT>& st, uint32_t buf) {
         uint16_t* xd = xl + buf * XBUF + xslot;
 #pragma unroll
         for (int j = 0; j < XP; ++j) store16(xd + uint32_t(wave + NW * j) * 512u, st.x[j]);
 #pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
         for (int it = 0; it < IPT; ++it) {
-            const LItem& f = st.w[it];
+            const LItem& f = st.w[m][it];
             uint32_t w[8];
             if (SRC == SRC_BF16) {
 #pragma unroll
@@ -216,7 +232,7 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
             } else {
                 uint32_t e7[8];
 #pragma unroll
-                for (int p = 0; p < 8; ++p) e7[p] = lut[(f.nib[p >> 2] >> (8 * (p & 3))) & 0xFFu];
+                for (int p = 0; p < 8; ++p) e7[p] = lut[m][(f.nib[p >> 2] >> (8 * (p & 3))) & 0xFFu];
                 if (__builtin_amdgcn_ballot_w64(f.verb != 0)) {      // rare: raw exponents for verbatim lanes
 #pragma unroll
                     for (int p = 0; p < 8; ++p) {
@@ -228,18 +244,20 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
                 for (int p = 0; p < 8; ++p)
                     w[p] = (p & 1) ? join_pair<1>(f.sm[p >> 1], e7[p]) : join_pair<0>(f.sm[p >> 1], e7[p]);
             }
-            uint16_t* wd = wl + buf * WBUF + uint32_t(wave + NW * it) * (2u * 64u * 8u) + wslot;
+            uint16_t* wd = wl[m] + buf * WBUF + uint32_t(wave + NW * it) * (2u * 64u * 8u) + wslot;
             store16(wd, u32x4_t{w[0], w[1], w[2], w[3]});
             store16(wd + 16 * 8, u32x4_t{w[4], w[5], w[6], w[7]});
         }
     };
 
     const uint32_t wm = uint32_t(wave) / WGN, wn = uint32_t(wave) % WGN;
-    f32x4_t acc[FM][FN];
+    f32x4_t acc[NMAT][FM][FN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) acc[m][fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // fragment reads: lane l takes chunk l/16 of row l%16 (swizzled slot)
     const uint32_t rq = uint32_t(lane >> 4), rr = uint32_t(lane & 15);
@@ -249,16 +267,18 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
     // a step's fragments: read from LDS right after the barrier that makes
     // them visible, while the previous step's MFMAs still run
     struct Frags {
-        bf16x8_t A[2][FM], B[2][FN];
+        bf16x8_t A[NMAT][2][FM], B[2][FN];
     };
     auto read_frags = [&](uint32_t buf, Frags& fr) {
-        const uint16_t* wsrc = wl + buf * WBUF;
         const uint16_t* xsrc = xl + buf * XBUF + xread;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
             for (int fm = 0; fm < FM; ++fm)
-                fr.A[h][fm] = *reinterpret_cast<const bf16x8_t*>(wsrc + (wm * FM + fm) * 1024u + (h ? wread1 : wread0));
+                fr.A[m][h][fm] = *reinterpret_cast<const bf16x8_t*>(wl[m] + buf * WBUF + (wm * FM + fm) * 1024u +
+                                                                    (h ? wread1 : wread0));
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
                 fr.B[h][fn] = *reinterpret_cast<const bf16x8_t*>(xsrc + ((wn * FN + fn) * 2u + h) * 512u);
@@ -268,10 +288,13 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.A[h][fm], fr.B[h][fn], acc[fm][fn], 0, 0, 0);
+                    acc[m][fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr.A[m][h][fm], fr.B[h][fn],
+                                                                             acc[m][fm][fn], 0, 0, 0);
     };
 
     // Start: the first P steps' weight and activation loads go out first, then
@@ -285,14 +308,16 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
     // barrier of the pass of step u-1.
     const uint32_t n = s_hi > s_lo ? s_hi - s_lo : 0u;
     const uint32_t first = n ? s_lo : 0u, last = n ? s_hi - 1u : 0u;
-    LStage<MT, NT, NW> st[NS];
+    LStage<MT, NT, NW, NMAT> st[NS];
 #pragma unroll
     for (int j = 0; j < P; ++j) issue_w(min(first + j, last), st[j]);
     if (SRC == SRC_PAL) {
-        for (uint32_t i = uint32_t(tid); i < nt; i += 64u * NW) {
-            tword[i] = a.bitmap[t_base + i];
-            tbase[i] = a.tile_vbase[t_base + i];
-        }
+        for (uint32_t i = uint32_t(tid); i < nt; i += 64u * NW)
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m) {
+                tword[m][i] = mat(m).bitmap[t_base + i];
+                tbase[m][i] = mat(m).tile_vbase[t_base + i];
+            }
     }
     __syncthreads();                                   // LUT and tables ready
 #pragma unroll
@@ -336,8 +361,40 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
     }
 
     // D layout: lane l holds batch column l%16, rows 4*(l/16) .. +3
-    float* out = split > 1 ? a.partial + uint64_t(s_t) * a.B * a.R : a.Y;
     const uint32_t col = lane & 15, q = uint32_t(lane) >> 4;
+    if constexpr (DUAL) {
+        // h = bf16(SiLU(g) * u), as uw_silu_mul_bf16 computes it; g and u too
+        // when asked for
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const uint32_t r = band0 + (wm * FM + fm) * 16u + 4u * q;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const uint32_t b = n0 + (wn * FN + fn) * 16u + col;
+                if (b >= B) continue;
+                const f32x4_t gv = acc[0][fm][fn], uv = acc[1][fm][fn];
+                uint32_t hb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) hb[i] = f32_to_bf16_rne(silu_mul1(gv[i], uv[i]));
+                const uint64_t o = uint64_t(b) * R + r;
+                if (r + 3 < R && (R & 3u) == 0) {
+                    *reinterpret_cast<u32x2_t*>(H + o) = u32x2_t{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+                    if (a.Y) *reinterpret_cast<f32x4_t*>(a.Y + o) = gv;
+                    if (up.Y) *reinterpret_cast<f32x4_t*>(up.Y + o) = uv;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (r + i < R) {
+                            H[o + i] = uint16_t(hb[i]);
+                            if (a.Y) a.Y[o + i] = gv[i];
+                            if (up.Y) up.Y[o + i] = uv[i];
+                        }
+                }
+            }
+        }
+        return;
+    }
+    float* out = split > 1 ? a.partial + uint64_t(s_t) * a.B * a.R : a.Y;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
         const uint32_t r = band0 + (wm * FM + fm) * 16u + 4u * q;
@@ -346,7 +403,7 @@ void lds_gemm_kernel(MatArgs a, int tiles_n, int split, int order) {
             const uint32_t b = n0 + (wn * FN + fn) * 16u + col;
             if (b >= B) continue;
             float* o = out + uint64_t(b) * R + r;
-            const f32x4_t v = acc[fm][fn];
+            const f32x4_t v = acc[0][fm][fn];
             if (r + 3 < R && (R & 3u) == 0) {
                 *reinterpret_cast<f32x4_t*>(o) = v;
             } else {
@@ -399,8 +456,18 @@ template <int SRC, int MT, int NT, int NW, int WGM, int P>
 void lds_launch_cfg(const MatArgs& a, hipStream_t s) {
     const int tiles_m = int((a.R + MT - 1) / MT), tiles_n = int((a.B + NT - 1) / NT);
     const int64_t grid = int64_t(tiles_m) * tiles_n * a.split_k;
-    launch_timed(lds_gemm_kernel<SRC, MT, NT, NW, WGM, P>, dim3(unsigned(grid)), dim3(64 * NW), 0, s, a, tiles_n,
-                 int(a.split_k), lenv_int("UW_LDS_ORDER", 1));
+    launch_timed(lds_gemm_kernel<SRC, MT, NT, NW, WGM, P>, dim3(unsigned(grid)), dim3(64 * NW), 0, s, a, a,
+                 static_cast<uint16_t*>(nullptr), tiles_n, int(a.split_k), lenv_int("UW_LDS_ORDER", 1));
+}
+
+// The gate/up pair: 128 x 64 tiles through batch 128, 128 x 128 above (the
+// Llama gate/up shape gets 224 workgroups at batch 128 and 256); no split.
+template <int CI>
+void lds_launch_pair(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
+    constexpr LCfg c = kLCfgs[CI];
+    const int tiles_m = int((g.R + c.mt - 1) / c.mt), tiles_n = int((g.B + c.nt - 1) / c.nt);
+    launch_timed(lds_gemm_kernel<SRC_PAL, c.mt, c.nt, c.nw, c.wgm, 2, true>, dim3(unsigned(tiles_m * tiles_n)),
+                 dim3(64 * c.nw), 0, s, g, u, h, tiles_n, 1, 1);
 }
 
 // P: steps of loads in flight (UW_LDS_P overrides; 2, 3, 4 or 6, and at
@@ -455,6 +522,25 @@ int lds_gemm_default_split(int src, const MatArgs& a, int cus) {
     int split = 1;
     while (split < 8 && tiles * split * 4 < int64_t(cus) * 3 && steps / (2 * split) >= 4) split *= 2;
     return split;
+}
+
+// The gate/up pair on this kernel: palette sources of one shape whose band
+// tables fit, above batch 128.  Measured on the Llama MLP stack (8 layers,
+// MI355X): batch 256 1.509 ms against 1.669 ms for two launches and the SiLU
+// kernel; at batch 128 the pair (no K split, 128 x 64 tiles) took 1.178
+// against 1.146 ms for two launches on 128 x 128 tiles split in two.
+// UW_GATEUP_LDS=0 turns it off, =2 takes it from batch 65.
+bool lds_gateup_supported(const MatArgs& g, const MatArgs& u) {
+    const int e = lenv_int("UW_GATEUP_LDS", 1);
+    return e != 0 && g.R == u.R && g.C == u.C && g.B == u.B && g.B > (e == 2 ? 64 : 128) &&
+           lds_gemm_supported(SRC_PAL, g) && g.R * g.C < (int64_t(1) << 31) && g.B * g.C < (int64_t(1) << 31) &&
+           g.B * g.R < (int64_t(1) << 31);
+}
+
+hipError_t launch_lds_gateup(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
+    if (g.B <= 128) lds_launch_pair<0>(g, u, h, s);
+    else lds_launch_pair<1>(g, u, h, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_lds_gemm(int src, const MatArgs& a, hipStream_t s) {

@@ -68,6 +68,10 @@ bool lds_gemm_supported(int src, const MatArgs& a);
 bool lds_gemm_preferred(int src, const MatArgs& a);
 int lds_gemm_default_split(int src, const MatArgs& a, int cus);
 hipError_t launch_lds_gemm(int src, const MatArgs& a, hipStream_t s);
+// The fused gate/up pair with the SiLU product on that kernel (palette
+// sources, batch above 64); g.Y / u.Y receive g and u when not NULL.
+bool lds_gateup_supported(const MatArgs& g, const MatArgs& u);
+hipError_t launch_lds_gateup(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s);
 hipError_t launch_mfma_gemv(int src, const MatArgs& a, hipStream_t s);
 bool mfma_gemv_supported(const MatArgs& a);
 // Fused gate/up on the skinny MFMA kernel with the SiLU product (palette

@@ -149,3 +149,67 @@ def test_lds_gemm_default_choice(torch_cuda):
         Y = uw.matmul(dm, to_dev_bf16(x), pipeline=uw.UW_PIPE_DIRECT, kernel=uw.UW_KERNEL_MFMA, split_k=0,
                       scratch=scr)
         assert_matmul_close(Y.cpu().numpy(), w, x, what=f"lds gemm default B={B}")
+
+
+def _bf16_key(b):
+    b = np.asarray(b).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+
+@pytest.mark.parametrize("R,C,B", [(300, 4096 + 1024, 70), (129, 2048, 128), (257, 1024, 129), (200, 1088, 300),
+                                   (2088, 4096, 200)])
+def test_lds_gate_up_pair(torch_cuda, monkeypatch, R, C, B):
+    """The fused gate/up pair (uw_mlp_gate_up above batch 128, from batch 65
+    with UW_GATEUP_LDS=2): g and u bit for bit equal to single launches on
+    the same tile (128 x 64 through batch 128, 128 x 128 above, no split), h
+    bit for bit equal to uw_silu_mul_bf16 on them and to the h-only call; g,
+    u within tolerance of the oracle, h within one bf16 ulp of
+    bf16(SiLU(g)*u) in fp64.  Bands past R, batch tiles past B, row segments
+    straddling tiles."""
+    print_case(f"lds gate/up pair R={R} C={C} B={B}")
+    monkeypatch.setenv("UW_GATEUP_LDS", "2")
+    import torch
+    from tests.gpu_util import from_dev_bits
+    rng = np.random.default_rng(R + 3 * C + B)
+    wg = workloads.gaussian_weights(rng, R, C, 0.02, 0.004, 1.0)
+    wu = workloads.gaussian_weights(rng, R, C, 0.03, 0.002, 2.0)
+    x = workloads.gaussian_activations(np.random.default_rng(B * 7), B, C)
+    dg, du = uw.compress(wg).to_device(), uw.compress(wu).to_device()
+    X = to_dev_bf16(x)
+    g = torch.empty((B, R), dtype=torch.float32, device="cuda")
+    u = torch.empty_like(g)
+    h = uw.mlp_gate_up(dg, du, X, g=g, u=u)
+    h_only = uw.mlp_gate_up(dg, du, X)
+    _force(monkeypatch, 0 if B <= 128 else 1, 2, 1)
+    g2 = uw.gemm_recon_pal(dg, None, X, kernel=uw.UW_KERNEL_MFMA, split_k=1)
+    u2 = uw.gemm_recon_pal(du, None, X, kernel=uw.UW_KERNEL_MFMA, split_k=1)
+    h2 = uw.silu_mul_bf16(g2, u2)
+    gn, un = g.cpu().numpy(), u.cpu().numpy()
+    assert np.array_equal(gn.view(np.uint32), g2.cpu().numpy().view(np.uint32)), "g"
+    assert np.array_equal(un.view(np.uint32), u2.cpu().numpy().view(np.uint32)), "u"
+    hb = from_dev_bits(h)
+    assert np.array_equal(hb, from_dev_bits(h2)), "h"
+    assert np.array_equal(hb, from_dev_bits(h_only)), "h without g/u"
+    rows = None if R * C * B <= 300 * 5120 * 70 else np.arange(0, R, 7)
+    if rows is None:
+        assert_matmul_close(gn, wg, x, what="pair gate")
+        assert_matmul_close(un, wu, x, what="pair up")
+    else:
+        assert_matmul_close(gn[:, rows], wg, x, rows=rows, what="pair gate")
+        assert_matmul_close(un[:, rows], wu, x, rows=rows, what="pair up")
+    href = numerics.f64_to_bf16_bits(numerics.silu_mul(gn.astype(np.float64), un.astype(np.float64)))
+    assert np.abs(_bf16_key(hb) - _bf16_key(href)).max() <= 1
+
+
+def test_lds_gate_up_pair_rejects(torch_cuda):
+    """Batch 33-128 has no fused pair by default: uw_mlp_gate_up reports it
+    unsupported; batch 129 takes the pair."""
+    print_case("lds gate/up pair batch range")
+    w = workloads.gaussian_weights(np.random.default_rng(5), 256, 1024, 0.02, 0.0, 1.0)
+    d = uw.compress(w).to_device()
+    for B in (48, 128):
+        X = to_dev_bf16(workloads.gaussian_activations(np.random.default_rng(6), B, 1024))
+        with pytest.raises(uw.UnweightError) as e:
+            uw.mlp_gate_up(d, d, X)
+        assert e.value.code == uw.UW_EUNSUPPORTED, B
+    uw.mlp_gate_up(d, d, to_dev_bf16(workloads.gaussian_activations(np.random.default_rng(6), 129, 1024)))
