@@ -68,16 +68,17 @@ struct LItem {
 
 template <int MT, int NT, int NW, int NMAT>
 struct LStage {
-    LItem w[NMAT][MT / (16 * NW)];
+    LItem w[NMAT * MT / (16 * NW)];
     u32x4_t x[NT / (8 * NW)];
 };
 
 // MT rows x NT batch columns per workgroup of NW waves, laid out WGM x (NW /
 // WGM) over the tile; P steps of loads in flight.  DUAL: the gate/up pair of
 // an MLP block (`a` gate, `up` up, same shape, palette sources, no K split):
-// each step rebuilds the band's rows of both matrices, both use the one
-// activation tile, and the epilogue writes H = bf16(SiLU(g) * u) (and g, u
-// into a.Y, up.Y when those are not NULL).
+// each step rebuilds the band's rows of both matrices (with 64-row bands,
+// waves 0-3 rebuild gate and 4-7 up), both use the one activation tile, each
+// wave accumulates its output block of both, and the epilogue writes
+// H = bf16(SiLU(g) * u) (and g, u into a.Y, up.Y when those are not NULL).
 template <int SRC, int MT, int NT, int NW, int WGM, int P, bool DUAL = false>
 __global__ __launch_bounds__(64 * NW, 1)
 void lds_gemm_kernel(MatArgs a, MatArgs up, uint16_t* H, int tiles_n, int split, int order) {
@@ -86,8 +87,12 @@ void lds_gemm_kernel(MatArgs a, MatArgs up, uint16_t* H, int tiles_n, int split,
     constexpr int WGN = NW / WGM;
     constexpr int NS = P;                              // register sets of loads
     constexpr int FM = MT / 16 / WGM, FN = NT / 16 / WGN;
-    constexpr int IPT = MT / (16 * NW), XP = NT / (8 * NW);
-    static_assert(IPT >= 1 && XP >= 1 && FM >= 1 && FN >= 1, "tile too small for the waves");
+    // rebuild items: a lane's item it is block wave + NW*it of the NMAT*RB
+    // 16-row blocks (matrix block/RB, row block block%RB)
+    constexpr int RB = MT / 16;
+    constexpr int IPT = NMAT * RB / NW, XP = NT / (8 * NW);
+    static_assert(IPT >= 1 && NMAT * RB % NW == 0 && (NW == RB || NW == 2 * RB) && XP >= 1 && FM >= 1 && FN >= 1,
+                  "tile too small for the waves");
     constexpr int WBUF = MT * kLS, XBUF = NT * kLS;     // bf16 elements per buffer
     __shared__ __align__(16) uint16_t wl[NMAT][2 * WBUF];
     __shared__ __align__(16) uint16_t xl[2 * XBUF];
@@ -134,9 +139,13 @@ void lds_gemm_kernel(MatArgs a, MatArgs up, uint16_t* H, int tiles_n, int split,
     // fragment sits at slot 16q + (r ^ m), m from the chunk's position, which
     // keeps these row-order writes and the fragment-order reads free of bank
     // conflicts.
+    // matrix and row block of item it (NW == RB: matrix it, block wave;
+    // NW == 2 RB, one item: matrix wave/RB, block wave%RB)
+    auto item_mat = [&](int it) -> int { return NW == RB ? it : (wave + NW * it) / RB; };
+    auto item_rb = [&](int it) -> uint32_t { return NW == RB ? uint32_t(wave) : uint32_t((wave + NW * it) % RB); };
     uint32_t rowc[IPT];
 #pragma unroll
-    for (int it = 0; it < IPT; ++it) rowc[it] = min(band0 + 16u * uint32_t(wave + NW * it) + uint32_t(lane >> 2), R - 1u);
+    for (int it = 0; it < IPT; ++it) rowc[it] = min(band0 + 16u * item_rb(it) + uint32_t(lane >> 2), R - 1u);
     const uint32_t lc = uint32_t(lane & 3), lr = uint32_t(lane >> 2);
     const uint32_t koff = 16u * lc;
     // W: the item's chunks 2(lc%2), 2(lc%2)+1 of half lc/2 (bf16 elements,
@@ -168,11 +177,10 @@ void lds_gemm_kernel(MatArgs a, MatArgs up, uint16_t* H, int tiles_n, int split,
             st.x[j] = load16(a.X + b * C + k0 + 32u * (f & 1u) + 8u * lc);
         }
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
         for (int it = 0; it < IPT; ++it) {
+            const int m = item_mat(it);
             const uint32_t pos = rowc[it] * C + k0 + koff;
-            LItem& f = st.w[m][it];
+            LItem& f = st.w[it];
             const uint16_t* wb = static_cast<const uint16_t*>(mat(m).w);
             const uint8_t* w8 = static_cast<const uint8_t*>(mat(m).w);
             if (SRC == SRC_BF16) {
@@ -191,14 +199,13 @@ void lds_gemm_kernel(MatArgs a, MatArgs up, uint16_t* H, int tiles_n, int split,
         if (SRC != SRC_PAL) return;
         const uint32_t k0 = s * kLS;
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
         for (int it = 0; it < IPT; ++it) {
+            const int m = item_mat(it);
             const uint32_t pos = rowc[it] * C + k0 + koff;
             const uint32_t g = pos >> 6, bit = g & 63u;
             const uint32_t tl = (g >> 6) - t_base;
             const uint64_t word = tword[m][tl];
-            LItem& f = st.w[m][it];
+            LItem& f = st.w[it];
             f.verb = uint32_t(word >> bit) & 1u;
             const uint32_t slot = verbatim_slot(word, bit, tbase[m][tl]);
             const uint8_t* vb_ptr = mat(m).vexp ? mat(m).vexp : mat(m).sm;
@@ -213,10 +220,9 @@ void lds_gemm_kernel(MatArgs a, MatArgs up, uint16_t* H, int tiles_n, int split,
 #pragma unroll
         for (int j = 0; j < XP; ++j) store16(xd + uint32_t(wave + NW * j) * 512u, st.x[j]);
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
         for (int it = 0; it < IPT; ++it) {
-            const LItem& f = st.w[m][it];
+            const int m = item_mat(it);
+            const LItem& f = st.w[it];
             uint32_t w[8];
             if (SRC == SRC_BF16) {
 #pragma unroll
@@ -244,7 +250,7 @@ void lds_gemm_kernel(MatArgs a, MatArgs up, uint16_t* H, int tiles_n, int split,
                 for (int p = 0; p < 8; ++p)
                     w[p] = (p & 1) ? join_pair<1>(f.sm[p >> 1], e7[p]) : join_pair<0>(f.sm[p >> 1], e7[p]);
             }
-            uint16_t* wd = wl[m] + buf * WBUF + uint32_t(wave + NW * it) * (2u * 64u * 8u) + wslot;
+            uint16_t* wd = wl[m] + buf * WBUF + item_rb(it) * (2u * 64u * 8u) + wslot;
             store16(wd, u32x4_t{w[0], w[1], w[2], w[3]});
             store16(wd + 16 * 8, u32x4_t{w[4], w[5], w[6], w[7]});
         }
@@ -460,18 +466,6 @@ void lds_launch_cfg(const MatArgs& a, hipStream_t s) {
                  static_cast<uint16_t*>(nullptr), tiles_n, int(a.split_k), lenv_int("UW_LDS_ORDER", 1));
 }
 
-// The gate/up pair: 128 x 64 tiles through batch 128, 128 x 128 above (the
-// Llama gate/up shape gets 224 workgroups at batch 128 and 256); no split.
-template <int CI>
-void lds_launch_pair(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
-    constexpr LCfg c = kLCfgs[CI];
-    const int tiles_m = int((g.R + c.mt - 1) / c.mt), tiles_n = int((g.B + c.nt - 1) / c.nt);
-    launch_timed(lds_gemm_kernel<SRC_PAL, c.mt, c.nt, c.nw, c.wgm, 2, true>, dim3(unsigned(tiles_m * tiles_n)),
-                 dim3(64 * c.nw), 0, s, g, u, h, tiles_n, 1, 1);
-}
-
-// P: steps of loads in flight (UW_LDS_P overrides; 2, 3, 4 or 6, and at
-// most 3 with 256 batch columns, whose register sets are largest).
 template <int SRC, int CI>
 void lds_launch_ci(const MatArgs& a, hipStream_t s) {
     constexpr LCfg c = kLCfgs[CI];
@@ -525,21 +519,30 @@ int lds_gemm_default_split(int src, const MatArgs& a, int cus) {
 }
 
 // The gate/up pair on this kernel: palette sources of one shape whose band
-// tables fit, above batch 128.  Measured on the Llama MLP stack (8 layers,
-// MI355X): batch 256 1.509 ms against 1.669 ms for two launches and the SiLU
-// kernel; at batch 128 the pair (no K split, 128 x 64 tiles) took 1.178
-// against 1.146 ms for two launches on 128 x 128 tiles split in two.
-// UW_GATEUP_LDS=0 turns it off, =2 takes it from batch 65.
+// tables fit, above batch 64 (UW_GATEUP_LDS=0 turns it off).  Bands of 64
+// rows, waves 0-3 rebuilding gate and 4-7 up, 128 batch columns through
+// batch 128 and 256 above (224 workgroups for the Llama gate/up shape), K
+// unsplit.  Measured on the Llama MLP stack (8 layers, MI355X) against two
+// launches and the SiLU kernel: batch 128 0.974 against 1.13-1.15 ms, batch
+// 256 1.398 against 1.67 ms.  Bands of 128 rows (each weight rebuilt once
+// per 64 or 128 batch columns) took 1.219 ms at batch 128 and 1.52-1.54 ms
+// at 256.
 bool lds_gateup_supported(const MatArgs& g, const MatArgs& u) {
-    const int e = lenv_int("UW_GATEUP_LDS", 1);
-    return e != 0 && g.R == u.R && g.C == u.C && g.B == u.B && g.B > (e == 2 ? 64 : 128) &&
-           lds_gemm_supported(SRC_PAL, g) && g.R * g.C < (int64_t(1) << 31) && g.B * g.C < (int64_t(1) << 31) &&
-           g.B * g.R < (int64_t(1) << 31);
+    return g.R == u.R && g.C == u.C && g.B == u.B && g.B > 64 && lds_gemm_supported(SRC_PAL, g) &&
+           g.R * g.C < (int64_t(1) << 31) && g.B * g.C < (int64_t(1) << 31) && g.B * g.R < (int64_t(1) << 31) &&
+           lenv_int("UW_GATEUP_LDS", 1) != 0;
+}
+
+template <int NT>
+void lds_launch_pair(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
+    const int tiles_m = int((g.R + 63) / 64), tiles_n = int((g.B + NT - 1) / NT);
+    launch_timed(lds_gemm_kernel<SRC_PAL, 64, NT, 8, 2, 2, true>, dim3(unsigned(tiles_m * tiles_n)), dim3(512), 0, s,
+                 g, u, h, tiles_n, 1, 1);
 }
 
 hipError_t launch_lds_gateup(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
-    if (g.B <= 128) lds_launch_pair<0>(g, u, h, s);
-    else lds_launch_pair<1>(g, u, h, s);
+    if (g.B <= 128) lds_launch_pair<128>(g, u, h, s);
+    else lds_launch_pair<256>(g, u, h, s);
     return hipGetLastError();
 }
 

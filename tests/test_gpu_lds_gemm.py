@@ -20,9 +20,10 @@ from tests.gpu_util import assert_matmul_close, print_case, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
-# (config, prefetch depth, workgroup order) the kernel is instantiated with:
+# (config, prefetch depth, workgroup order) the kernel is instantiated with
+# (prefetch 4 and 6 run as 3 with 256 columns):
 # configs 0/1/2 are 128 rows x 64/128/256 batch columns
-_VARIANTS = list(itertools.product((0, 1, 2), (2, 3), (0, 1)))
+_VARIANTS = list(itertools.product((0, 1, 2), (2, 3, 4, 6), (0, 1)))
 
 
 @pytest.fixture(scope="module")
@@ -159,15 +160,14 @@ def _bf16_key(b):
 @pytest.mark.parametrize("R,C,B", [(300, 4096 + 1024, 70), (129, 2048, 128), (257, 1024, 129), (200, 1088, 300),
                                    (2088, 4096, 200)])
 def test_lds_gate_up_pair(torch_cuda, monkeypatch, R, C, B):
-    """The fused gate/up pair (uw_mlp_gate_up above batch 128, from batch 65
-    with UW_GATEUP_LDS=2): g and u bit for bit equal to single launches on
-    the same tile (128 x 64 through batch 128, 128 x 128 above, no split), h
-    bit for bit equal to uw_silu_mul_bf16 on them and to the h-only call; g,
-    u within tolerance of the oracle, h within one bf16 ulp of
-    bf16(SiLU(g)*u) in fp64.  Bands past R, batch tiles past B, row segments
-    straddling tiles."""
+    """The fused gate/up pair (uw_mlp_gate_up above batch 64; 64-row bands x
+    128 batch columns through batch 128, x 256 above, no split): g and u bit
+    for bit equal to single launches at split 1 (every tiling sums each
+    output over K in the same order), h bit for bit equal to
+    uw_silu_mul_bf16 on them and to the h-only call; g, u within tolerance
+    of the oracle, h within one bf16 ulp of bf16(SiLU(g)*u) in fp64.  Bands
+    past R, batch tiles past B, row segments straddling tiles."""
     print_case(f"lds gate/up pair R={R} C={C} B={B}")
-    monkeypatch.setenv("UW_GATEUP_LDS", "2")
     import torch
     from tests.gpu_util import from_dev_bits
     rng = np.random.default_rng(R + 3 * C + B)
@@ -202,14 +202,14 @@ def test_lds_gate_up_pair(torch_cuda, monkeypatch, R, C, B):
 
 
 def test_lds_gate_up_pair_rejects(torch_cuda):
-    """Batch 33-128 has no fused pair by default: uw_mlp_gate_up reports it
-    unsupported; batch 129 takes the pair."""
+    """Batch 33-64 has no fused pair: uw_mlp_gate_up reports it unsupported;
+    batch 65 takes the pair."""
     print_case("lds gate/up pair batch range")
     w = workloads.gaussian_weights(np.random.default_rng(5), 256, 1024, 0.02, 0.0, 1.0)
     d = uw.compress(w).to_device()
-    for B in (48, 128):
+    for B in (48, 64):
         X = to_dev_bf16(workloads.gaussian_activations(np.random.default_rng(6), B, 1024))
         with pytest.raises(uw.UnweightError) as e:
             uw.mlp_gate_up(d, d, X)
         assert e.value.code == uw.UW_EUNSUPPORTED, B
-    uw.mlp_gate_up(d, d, to_dev_bf16(workloads.gaussian_activations(np.random.default_rng(6), 129, 1024)))
+    uw.mlp_gate_up(d, d, to_dev_bf16(workloads.gaussian_activations(np.random.default_rng(6), 65, 1024)))
