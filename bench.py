@@ -221,7 +221,7 @@ class Step:
         st = ct.c_void_p(stream.cuda_stream)
         P = lambda t: ct.c_void_p(t.data_ptr())
         scr, nsc = P(self.scratch), ct.c_uint64(self.scratch.numel())
-        self.fused = fuse and (batch <= 32 or batch > 64) and self._plans_direct(uw, pipe, F, H, batch) and \
+        self.fused = fuse and self._plans_direct(uw, pipe, F, H, batch) and \
             self._pair_supported(uw, layers[0], self.X[0], batch)
         self.calls = []          # per layer: the bound calls in launch order
         self.kinds = []          # per layer: what each timed (matmul) launch is
@@ -280,7 +280,7 @@ class Step:
     @staticmethod
     def _pair_supported(uw, lay, X, batch):
         """Whether uw_mlp_gate_up takes this shape at this batch (batch 17-32
-        only on tall matrices; none at 33-64)."""
+        only on tall matrices; the LDS-tile pair above 32)."""
         if lay.mats[0] is None:
             return False
         try:
@@ -294,7 +294,7 @@ class Step:
     @staticmethod
     def _plans_direct(uw, pipe, F, H, batch):
         """Gate/up may be fused (uw_mlp_gate_up: the GEMV pair at batch 1-2,
-        a skinny MFMA pair at 3-32, the LDS-tile MFMA pair above 64) when they
+        a skinny MFMA pair at 3-32, the LDS-tile MFMA pair above 32) when they
         would run on the direct-palette form with those kernels: asked for
         directly, or what the plan table holds for the gate shape at this
         batch (no entry: direct palette with the library's kernel choice)."""

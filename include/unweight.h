@@ -348,11 +348,12 @@ int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, voi
  * within the matmul's fp32 rounding, not bit for bit).  Other shapes at
  * batch 3-16 run the register-staged skinny pair: g and u equal
  * uw_gemm_recon_pal with UW_KERNEL_SKINNY bit for bit (same K-split).
- * Above batch 64 the pair runs on the tiled MFMA kernel that rebuilds each
- * weight once per workgroup into an LDS tile (64-row bands x 128 batch
- * columns through batch 128, x 256 above, K unsplit; both matrices share each
- * activation tile): g and u equal uw_gemm_recon_pal with UW_KERNEL_MFMA at
- * split_k 1 above batch 64 bit for bit (same K order).  In every case h is bit-identical
+ * Above batch 32 (other shapes and batches where the skinny pairs do not
+ * apply) the pair runs on the tiled MFMA kernel that rebuilds each weight
+ * once per workgroup into an LDS tile (64-row bands x 64, 128 or 256 batch
+ * columns, K unsplit; both matrices share each activation tile): g and u
+ * equal uw_gemm_recon_pal with UW_KERNEL_MFMA at split_k 1 above batch 64 bit
+ * for bit (same K order), and that kernel forced (UW_MFMA_LDS=1) at 33-64.  In every case h is bit-identical
  * to uw_silu_mul_bf16 on the g, u the call computes.
  * gate, up: same shape [rows, cols], both with a NIB section; X bf16 bits
  * [batch, cols]; h bf16 bits [batch, rows]; g_out, u_out fp32 [batch, rows]
@@ -364,7 +365,7 @@ int uw_silu_mul_bf16(const float* g, const float* u, int64_t n, uint16_t* h, voi
  * 1 <= batch <= 16 and the library splits K at most 4 ways for this shape on
  * the current device (about one wave per SIMD: at least ~4096 rows on
  * MI355X), or, at batch 1-2, batch*cols*2 <= 32768 and cols <= 245760, or
- * batch above 64 with cols % 64 == 0 (and cols <= 20416, the verbatim
+ * batch above 32 with cols % 64 == 0 (and cols <= 20416, the verbatim
  * tables of a 128-row band in LDS). */
 int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, int64_t batch,
                    uint16_t* h, float* g_out, float* u_out, void* stream);

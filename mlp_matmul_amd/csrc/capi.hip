@@ -565,7 +565,7 @@ int uw_mlp_gate_up(const uw_dmat* gate, const uw_dmat* up, const uint16_t* X, in
         return uw::fail(UW_EUNSUPPORTED, std::string(who) +
                                              ": needs batch 1..16, cols % 128 == 0, cols <= 32768 and a K-split of at "
                                              "most 4 for the shape (batch 1-2: or batch*cols*2 <= 32768; batch 17-32: "
-                                             "at least 48 rows per compute unit), or batch above 64");
+                                             "at least 48 rows per compute unit), or batch above 32");
     return e == hipSuccess ? UW_OK : hip_fail(e, who);
 }
 

@@ -519,18 +519,19 @@ int lds_gemm_default_split(int src, const MatArgs& a, int cus) {
 }
 
 // The gate/up pair on this kernel: palette sources of one shape whose band
-// tables fit, above batch 64 (UW_GATEUP_LDS=0 turns it off).  Bands of 64
-// rows, waves 0-3 rebuilding gate and 4-7 up, 128 batch columns through
-// batch 128 and 256 above (224 workgroups for the Llama gate/up shape), K
-// unsplit.  Measured on the Llama MLP stack (8 layers, MI355X) against two
-// launches and the SiLU kernel: batch 128 0.974 against 1.13-1.15 ms, batch
-// 256 1.398 against 1.67 ms.  Bands of 128 rows (each weight rebuilt once
-// per 64 or 128 batch columns) took 1.219 ms at batch 128 and 1.52-1.54 ms
-// at 256.
+// tables fit, above batch 32 (UW_GATEUP_LDS=0 turns it off,
+// UW_GATEUP_LDS_MIN moves the threshold).  Bands of 64 rows, waves 0-3
+// rebuilding gate and 4-7 up, 64 batch columns through batch 64, 128 through
+// 128, 256 above (224 workgroups for the Llama gate/up shape through batch
+// 256), K unsplit.  Measured on the Llama MLP stack (8 layers, MI355X)
+// against two launches and the SiLU kernel: batch 48 0.758 against
+// 0.86-0.90 ms, 64 0.813 against 0.93, 128 0.974 against 1.13-1.15, 256
+// 1.398 against 1.67.  Bands of 128 rows (each weight rebuilt once per 64 or
+// 128 batch columns) took 1.219 ms at batch 128 and 1.52-1.54 ms at 256.
 bool lds_gateup_supported(const MatArgs& g, const MatArgs& u) {
-    return g.R == u.R && g.C == u.C && g.B == u.B && g.B > 64 && lds_gemm_supported(SRC_PAL, g) &&
-           g.R * g.C < (int64_t(1) << 31) && g.B * g.C < (int64_t(1) << 31) && g.B * g.R < (int64_t(1) << 31) &&
-           lenv_int("UW_GATEUP_LDS", 1) != 0;
+    return g.R == u.R && g.C == u.C && g.B == u.B && g.B > lenv_int("UW_GATEUP_LDS_MIN", 32) &&
+           lds_gemm_supported(SRC_PAL, g) && g.R * g.C < (int64_t(1) << 31) && g.B * g.C < (int64_t(1) << 31) &&
+           g.B * g.R < (int64_t(1) << 31) && lenv_int("UW_GATEUP_LDS", 1) != 0;
 }
 
 template <int NT>
@@ -541,7 +542,8 @@ void lds_launch_pair(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_
 }
 
 hipError_t launch_lds_gateup(const MatArgs& g, const MatArgs& u, uint16_t* h, hipStream_t s) {
-    if (g.B <= 128) lds_launch_pair<128>(g, u, h, s);
+    if (g.B <= 64) lds_launch_pair<64>(g, u, h, s);
+    else if (g.B <= 128) lds_launch_pair<128>(g, u, h, s);
     else lds_launch_pair<256>(g, u, h, s);
     return hipGetLastError();
 }

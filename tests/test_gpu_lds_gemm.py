@@ -1,5 +1,6 @@
 """GPU parity of the tiled MFMA kernel that rebuilds each weight once per
-workgroup into a shared LDS tile (above batch 64 by default).
+workgroup into a shared LDS tile (above batch 64 by default for single
+matrices, above batch 32 for the fused gate/up pair).
 
 Every tile configuration, prefetch depth and workgroup order sums each
 output over the same K order (the tiling only moves rows and batch columns
@@ -157,12 +158,12 @@ def _bf16_key(b):
     return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
 
 
-@pytest.mark.parametrize("R,C,B", [(300, 4096 + 1024, 70), (129, 2048, 128), (257, 1024, 129), (200, 1088, 300),
-                                   (2088, 4096, 200)])
+@pytest.mark.parametrize("R,C,B", [(300, 4096 + 1024, 33), (129, 2048, 64), (300, 4096 + 1024, 70), (129, 2048, 128),
+                                   (257, 1024, 129), (200, 1088, 300), (2088, 4096, 200)])
 def test_lds_gate_up_pair(torch_cuda, monkeypatch, R, C, B):
-    """The fused gate/up pair (uw_mlp_gate_up above batch 64; 64-row bands x
-    128 batch columns through batch 128, x 256 above, no split): g and u bit
-    for bit equal to single launches at split 1 (every tiling sums each
+    """The fused gate/up pair (uw_mlp_gate_up above batch 32; 64-row bands x
+    64, 128 or 256 batch columns, no split): g and u bit for bit equal to
+    single launches of the same kernel at split 1 (every tiling sums each
     output over K in the same order), h bit for bit equal to
     uw_silu_mul_bf16 on them and to the h-only call; g, u within tolerance
     of the oracle, h within one bf16 ulp of bf16(SiLU(g)*u) in fp64.  Bands
@@ -180,7 +181,7 @@ def test_lds_gate_up_pair(torch_cuda, monkeypatch, R, C, B):
     u = torch.empty_like(g)
     h = uw.mlp_gate_up(dg, du, X, g=g, u=u)
     h_only = uw.mlp_gate_up(dg, du, X)
-    _force(monkeypatch, 0 if B <= 128 else 1, 2, 1)
+    _force(monkeypatch, 0 if B <= 128 else 1, 2, 1)       # the LDS-tile kernel at every batch
     g2 = uw.gemm_recon_pal(dg, None, X, kernel=uw.UW_KERNEL_MFMA, split_k=1)
     u2 = uw.gemm_recon_pal(du, None, X, kernel=uw.UW_KERNEL_MFMA, split_k=1)
     h2 = uw.silu_mul_bf16(g2, u2)
@@ -202,14 +203,15 @@ def test_lds_gate_up_pair(torch_cuda, monkeypatch, R, C, B):
 
 
 def test_lds_gate_up_pair_rejects(torch_cuda):
-    """Batch 33-64 has no fused pair: uw_mlp_gate_up reports it unsupported;
-    batch 65 takes the pair."""
+    """On a matrix too short for the skinny pairs, batch 17-32 has no fused
+    pair (uw_mlp_gate_up reports it unsupported); batch 33 takes the
+    LDS-tile pair."""
     print_case("lds gate/up pair batch range")
     w = workloads.gaussian_weights(np.random.default_rng(5), 256, 1024, 0.02, 0.0, 1.0)
     d = uw.compress(w).to_device()
-    for B in (48, 64):
+    for B in (17, 32):
         X = to_dev_bf16(workloads.gaussian_activations(np.random.default_rng(6), B, 1024))
         with pytest.raises(uw.UnweightError) as e:
             uw.mlp_gate_up(d, d, X)
         assert e.value.code == uw.UW_EUNSUPPORTED, B
-    uw.mlp_gate_up(d, d, to_dev_bf16(workloads.gaussian_activations(np.random.default_rng(6), 65, 1024)))
+    uw.mlp_gate_up(d, d, to_dev_bf16(workloads.gaussian_activations(np.random.default_rng(6), 33, 1024)))
