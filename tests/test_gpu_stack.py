@@ -148,9 +148,10 @@ def test_stack_layer(torch_cuda, stack_plan, layer):
                           scratch=_plan_scratch(*w.shape, B)).cpu().numpy()
             rows = _rows(w.shape[0], 1000 * layer + 10 * m + B)
             assert_matmul_close(Y[:, rows], w, x, rows=rows, what=f"layer {layer} {NAMES[m]} B={B}")
-    # the benchmark's step: fused gate/up + SiLU, down on its h
+    # the benchmark's step: fused gate/up + SiLU (the GEMV, DMA skinny and
+    # LDS-tile MFMA pairs), down on its h
     (wg, _), (wu, _), (wd, _) = host
-    for B in (1, 16):
+    for B in (1, 16, 256):
         print_case(f"stack layer {layer} fused step B={B}")
         x = workloads.layer_activation(5, layer, 0, B)
         g = torch.empty((B, wg.shape[0]), dtype=torch.float32, device="cuda")
@@ -245,8 +246,10 @@ SHARDS = {0: (workloads.LLAMA_FFN // 8, workloads.LLAMA_HIDDEN), 1: (workloads.L
 def test_tensor_parallel_shard_shapes(torch_cuda, B):
     """One GPU's share of the stack's layer 0 under 8-way tensor parallelism
     (gate/up split by rows, down by columns): every pipeline with the
-    library's kernel choice, every output against the oracle; at batch 1
-    the fused gate/up launch and the down projection on its h."""
+    library's kernel choice, every output against the oracle; the fused
+    gate/up launch where the shape takes one (the GEMV pair at batch 1, the
+    LDS-tile pair at 256; 1792 rows are too few for a skinny pair at 16)
+    and the down projection on its h."""
     torch = torch_cuda
     mats = {m: workloads.layer_weight(5, 0, m, shape=SHARDS[m]) for m in range(3)}
     dms = {m: uw.compress(w).to_device() for m, w in mats.items()}
@@ -259,19 +262,19 @@ def test_tensor_parallel_shard_shapes(torch_cuda, B):
             Y = uw.matmul(dms[m], X, pipeline=p, kernel=uw.UW_KERNEL_AUTO, split_k=0,
                           scratch=uw.alloc_scratch(p, R, C, B, 0))
             assert_matmul_close(Y.cpu().numpy(), w, x, what=f"shard {NAMES[m]} {name} B={B}")
-    if B <= 16:
-        x = workloads.layer_activation(5, 0, 0, B, cols=SHARDS[0][1])
-        g = torch.empty((B, SHARDS[0][0]), dtype=torch.float32, device="cuda")
-        u = torch.empty_like(g)
-        try:
-            h = uw.mlp_gate_up(dms[0], dms[1], to_dev_bf16(x), g=g, u=u)
-        except uw.UnweightError as e:
-            assert e.code == uw.UW_EUNSUPPORTED and B > 2, str(e)   # the GEMV pair takes any row count
-            return
-        gn, un, hb = g.cpu().numpy(), u.cpu().numpy(), from_dev_bits(h)
-        assert_matmul_close(gn, mats[0], x, what="shard fused gate")
-        assert_matmul_close(un, mats[1], x, what="shard fused up")
-        check_silu_product(hb, gn, un, what="shard")
-        y = uw.matmul(dms[2], h, pipeline=uw.UW_PIPE_DIRECT, kernel=uw.UW_KERNEL_AUTO, split_k=0,
-                      scratch=uw.alloc_scratch(uw.UW_PIPE_DIRECT, *SHARDS[2], B, 0))
-        assert_matmul_close(y.cpu().numpy(), mats[2], hb, what="shard down on h")
+    # the fused pair, where the shape takes one
+    x = workloads.layer_activation(5, 0, 0, B, cols=SHARDS[0][1])
+    g = torch.empty((B, SHARDS[0][0]), dtype=torch.float32, device="cuda")
+    u = torch.empty_like(g)
+    try:
+        h = uw.mlp_gate_up(dms[0], dms[1], to_dev_bf16(x), g=g, u=u)
+    except uw.UnweightError as e:
+        assert e.code == uw.UW_EUNSUPPORTED and B > 2, str(e)   # the GEMV pair takes any row count
+        return
+    gn, un, hb = g.cpu().numpy(), u.cpu().numpy(), from_dev_bits(h)
+    assert_matmul_close(gn, mats[0], x, what="shard fused gate")
+    assert_matmul_close(un, mats[1], x, what="shard fused up")
+    check_silu_product(hb, gn, un, what="shard")
+    y = uw.matmul(dms[2], h, pipeline=uw.UW_PIPE_DIRECT, kernel=uw.UW_KERNEL_AUTO, split_k=0,
+                  scratch=uw.alloc_scratch(uw.UW_PIPE_DIRECT, *SHARDS[2], B, 0))
+    assert_matmul_close(y.cpu().numpy(), mats[2], hb, what="shard down on h")
