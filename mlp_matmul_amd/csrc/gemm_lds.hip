@@ -1,6 +1,7 @@
 // bf16 MFMA matmul on gfx950 for batch 64 and up, over uncompressed weights
 // or with on-chip weight reconstruction, in which every weight is rebuilt
-// once per workgroup into a shared LDS tile.
+// once per workgroup into a shared LDS tile; and the fused gate/up pair of an
+// MLP block with the SiLU product, above batch 32.
 //
 // Method: Cloudflare, "Unweight: how we compressed an LLM 22% without
 // sacrificing quality", "How the reconstructive matmul works": compressed
@@ -39,6 +40,11 @@
 // Each weight is rebuilt once per workgroup (the register-rebuilding tiled
 // kernel rebuilds it once per wave that uses it), and a 128-row band streams
 // the activations once per 128 rows.
+// The gate/up pair runs 64-row bands of both matrices: waves 0-3 rebuild the
+// gate rows and waves 4-7 the up rows, every wave accumulates its output
+// block of both from the one activation tile, and the epilogue writes
+// h = bf16(SiLU(g) * u), K unsplit (224 workgroups for the Llama gate/up
+// shape with 64, 128 or 256 batch columns).
 // Split-K adds workgroups for short matrices; partial tiles go to a scratch
 // array that a second kernel sums in a fixed order (deterministic).
 // Workgroups are numbered so that each XCD's run of workgroups shares one
